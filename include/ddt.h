@@ -1,0 +1,194 @@
+/*
+ * ddt.h -- C ABI of libddt.so: the data-parallel hot path of one DDTree
+ * verify step for an MLA model, on one MI355X (gfx950).
+ *
+ * The step, as described on the pages
+ *   "The Architecture of Pragmatic Ambition: Building a Native C++ Inference
+ *    Engine for Kimi K2.6" (below: [Ambition]) and
+ *   "The Architectural Keystone: Writing the Model Header for a Native
+ *    DDTree Inference Engine" (below: [Keystone]),
+ * is: parent array -> ancestor mask; tree-verify attention in absorbed MLA
+ * form over the committed latent cache plus the tree nodes; target argmax;
+ * greedy tree acceptance; compaction of the accepted path's latents.
+ *
+ * Conventions for every call:
+ *  - Pointers are caller-owned DEVICE memory unless the name ends in _host.
+ *    Nothing here allocates device memory.  Buffers a call needs beyond its
+ *    inputs and outputs are passed in as a caller-owned workspace, sized by
+ *    the matching *_workspace query.
+ *  - Every call is asynchronous on `stream` (0 = the null stream) and
+ *    returns DDT_OK or a negative ddt_status synchronously.  Argument errors
+ *    that the host can see (null pointers, sizes out of range, unsupported
+ *    shapes or dtypes, misalignment, a workspace that is too small) return
+ *    an error before anything is launched.  Errors that depend on device
+ *    data (an invalid tree) are reported through device-side flags.
+ *  - Calls keep no state between invocations and may be made from several
+ *    host threads on different streams.  Calls that write the same buffers
+ *    must be ordered by the caller.
+ *  - Floating point data is fp32 (DDT_F32) or bf16 (DDT_BF16, stored as
+ *    16-bit patterns); accumulation is always fp32.
+ */
+#ifndef DDT_H
+#define DDT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DDT_OK = 0,
+    DDT_EINVAL = -1,       /* null pointer, size or stride out of range, misalignment */
+    DDT_EUNSUPPORTED = -2, /* shape / dtype combination not built into the library   */
+    DDT_EWORKSPACE = -3,   /* workspace missing or smaller than the query returned   */
+    DDT_EHIP = -4          /* a HIP runtime call or kernel launch failed              */
+} ddt_status;
+
+typedef enum { DDT_F32 = 0, DDT_BF16 = 1 } ddt_dtype;
+
+#define DDT_MAX_NODES 1024 /* budget + 1 */
+#define DDT_MAX_BATCH 128  /* requests per verify-attention call */
+
+/* Library version (major*10000 + minor*100 + patch) and a status name. */
+int ddt_version(void);
+const char* ddt_status_string(int status);
+
+/*
+ * Ancestor mask of each request's draft tree.
+ *
+ * [Ambition], section "The Decision Architecture": prefill, decode and tree
+ * verification share one attention and differ only in the mask; in tree
+ * verification a node sees the committed prefix and, inside the tree, only
+ * its own ancestors.  A node also sees itself (so a chain-shaped tree is
+ * causal attention and a one-node tree is plain decode).
+ *
+ * parents  [B][N] int32: parents[b][0] = -1 (root), parents[b][i] in [0, i).
+ * mask     [B][N][W] uint64, W = ceil(N/64): bit (j % 64) of word j / 64 of
+ *          row (b, i) is set iff node j is i or an ancestor of i.
+ * depth    [B][N] int32 or NULL: edges from node i to the root.
+ * tree_err [B] int32 or NULL: 0 for a valid tree, 1 otherwise; an invalid
+ *          request gets an all-zero mask and depth -1.
+ * 1 <= N <= DDT_MAX_NODES, B >= 0 (B = 0 launches nothing).
+ */
+int ddt_build_mask(const int32_t* parents, int B, int N, uint64_t* mask, int32_t* depth,
+                   int32_t* tree_err, hipStream_t stream);
+
+/*
+ * Shape and layout of a tree-verify attention call.
+ *
+ * Queries: flat row r = (b*N + i)*H + h (node-major, head-minor).  The
+ * absorbed no-rope query q_lat (d_lat wide) of row r starts at
+ * q_lat + r*ld_ql and its rope part q_pe (d_rope wide) at q_pe + r*ld_qp
+ * (elements).  [Ambition], section "The Thinking Process": absorbing W_UK
+ * into the query turns q_nope . (W_UK c_kv) into q_lat . c_kv, so the keys
+ * and values are the cached latents themselves.
+ *
+ * Cache: [Keystone], section "What the Header Declares": per token the
+ * cache keeps the latent c_kv (d_lat = kv_lora_rank) and the decoupled rope
+ * key k_pe (d_rope).  Cache row t of request b is pool row kv_base[b] + t;
+ * its c_kv starts at ckv + row*ld_ckv and its k_pe at kpe + row*ld_kpe.  The
+ * usual layout interleaves them: kpe = ckv + d_lat, ld_ckv = ld_kpe =
+ * d_lat + d_rope.  [Keystone], section "The Reasoning That Preceded the
+ * Header": the committed prefix occupies rows [0, P_b) and the N tree nodes
+ * (root = last committed token, recomputed) occupy rows P_b .. P_b+N-1, so
+ * node j is key P_b + j and a request has T_b = P_b + N keys.
+ *
+ * scale multiplies the full score q_lat.c_kv + q_pe.k_pe before softmax.
+ * kv_chunk: keys per split of the key range (rounded up to a multiple of
+ * 32); 0 lets the library choose.  Results do not depend on it beyond
+ * rounding.
+ *
+ * Built instances (d_lat, d_rope, dtype): (512, 64, BF16), (64, 16, F32).
+ * Alignment: q_lat, q_pe, ckv, kpe 16-byte aligned; every row stride times
+ * the element size a multiple of 16 bytes.
+ */
+typedef struct {
+    int B, H, N;
+    int d_lat, d_rope;
+    int dtype; /* ddt_dtype */
+    float scale;
+    int kv_chunk;
+    int64_t ld_ql, ld_qp;
+    int64_t ld_ckv, ld_kpe;
+} ddt_attn_desc;
+
+/* Workspace bytes ddt_verify_attn needs for this shape and these prefix
+ * lengths (host array [B]); may be 0. */
+int ddt_verify_workspace(const ddt_attn_desc* d, const int32_t* prefix_len_host, size_t* bytes);
+
+/*
+ * Tree-verify attention, absorbed MLA form.  For every (b, i, h):
+ *   visible keys V = [0, P_b) u {P_b + j : mask bit j of row (b, i) set}
+ *   s_t  = scale * (q_lat . c_kv[t] + q_pe . k_pe[t])
+ *   out  = sum_{t in V} softmax(s)_t c_kv[t]          [B][N][H][d_lat], dtype
+ *   lse  = ln sum_{t in V} exp(s_t)                   [B][N][H] fp32
+ * out rows are contiguous (row stride d_lat).  prefix_len_host [B] is read
+ * on the host during the call (it plans the work split); kv_base [B] int64
+ * and mask (from ddt_build_mask) are device arrays.  Keys past T_b are never
+ * read.  Accumulation and softmax are fp32; probabilities enter the value
+ * product in the input dtype.  Requires B <= DDT_MAX_BATCH,
+ * N <= DDT_MAX_NODES, P_b >= 0.
+ */
+int ddt_verify_attn(const ddt_attn_desc* d, const void* q_lat, const void* q_pe, const void* ckv,
+                    const void* kpe, const int64_t* kv_base, const int32_t* prefix_len_host,
+                    const uint64_t* mask, void* out, float* lse, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Target argmax.  [Ambition], section "The Decision Architecture": greedy
+ * token selection from logits.  idx[r] = lowest index of the maximum of row
+ * r of logits (row r at logits + r*ld, V entries, dtype fp32 or bf16).  -0
+ * and +0 compare equal; a NaN counts as larger than every number, so the
+ * first NaN wins.  rows >= 0, 1 <= V <= 2^31-1, ld >= V.
+ */
+int ddt_argmax_workspace(int64_t rows, int64_t V, size_t* bytes);
+int ddt_argmax(const void* logits, int dtype, int64_t rows, int64_t V, int64_t ld, int32_t* idx,
+               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Greedy tree acceptance.  [Ambition], section "The Knowledge
+ * Architecture": walk the verified tree greedily for the longest path that
+ * matches the target's predictions.  target_ids[b][c] is the target's
+ * greedy token after node c.  From the root, repeatedly move to the
+ * lowest-numbered child k of the current node c with
+ * draft_ids[b][k] == target_ids[b][c]; stop when none matches.
+ *   path[b]       = [0, k1, k2, ...] then -1            [B][N] int32
+ *   accept_len[b] = number of accepted draft nodes       [B] int32
+ *   tokens[b]     = draft ids along the path, then the bonus token
+ *                   target_ids[b][last], then -1       [B][N] int32
+ * draft_ids[b][0] is not read.  parents as for ddt_build_mask; on an
+ * invalid tree the walk still ends (it only moves to higher node numbers).
+ */
+int ddt_greedy_accept(const int32_t* target_ids, const int32_t* draft_ids, const int32_t* parents,
+                      int B, int N, int32_t* accept_len, int32_t* path, int32_t* tokens,
+                      hipStream_t stream);
+
+/*
+ * KV compaction and length update.  [Keystone], section "The Reasoning That
+ * Preceded the Header": after acceptance the accepted path's latents, the
+ * recomputed root included, are gathered into contiguous slots and the
+ * cache length advances; section "Mistakes and Iterative Refinement":
+ * source and destination slots alias, which must not race.
+ * For request b with P = prefix_len[b] and k = accept_len[b]:
+ *   cache row P+j <- old cache row P+path[b][j], j = 0..k (c_kv and k_pe),
+ *   prefix_len[b] <- P + k + 1        (device array, updated in place),
+ *   src_slot[b][j] = P + path[b][j] for j <= k, else -1   (NULL allowed).
+ * Rows from P+k+1 on are left as they were.  A request whose accept_len is
+ * outside [0, N) or whose path is not 0 followed by increasing node numbers
+ * below N is left untouched (src_slot all -1, prefix_len unchanged).
+ * Layout arguments as in ddt_attn_desc; row strides times the element size
+ * and the pointers must be 4-byte aligned.
+ */
+int ddt_compact_kv(void* ckv, int64_t ld_ckv, void* kpe, int64_t ld_kpe, int dtype, int d_lat,
+                   int d_rope, const int64_t* kv_base, int32_t* prefix_len, const int32_t* path,
+                   const int32_t* accept_len, int B, int N, int32_t* src_slot, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DDT_H */

@@ -1,0 +1,223 @@
+"""Thin ctypes binding over libddt.so (include/ddt.h).
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+Tensors are torch CUDA tensors (torch supplies device memory and the
+current stream); host-side arrays (prefix lengths for planning) are numpy
+arrays or lists.  Outputs that are not passed in are allocated with torch.
+The library must be built (``python -m mla_tree_verify_parents_amd.build``);
+loading fails loudly otherwise -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+from .build import LIB
+
+DDT_F32, DDT_BF16 = 0, 1
+MAX_NODES = 1024
+MAX_BATCH = 128
+
+_lib = None
+
+
+class DdtError(RuntimeError):
+    pass
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("H", ctypes.c_int), ("N", ctypes.c_int),
+                ("d_lat", ctypes.c_int), ("d_rope", ctypes.c_int), ("dtype", ctypes.c_int),
+                ("scale", ctypes.c_float), ("kv_chunk", ctypes.c_int),
+                ("ld_ql", ctypes.c_int64), ("ld_qp", ctypes.c_int64),
+                ("ld_ckv", ctypes.c_int64), ("ld_kpe", ctypes.c_int64)]
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            raise DdtError(f"{LIB} is not built; run `python -m mla_tree_verify_parents_amd.build`")
+        L = ctypes.CDLL(LIB)
+        P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+        L.ddt_version.argtypes = []
+        L.ddt_status_string.argtypes = [i32]
+        L.ddt_status_string.restype = ctypes.c_char_p
+        L.ddt_build_mask.argtypes = [P, i32, i32, P, P, P, P]
+        L.ddt_verify_workspace.argtypes = [ctypes.POINTER(AttnDesc), P, ctypes.POINTER(sz)]
+        L.ddt_verify_attn.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P, P, P, P, sz, P]
+        L.ddt_argmax_workspace.argtypes = [i64, i64, ctypes.POINTER(sz)]
+        L.ddt_argmax.argtypes = [P, i32, i64, i64, i64, P, P, sz, P]
+        L.ddt_greedy_accept.argtypes = [P, P, P, i32, i32, P, P, P, P]
+        L.ddt_compact_kv.argtypes = [P, i64, P, i64, i32, i32, i32, P, P, P, P, i32, i32, P, P]
+        for f in ("ddt_version", "ddt_build_mask", "ddt_verify_workspace", "ddt_verify_attn",
+                  "ddt_argmax_workspace", "ddt_argmax", "ddt_greedy_accept", "ddt_compact_kv"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise DdtError(f"{what}: {lib().ddt_status_string(rc).decode()} ({rc})")
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t, dtype, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _contig(t, dtype, name):
+    _dev(t, dtype, name)
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _rows(t, name):
+    """2-D view with unit column stride -> row stride in elements."""
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D view with unit column stride")
+    return t.stride(0)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return DDT_F32
+    if t.dtype == torch.bfloat16:
+        return DDT_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def build_mask(parents, mask=None, depth=None, tree_err=None, stream=None):
+    """parents [B, N] int32 -> (mask [B, N, W] int64 bit words, depth [B, N], tree_err [B])."""
+    _contig(parents, torch.int32, "parents")
+    B, N = parents.shape
+    W = (N + 63) // 64
+    dev = parents.device
+    if mask is None:
+        mask = torch.empty((B, N, W), dtype=torch.int64, device=dev)
+    if depth is None:
+        depth = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if tree_err is None:
+        tree_err = torch.empty((B,), dtype=torch.int32, device=dev)
+    _check(lib().ddt_build_mask(_p(parents), B, N, _p(mask), _p(depth), _p(tree_err), _stream(stream)),
+           "ddt_build_mask")
+    return mask, depth, tree_err
+
+
+def attn_desc(q_lat, q_pe, ckv, kpe, *, B, H, N, scale, kv_chunk=0):
+    return AttnDesc(B, H, N, q_lat.shape[1], q_pe.shape[1], _dtype_code(q_lat), float(scale), int(kv_chunk),
+                    _rows(q_lat, "q_lat"), _rows(q_pe, "q_pe"), _rows(ckv, "ckv"), _rows(kpe, "kpe"))
+
+
+def verify_workspace_bytes(desc: AttnDesc, prefix_len_host) -> int:
+    pl = np.ascontiguousarray(prefix_len_host, dtype=np.int32)
+    n = ctypes.c_size_t(0)
+    _check(lib().ddt_verify_workspace(ctypes.byref(desc), pl.ctypes.data, ctypes.byref(n)),
+           "ddt_verify_workspace")
+    return n.value
+
+
+def verify_attn(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, *, H, scale, out=None, lse=None,
+                workspace=None, kv_chunk=0, stream=None):
+    """Tree-verify attention.  q_lat [B*N*H, d_lat], q_pe [B*N*H, d_rope] (2-D views),
+    ckv [pool, d_lat], kpe [pool, d_rope] (2-D views of the cache pool), kv_base [B]
+    int64 (device), prefix_len_host [B] (host), mask [B, N, W] from build_mask.
+    Returns (out [B*N*H, d_lat], lse [B*N*H] fp32)."""
+    for t, n in ((q_lat, "q_lat"), (q_pe, "q_pe"), (ckv, "ckv"), (kpe, "kpe")):
+        _dev(t, q_lat.dtype, n)
+    _contig(kv_base, torch.int64, "kv_base")
+    _contig(mask, torch.int64, "mask")
+    B, N = mask.shape[0], mask.shape[1]
+    rows = B * N * H
+    if q_lat.shape[0] != rows or q_pe.shape[0] != rows:
+        raise ValueError("q rows must be B*N*H")
+    pl = np.ascontiguousarray(prefix_len_host, dtype=np.int32)
+    if pl.shape != (B,):
+        raise ValueError("prefix_len_host must have B entries")
+    desc = attn_desc(q_lat, q_pe, ckv, kpe, B=B, H=H, N=N, scale=scale, kv_chunk=kv_chunk)
+    if out is None:
+        out = torch.empty((rows, q_lat.shape[1]), dtype=q_lat.dtype, device=q_lat.device)
+    if lse is None:
+        lse = torch.empty((rows,), dtype=torch.float32, device=q_lat.device)
+    _contig(out, q_lat.dtype, "out")
+    _contig(lse, torch.float32, "lse")
+    need = verify_workspace_bytes(desc, pl)
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=q_lat.device)
+    ws_n = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().ddt_verify_attn(ctypes.byref(desc), _p(q_lat), _p(q_pe), _p(ckv), _p(kpe), _p(kv_base),
+                                 pl.ctypes.data, _p(mask), _p(out), _p(lse), _p(workspace), ws_n,
+                                 _stream(stream)), "ddt_verify_attn")
+    return out, lse
+
+
+def argmax_workspace_bytes(rows: int, V: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().ddt_argmax_workspace(rows, V, ctypes.byref(n)), "ddt_argmax_workspace")
+    return n.value
+
+
+def argmax(logits, idx=None, workspace=None, stream=None):
+    """logits [rows, V] fp32/bf16 (2-D view) -> idx [rows] int32."""
+    _dev(logits, None, "logits")
+    ld = _rows(logits, "logits")
+    rows, V = logits.shape
+    if idx is None:
+        idx = torch.empty((rows,), dtype=torch.int32, device=logits.device)
+    _contig(idx, torch.int32, "idx")
+    need = argmax_workspace_bytes(rows, V)
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=logits.device)
+    ws_n = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().ddt_argmax(_p(logits), _dtype_code(logits), rows, V, ld, _p(idx), _p(workspace), ws_n,
+                            _stream(stream)), "ddt_argmax")
+    return idx
+
+
+def greedy_accept(target_ids, draft_ids, parents, accept_len=None, path=None, tokens=None, stream=None):
+    """-> (accept_len [B], path [B, N], tokens [B, N]) int32 device tensors."""
+    for t, n in ((target_ids, "target_ids"), (draft_ids, "draft_ids"), (parents, "parents")):
+        _contig(t, torch.int32, n)
+    B, N = parents.shape
+    dev = parents.device
+    if accept_len is None:
+        accept_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    if path is None:
+        path = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if tokens is None:
+        tokens = torch.empty((B, N), dtype=torch.int32, device=dev)
+    _check(lib().ddt_greedy_accept(_p(target_ids), _p(draft_ids), _p(parents), B, N, _p(accept_len), _p(path),
+                                   _p(tokens), _stream(stream)), "ddt_greedy_accept")
+    return accept_len, path, tokens
+
+
+def compact_kv(ckv, kpe, kv_base, prefix_len, path, accept_len, src_slot=None, stream=None):
+    """In-place compaction of the cache pool views; prefix_len [B] int32 (device) is updated."""
+    _dev(ckv, None, "ckv")
+    _dev(kpe, ckv.dtype, "kpe")
+    _contig(kv_base, torch.int64, "kv_base")
+    _contig(prefix_len, torch.int32, "prefix_len")
+    _contig(path, torch.int32, "path")
+    _contig(accept_len, torch.int32, "accept_len")
+    B, N = path.shape
+    _check(lib().ddt_compact_kv(_p(ckv), _rows(ckv, "ckv"), _p(kpe), _rows(kpe, "kpe"), _dtype_code(ckv),
+                                ckv.shape[1], kpe.shape[1], _p(kv_base), _p(prefix_len), _p(path),
+                                _p(accept_len), B, N, _p(src_slot), _stream(stream)), "ddt_compact_kv")
+    return prefix_len, src_slot

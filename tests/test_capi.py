@@ -1,0 +1,67 @@
+"""CPU checks of the C ABI: the built library loads and exports every
+function include/ddt.h declares, and host-side argument validation rejects
+bad calls before anything reaches the GPU (no kernel is launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mla_tree_verify_parents_amd import build, ddt
+
+HEADER = os.path.join(build.ROOT, "include", "ddt.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ddt_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(build.LIB):
+        build.build()
+    return ddt.lib()
+
+
+def test_header_declares_the_path():
+    names = declared_functions()
+    for f in ("ddt_build_mask", "ddt_verify_attn", "ddt_verify_workspace", "ddt_argmax",
+              "ddt_argmax_workspace", "ddt_greedy_accept", "ddt_compact_kv"):
+        assert f in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    missing = [f for f in declared_functions() if not hasattr(lib, f)]
+    assert not missing, missing
+
+
+def test_version_and_status_strings(lib):
+    assert lib.ddt_version() >= 100
+    assert b"EINVAL" in lib.ddt_status_string(-1)
+    assert b"OK" in lib.ddt_status_string(0)
+
+
+def test_host_side_validation(lib):
+    null = None
+    # N out of range / negative B: rejected before any launch
+    assert lib.ddt_build_mask(null, 1, 0, null, null, null, null) == -1
+    assert lib.ddt_build_mask(null, 1, 1025, null, null, null, null) == -1
+    assert lib.ddt_build_mask(null, -1, 4, null, null, null, null) == -1
+    assert lib.ddt_build_mask(null, 0, 4, null, null, null, null) == 0      # nothing to do
+    assert lib.ddt_greedy_accept(null, null, null, 2, 0, null, null, null, null) == -1
+    assert lib.ddt_argmax(null, 0, 4, 10, 5, null, null, 0, null) == -1     # ld < V
+    assert lib.ddt_argmax(null, 7, 4, 10, 10, null, null, 0, null) == -2    # dtype
+    assert lib.ddt_compact_kv(null, 576, null, 576, 1, 512, 64, null, null, null, null, 1, 0, null, null) == -1
+    d = ddt.AttnDesc(1, 8, 64, 512, 64, ddt.DDT_BF16, 0.04, 0, 576, 576, 576, 576)
+    pl = (ctypes.c_int32 * 1)(100)
+    n = ctypes.c_size_t(0)
+    bad = ddt.AttnDesc(1, 8, 64, 256, 64, ddt.DDT_BF16, 0.04, 0, 576, 576, 576, 576)
+    assert lib.ddt_verify_workspace(ctypes.byref(bad), pl, ctypes.byref(n)) == -2   # not built
+    bad = ddt.AttnDesc(1, 8, 64, 512, 64, ddt.DDT_BF16, 0.04, 0, 577, 576, 576, 576)
+    assert lib.ddt_verify_workspace(ctypes.byref(bad), pl, ctypes.byref(n)) == -1   # stride alignment
+    bad = ddt.AttnDesc(129, 8, 64, 512, 64, ddt.DDT_BF16, 0.04, 0, 576, 576, 576, 576)
+    assert lib.ddt_verify_workspace(ctypes.byref(bad), pl, ctypes.byref(n)) == -1   # batch limit
+    assert lib.ddt_verify_attn(ctypes.byref(d), null, null, null, null, null, pl, null, null, null,
+                               null, 0, null) == -1

@@ -1,0 +1,233 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle on the
+same seeded inputs.  Discrete outputs (mask, depth, argmax, accept, paths,
+tokens, compacted rows, lengths) must match bit for bit; attention outputs
+within relative L2 1e-5 (fp32 inputs) / 1e-2 (bf16 inputs, fp32 accumulate)."""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+from mla_tree_verify_parents_amd import ddt, synth
+from tests.helpers import ATTN_TOL, DevWorkload, as_f64, oracle_attn, rel_l2, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def all_parent_arrays(N):
+    for tail in itertools.product(*[range(i) for i in range(1, N)]):
+        yield np.array((-1,) + tail, np.int32)
+
+
+# ----------------------------------------------------------------- mask ----
+
+def _mask_check(orc, pars):
+    m, d, e = ddt.build_mask(to_dev(pars))
+    torch.cuda.synchronize()
+    om, od, oe = orc.build_mask(pars)
+    assert (to_host(m).view(np.uint64) == om).all()
+    assert (to_host(d) == od).all()
+    assert (to_host(e) == oe).all()
+
+
+@pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_mask_every_tree(orc, N):
+    _mask_check(orc, np.stack(list(all_parent_arrays(N))))
+
+
+@pytest.mark.parametrize("N", [63, 64, 65, 130, 1024])
+def test_mask_random_chain_star(orc, N):
+    rng = np.random.default_rng(N)
+    pars = synth.random_parents(rng, 5, N)
+    pars[3] = np.arange(-1, N - 1)
+    pars[4] = 0
+    pars[4, 0] = -1
+    _mask_check(orc, pars)
+
+
+def test_mask_invalid_trees(orc):
+    pars = np.array([[-1, 0, 1, 2], [0, 0, 1, 2], [-1, 1, 0, 0], [-1, 0, 3, 1], [-1, -1, 0, 1]], np.int32)
+    _mask_check(orc, pars)
+
+
+# --------------------------------------------------------------- accept ----
+
+@pytest.mark.parametrize("N", [1, 2, 3, 4, 5])
+def test_accept_exhaustive_vocab2(orc, N):
+    cases = [(p, (5,) + d, t) for p in all_parent_arrays(N)
+             for d in itertools.product((0, 1), repeat=N - 1)
+             for t in itertools.product((0, 1), repeat=N)]
+    par = np.stack([c[0] for c in cases])
+    dr = np.array([c[1] for c in cases], np.int32)
+    tt = np.array([c[2] for c in cases], np.int32)
+    acc, path, tok = ddt.greedy_accept(to_dev(tt), to_dev(dr), to_dev(par))
+    oa, op, ot = orc.greedy_accept(tt, dr, par)
+    assert (to_host(acc) == oa).all() and (to_host(path) == op).all() and (to_host(tok) == ot).all()
+
+
+@pytest.mark.parametrize("N,V", [(64, 3), (200, 2), (1024, 2), (1024, 100)])
+def test_accept_random(orc, N, V):
+    rng = np.random.default_rng(N + V)
+    B = 16
+    par = synth.random_parents(rng, B, N)
+    par[0] = np.arange(-1, N - 1)               # a chain: the walk can go N-1 deep
+    dr = rng.integers(0, V, size=(B, N)).astype(np.int32)
+    t = synth.planted_targets(rng, par, dr, V, 0.8)
+    t[0, :-1] = dr[0, 1:]
+    acc, path, tok = ddt.greedy_accept(to_dev(t), to_dev(dr), to_dev(par))
+    oa, op, ot = orc.greedy_accept(t, dr, par)
+    assert oa[0] == N - 1
+    assert (to_host(acc) == oa).all() and (to_host(path) == op).all() and (to_host(tok) == ot).all()
+
+
+# --------------------------------------------------------------- argmax ----
+
+@pytest.mark.parametrize("rows,V", [(64, 163840), (3, 1), (5, 1000), (2100, 4099), (2048, 4096), (1, 300001)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_argmax(orc, rows, V, dtype):
+    rng = np.random.default_rng(rows * 7 + V)
+    x = rng.standard_normal((rows, V)).astype(np.float32)
+    if V > 10 and rows > 4:
+        x[0, [3, V - 2]] = 40.0                     # tie -> lower index
+        x[1, :] = -3.0                              # all equal -> 0
+        x[2, V // 2] = np.nan                       # NaN wins
+        x[3, [V // 3, V - 1]] = np.nan              # first NaN wins
+        x[4, :] = -1.0
+        x[4, [5, 9]] = [-0.0, 0.0]                  # -0 == +0 -> index 5
+    if dtype == "bf16":
+        x = synth.to_bf16_bits(np.nan_to_num(x, nan=0.0))
+        x[2 % rows, V // 2] = synth.BF16_NAN
+    got = to_host(ddt.argmax(to_dev(x)))
+    assert (got == orc.argmax(x)).all()
+
+
+def test_argmax_unaligned_view(orc):
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((40, 5003)).astype(np.float32)
+    dev = to_dev(x)[:, 1:4999]                      # not 16-byte aligned rows
+    got = to_host(ddt.argmax(dev))
+    assert (got == orc.argmax(x[:, 1:4999])).all()
+
+
+# ------------------------------------------------------------ compaction ----
+
+def _tagged(rows, width, dtype):
+    r = np.arange(rows)
+    v = np.where(np.arange(width)[None, :] % 2 == 0, (r // 256)[:, None], (r % 256)[:, None]).astype(np.float32)
+    return v if dtype == "f32" else synth.to_bf16_bits(v)
+
+
+@pytest.mark.parametrize("dtype,dl,dr", [("bf16", 512, 64), ("f32", 64, 16), ("bf16", 6, 2)])
+def test_compact(orc, dtype, dl, dr):
+    N = 40
+    paths = [[0], [0, 1, 2, 3], [0, 5, 9], [0, 1, 4, 5, 39], list(range(40)), [0, 39], [0, 2, 3, 4, 5, 6, 7]]
+    B = len(paths)
+    P = np.array([3, 0, 20, 700, 1, 50, 9], np.int32)
+    cap = 800
+    base = np.array([5 + (cap + 3) * b for b in range(B)], np.int64)
+    pool = _tagged(int(base[-1]) + cap + 5, dl + dr, dtype)
+    path = np.full((B, N), -1, np.int32)
+    acc = np.zeros(B, np.int32)
+    for b, p in enumerate(paths):
+        path[b, : len(p)] = p
+        acc[b] = len(p) - 1
+    dpool = to_dev(pool)
+    dpl = to_dev(P)
+    src = torch.empty((B, N), dtype=torch.int32, device="cuda")
+    ddt.compact_kv(dpool[:, :dl], dpool[:, dl:], to_dev(base), dpl, to_dev(path), to_dev(acc), src)
+    opool = pool.copy()
+    opl, osrc = orc.compact_kv(opool[:, :dl], opool[:, dl:], base, P, path, acc)
+    assert (to_host(dpl) == opl).all()
+    assert (to_host(src) == osrc).all()
+    assert (to_host(dpool) == opool).all()
+
+
+def test_compact_separate_arrays_and_invalid(orc):
+    rng = np.random.default_rng(3)
+    ckv = rng.standard_normal((300, 64)).astype(np.float32)
+    kpe = rng.standard_normal((300, 16)).astype(np.float32)
+    P = np.array([10, 20, 30], np.int32)
+    base = np.array([0, 100, 200], np.int64)
+    path = np.array([[0, 2, 5, -1, -1, -1], [0, 1, 1, -1, -1, -1], [0, 3, -1, -1, -1, -1]], np.int32)
+    acc = np.array([2, 2, 7], np.int32)             # request 1: path not increasing, request 2: bad length
+    dc, dk = to_dev(ckv), to_dev(kpe)
+    dpl = to_dev(P)
+    src = torch.empty((3, 6), dtype=torch.int32, device="cuda")
+    ddt.compact_kv(dc, dk, to_dev(base), dpl, to_dev(path), to_dev(acc), src)
+    c2, k2 = ckv.copy(), kpe.copy()
+    orc.compact_kv(c2[0:100], k2[0:100], base[:1], P[:1], path[:1], acc[:1])
+    assert (to_host(dc) == c2).all() and (to_host(dk) == k2).all()
+    assert to_host(dpl).tolist() == [13, 20, 30]
+    s = to_host(src)
+    assert s[0].tolist() == [10, 12, 15, -1, -1, -1] and (s[1:] == -1).all()
+
+
+# ------------------------------------------------------------- attention ----
+
+def _attn_gpu(dw: DevWorkload, kv_chunk=0):
+    w = dw.w
+    mask, _, err = ddt.build_mask(dw.parents)
+    out, lse = ddt.verify_attn(dw.q_lat(), dw.q_pe(), dw.ckv(), dw.kpe(), dw.kv_base, w.prefix_len, mask,
+                               H=w.H, scale=w.scale, kv_chunk=kv_chunk)
+    torch.cuda.synchronize()
+    assert (to_host(err) == 0).all()
+    return to_host(out), to_host(lse)
+
+
+def _attn_check(orc, w, kv_chunks=(0,), rows=None):
+    dw = DevWorkload(w)
+    ref_out, ref_lse = oracle_attn(orc, w, rows=rows)
+    tol = ATTN_TOL[w.dtype]
+    results = []
+    for ch in kv_chunks:
+        out, lse = _attn_gpu(dw, ch)
+        o = as_f64(out)
+        if rows is not None:
+            o, lse = o[rows], lse[rows]
+        assert np.isfinite(o).all() and np.isfinite(lse).all()
+        e_out, e_lse = rel_l2(o, ref_out), rel_l2(lse, ref_lse)
+        print(f"{w.name} kv_chunk={ch}: rel_l2 out {e_out:.3e} lse {e_lse:.3e}")
+        assert e_out <= tol and e_lse <= tol, (ch, e_out, e_lse)
+        results.append(o)
+    return results
+
+
+def test_attn_config1_tiny_fp32(orc):
+    _attn_check(orc, synth.workload(1), kv_chunks=(0, 32, 64))
+
+
+def test_attn_config2_k2_head_share(orc):
+    w = synth.workload(2, with_logits=False)
+    _attn_check(orc, w, kv_chunks=(0, 32, 224, 4160))
+
+
+def test_attn_config3_ragged_small(orc):
+    w = synth.workload(3, B=5, prefix_range=(0, 3000))
+    _attn_check(orc, w, kv_chunks=(0, 96, 1 << 20))
+
+
+@pytest.mark.parametrize("cfg,over", [
+    (1, dict(prefix=0)),                    # no prefix: only tree keys
+    (1, dict(N=1, prefix=5)),               # budget 0: single-token decode
+    (1, dict(H=3, N=5, prefix=61)),         # 15 rows: partial row tiles, ragged key tail
+    (1, dict(H=1, N=1024, prefix=3)),       # maximum node count
+    (3, dict(B=3, N=1, prefix_range=(0, 40))),
+    (3, dict(B=2, H=1, N=1024, prefix_range=(31, 33))),
+    (2, dict(H=3, N=7, prefix=1, with_logits=False)),
+])
+def test_attn_edge_cases(orc, cfg, over):
+    _attn_check(orc, synth.workload(cfg, **over), kv_chunks=(0, 32))
+
+
+def test_attn_chain_tree_is_causal(orc):
+    """Chain tree through the whole path: equal to the oracle, which is pinned to causal SDPA."""
+    w = synth.workload(3, B=2, N=64, prefix_range=(100, 500))
+    w.parents[:] = np.arange(-1, 63)
+    _attn_check(orc, w, kv_chunks=(0, 64))
+
+
+def test_attn_config3_full_sampled(orc):
+    w = synth.workload(3)
+    rng = np.random.default_rng(0)
+    rows = np.sort(rng.choice(w.rows, 96, replace=False))
+    _attn_check(orc, w, rows=rows)
