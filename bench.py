@@ -1,0 +1,235 @@
+"""Benchmark of one DDTree verify step on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input
+already resident in HBM:
+    parents -> ancestor mask -> tree-verify MLA attention (absorbed, bf16,
+    fp32 accumulate) -> argmax over the target logits -> greedy acceptance
+    -> KV compaction (+ length update).
+The default workload is the K2-like single-GPU head share: 1 request,
+8 heads, kv_lora_rank 512 + rope 64, prefix 4096, 64 tree nodes (a
+best-first tree from seeded top-4 draft candidates), target logits over a
+163840-token vocabulary.
+
+Prints ONE JSON line.  `value` is verify-attention TFLOP/s over the whole
+step (attention FLOPs / step time); `roofline` is the verify-attention
+launch (split-KV kernel + combine) against the bf16 MFMA peak;
+`cpu_baseline` times the fp64 oracle on the host for the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
+FLOP_PER_PAIR = 2 * (512 + 64) + 2 * 512   # QK over 576 + PV over 512
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2, help="workload configuration (2, 3 or 4)")
+    ap.add_argument("--attn-reps", type=int, default=200, help="back-to-back attention launches timed for the roofline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget for the oracle timing")
+    return ap.parse_args()
+
+
+def workload_for(cfg):
+    from mla_tree_verify_parents_amd import synth
+    if cfg == 2:
+        w = synth.workload(2)                       # logits on: argmax is part of the step
+        desc = ("K2-like head share: B=1, H=8, d_lat=512, d_rope=64, bf16, prefix 4096, "
+                "64 nodes (best-first, top-4, depth<=8), target logits 64x163840 fp32")
+    elif cfg == 3:
+        w = synth.workload(3)
+        desc = "batched ragged: B=16, H=8, 512+64 bf16, prefix U[1024,32768], 32 nodes, random trees"
+    elif cfg == 4:
+        w = synth.workload(4)
+        desc = "long context: B=4, H=64, 512+64 bf16, prefix 131072, 128 nodes (best-first, top-8, depth<=4)"
+    else:
+        raise SystemExit(f"bench runs configurations 2, 3 or 4, not {cfg}")
+    return w, desc
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the verify path has no multi-GPU part); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from mla_tree_verify_parents_amd import ddt
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w, desc = workload_for(args.config)
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    pool, q = to_dev(w.pool), to_dev(w.q)
+    parents, draft = to_dev(w.parents), to_dev(w.draft_ids)
+    kv_base = to_dev(w.kv_base)
+    prefix0 = to_dev(w.prefix_len)
+    prefix = prefix0.clone()
+    logits = None if w.logits is None else to_dev(w.logits)
+    target = None if w.target_ids is None else to_dev(w.target_ids)
+    dl = w.d_lat
+    q_lat, q_pe, ckv, kpe = q[:, :dl], q[:, dl:], pool[:, :dl], pool[:, dl:]
+    B, N, H = w.B, w.N, w.H
+    W = (N + 63) // 64
+    P_host = w.prefix_len.copy()
+
+    # preallocated outputs and workspaces: the timed loop allocates nothing
+    mask = torch.empty((B, N, W), dtype=torch.int64, device=dev)
+    depth = torch.empty((B, N), dtype=torch.int32, device=dev)
+    terr = torch.empty((B,), dtype=torch.int32, device=dev)
+    out = torch.empty((w.rows, dl), dtype=q.dtype, device=dev)
+    lse = torch.empty((w.rows,), dtype=torch.float32, device=dev)
+    desc_c = ddt.attn_desc(q_lat, q_pe, ckv, kpe, B=B, H=H, N=N, scale=w.scale)
+    ws_bytes = ddt.verify_workspace_bytes(desc_c, P_host)
+    ws = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
+    tids = torch.empty((B * N,), dtype=torch.int32, device=dev)
+    am_ws = None
+    if logits is not None:
+        n = ddt.argmax_workspace_bytes(B * N, logits.shape[1])
+        am_ws = torch.empty((max(n, 1),), dtype=torch.uint8, device=dev)
+    acc = torch.empty((B,), dtype=torch.int32, device=dev)
+    path = torch.empty((B, N), dtype=torch.int32, device=dev)
+    tok = torch.empty((B, N), dtype=torch.int32, device=dev)
+
+    # every call launches on torch's current stream, so the step can be
+    # captured into a HIP graph and replayed without host launch overhead
+    def attn():
+        ddt.verify_attn(q_lat, q_pe, ckv, kpe, kv_base, P_host, mask, H=H, scale=w.scale, out=out, lse=lse,
+                        workspace=ws)
+
+    def step():
+        prefix.copy_(prefix0)                      # same committed length every step
+        ddt.build_mask(parents, mask, depth, terr)
+        attn()
+        if logits is not None:
+            ddt.argmax(logits, tids, am_ws)
+            t = tids.view(B, N)
+        else:
+            t = target
+        ddt.greedy_accept(t, draft, parents, acc, path, tok)
+        ddt.compact_kv(ckv, kpe, kv_base, prefix, path, acc)
+
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            step()
+    torch.cuda.synchronize()
+    g_step = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_step):
+        step()
+    g_attn = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_attn):
+        for _ in range(args.attn_reps):
+            attn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        g_step.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        g_step.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # the dominant launch alone: attn_reps back-to-back calls in one graph
+    g_attn.replay()
+    torch.cuda.synchronize()
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record(stream)
+    g_attn.replay()
+    a1.record(stream)
+    torch.cuda.synchronize()
+    ms_attn = a0.elapsed_time(a1) / args.attn_reps
+
+    pairs = w.visible_pairs()
+    flops = pairs * FLOP_PER_PAIR
+    keys = int(w.keys().sum())
+    attn_bytes = keys * (dl + w.d_rope) * 2 + w.rows * ((dl + w.d_rope) * 2 + dl * 2 + 4)
+    achieved = flops / (ms_attn * 1e-3) / 1e12
+
+    res = {
+        "metric": "verify-attn TFLOP/s + cache tokens/s; % of MFMA/HBM roofline, 1xMI355X",
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) latents and queries, best-first draft tree, N(0,1)+boost logits)",
+        "config": {"workload": f"config{args.config} {desc}", "requests": B, "heads": H, "nodes": N,
+                   "cache_tokens": keys, "visible_pairs": pairs, "attn_flop_per_step": flops},
+        "cache_tokens_per_s": round(keys / (ms_step * 1e-3), 1),
+        "verify_attn_ms": round(ms_attn, 5),
+        "verify_attn_cache_tokens_per_s": round(keys / (ms_attn * 1e-3), 1),
+        "roofline": {"bound": "mfma", "kernel": "verify_split+verify_combine (ddt_verify_attn)",
+                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "algorithmic_bytes": attn_bytes,
+                     "achieved_GBps": round(attn_bytes / (ms_attn * 1e-3) / 1e9, 1)},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, flops)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(w, budget_s, flops):
+    """Time the fp64 oracle on the host for the same verify step (all rows of
+    the attention, mask, argmax, accept, compaction), repeated while within
+    the time budget (at least once)."""
+    from oracle import oracle
+
+    oracle.lib()
+    reps, t_att, t_rest = 0, 0.0, 0.0
+    while True:
+        t0 = time.perf_counter()
+        oracle.build_mask(w.parents)
+        oracle.verify_attn(w.q_lat(), w.q_pe(), w.ckv(), w.kpe(), w.kv_base, w.prefix_len, w.parents,
+                           H=w.H, scale=w.scale)
+        t1 = time.perf_counter()
+        t = oracle.argmax(w.logits).reshape(w.B, w.N) if w.logits is not None else w.target_ids
+        a, pth, _ = oracle.greedy_accept(t, w.draft_ids, w.parents)
+        pool = w.pool.copy()
+        oracle.compact_kv(pool[:, :w.d_lat], pool[:, w.d_lat:], w.kv_base, w.prefix_len, pth, a)
+        t2 = time.perf_counter()
+        reps += 1
+        t_att += t1 - t0
+        t_rest += t2 - t1
+        if t_att + t_rest >= budget_s or reps >= 20:
+            break
+    step_s = (t_att + t_rest) / reps
+    return {"value": round(flops / step_s / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"full verify step of the same workload, {reps} rep(s); "
+                      f"{step_s * 1e3:.1f} ms/step ({t_att / reps * 1e3:.1f} ms attention)"}
+
+
+if __name__ == "__main__":
+    main()

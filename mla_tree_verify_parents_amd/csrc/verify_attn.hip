@@ -46,36 +46,106 @@
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short short4v __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) short4v lds_short4v;
 
-constexpr int KT = 32;               // keys per tile
-constexpr int NW = 4;                // wavefronts per workgroup
-constexpr int ROWS_WG = 32 * NW;     // query rows per workgroup
+constexpr int KT = 64;               // keys per tile: 32 per wavefront of a pair
+constexpr int NW = 4;                // wavefronts per workgroup: 2 pairs
+constexpr int ROWS_WG = 64;          // query rows per workgroup: 32 per pair
 constexpr int kThreads = 64 * NW;
+constexpr int NSTAGE = 2;            // LDS ring depth
 constexpr int kMinChunk = 256;       // smallest automatic split (keys)
+constexpr int kRsrcFlags = 0x00020000;  // raw 32-bit buffer descriptor word 3
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
 
+// A key tile in LDS is two regions, each row-major with 16-byte chunks:
+//   A: c_kv,  KT rows x CA chunks    (CA = d_lat * elem / 16)
+//   B: k_pe,  KT rows x CB chunks    (CB = d_rope * elem / 16)
+// Chunk c of row r is stored at chunk c ^ sw(r) of that row.  Tiles are
+// filled by LDS-DMA (buffer_load ... lds): each 64-lane instruction writes
+// 64 consecutive chunks of one region, so every instruction reads from one
+// source array through one buffer descriptor.
 template <typename T>
 struct Traits;
 
+// bf16: MFMA 32x32x16, 8 k-values per lane.  Swizzles over the 16 LDS bank
+// groups of 16 bytes: region A rows are 1 KB and swA(r) = 4*(r%4) + (r/4)%4
+// keeps both the score reads (16 consecutive rows, one chunk) and the
+// transposed value reads (4 consecutive rows x 4 consecutive chunks) free of
+// conflicts; region B rows are 128 B and swB(r) = (r/2)%8 does the same for
+// the score reads.
 template <>
-struct Traits<uint16_t> {  // bf16 bit patterns
-    static constexpr int KPL = 8;  // k elements per lane per MFMA
+struct Traits<uint16_t> {
+    static constexpr int KPL = 8;
     using Frag = bf16x8;
     __device__ static floatx16 mfma(Frag a, Frag b, floatx16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
     }
-    __device__ static Frag load(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
-    __device__ static Frag zero() { return Frag{}; }
+    __device__ static Frag global_frag(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
     __device__ static Frag from_f32(const float* v) {
         Frag r;
 #pragma unroll
         for (int e = 0; e < 8; ++e) r[e] = static_cast<__bf16>(v[e]);
         return r;
     }
+    __device__ static constexpr int swA(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
+    __device__ static constexpr int swB(int r) { return (r >> 1) & 7; }
+
+    // Per-lane byte offsets inside a ring slot; each fragment address is one
+    // of these plus a compile-time immediate.
+    struct Lane {
+        uint32_t ka[8];     // score A operand, c_kv depth chunk 2ks+g: ka[ks & 7] + 256*(ks >> 3)
+        uint32_t kb[4];     // score A operand, k_pe depth chunk 2m+g
+        uint32_t v[2][4];   // value A operand: v[hi][c & 3] + 16*CA*16*kk + 256*(c >> 2)
+    };
+    // h: which 32-key half of the tile this wavefront scores
+    template <int DL, int DR>
+    __device__ static Lane lane_offsets(int lane, int h) {
+        constexpr int CA = DL / 8, CB = DR / 8;
+        static_assert(CA % 16 == 0 && CB == 8, "bf16 layout: c_kv rows of whole 16-chunk groups, 8-chunk k_pe rows");
+        const int g = lane >> 5, l32 = lane & 31, r = 32 * h + l32;
+        Lane L;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) L.ka[m] = (uint32_t)((r * CA + ((2 * m + g) ^ swA(r))) * 16);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) L.kb[m] = (uint32_t)((KT * CA + r * CB + ((2 * m + g) ^ swB(r))) * 16);
+        // Transposed value reads: in each 16-lane group, source lane a + 4k
+        // reads row 16kk + 8hi + 4g + k, columns 32c + 16half + 4a .. +3; the
+        // hardware hands lane 4a + e the 4 rows (keys) of column
+        // 32c + 16half + 4a + e.  swA of that row is 4k + 2hi + g.
+        const int grp = lane >> 4, s = lane & 15, a = s & 3, k = s >> 2, half = grp & 1;
+#pragma unroll
+        for (int hi = 0; hi < 2; ++hi) {
+            const int row = 8 * hi + 4 * g + k;
+#pragma unroll
+            for (int c3 = 0; c3 < 4; ++c3) {
+                const int chunk = (4 * c3 + 2 * half + (a >> 1)) ^ (4 * k + 2 * hi + g);
+                L.v[hi][c3] = (uint32_t)((row * CA + chunk) * 16 + (a & 1) * 8);
+            }
+        }
+        return L;
+    }
+    template <int DL, int DR>
+    __device__ static Frag k_frag(const char* slot, const Lane& L, int ks) {
+        constexpr int NKA = DL / 16;
+        const char* p = ks < NKA ? slot + L.ka[ks & 7] + 256 * (ks >> 3) : slot + L.kb[ks - NKA];
+        return *reinterpret_cast<const bf16x8*>(p);
+    }
+    // value A operand, 32 output columns [32c, 32c+32), key k-step kk (16 keys)
+    template <int DL, int DR>
+    __device__ static Frag v_frag(const char* slot, const Lane& L, int c, int kk) {
+        constexpr int CA = DL / 8;
+        const uint32_t imm = 16 * CA * 16 * kk + 256 * (c >> 2);
+        const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(slot + L.v[0][c & 3] + imm));
+        const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(slot + L.v[1][c & 3] + imm));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
 };
 
+// fp32: MFMA 32x32x2, 1 k-value per lane, no swizzle (small shapes only).
 template <>
 struct Traits<float> {
     static constexpr int KPL = 1;
@@ -83,10 +153,43 @@ struct Traits<float> {
     __device__ static floatx16 mfma(Frag a, Frag b, floatx16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
     }
-    __device__ static Frag load(const float* p) { return *p; }
-    __device__ static Frag zero() { return 0.f; }
+    __device__ static Frag global_frag(const float* p) { return *p; }
     __device__ static Frag from_f32(const float* v) { return v[0]; }
+    __device__ static constexpr int swA(int) { return 0; }
+    __device__ static constexpr int swB(int) { return 0; }
+    struct Lane {
+        uint32_t ka, kb, v;
+    };
+    template <int DL, int DR>
+    __device__ static Lane lane_offsets(int lane, int h) {
+        const int g = lane >> 5, l32 = lane & 31, r = 32 * h + l32;
+        return Lane{(uint32_t)((r * DL + g) * 4), (uint32_t)((KT * DL + r * DR + g) * 4),
+                    (uint32_t)((4 * g * DL + l32) * 4)};
+    }
+    // score A operand: key 32h + l32, depth 2ks + g
+    template <int DL, int DR>
+    __device__ static Frag k_frag(const char* slot, const Lane& L, int ks) {
+        constexpr int NKA = DL / 2;
+        const char* p = ks < NKA ? slot + L.ka + 8 * ks : slot + L.kb + 8 * (ks - NKA);
+        return *reinterpret_cast<const float*>(p);
+    }
+    // value A operand: column 32c + l32 of the key whose score sits at
+    // accumulator index a = kk % 16 of lane half g in key half kk / 16:
+    // key = 32*(kk/16) + 8*(a/4) + 4g + a%4.
+    template <int DL, int DR>
+    __device__ static Frag v_frag(const char* slot, const Lane& L, int c, int kk) {
+        const int key = 32 * (kk >> 4) + 8 * ((kk & 15) >> 2) + (kk & 3);
+        return *reinterpret_cast<const float*>(slot + L.v + (key * DL + 32 * c) * 4);
+    }
 };
+
+// A wave-uniform pointer, pinned to scalar registers.
+__device__ inline const char* uniform_ptr(const char* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
+}
 
 __device__ inline uint16_t f32_to_bf16_bits(float f) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f)); }
 
@@ -104,18 +207,6 @@ __device__ inline void store4<float>(float* dst, const float* v) {
     *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
 }
 
-// Position of tile key `key` (0..31) inside a V^T row.  The score
-// accumulator of lane half g holds, at index a = 4i + j, the key 8i + 4g + j;
-// the value MFMA consumes indices a in groups of KPL per k-step, lane half g
-// reading positions [ks*2*KPL + g*KPL, +KPL).  Storing each key at the
-// position its score occupies makes every A fragment one contiguous read.
-template <int KPL>
-__device__ constexpr int vt_pos(int key) {
-    const int i = key >> 3, g = (key >> 2) & 1, j = key & 3;
-    const int a = 4 * i + j;
-    return (a / KPL) * 2 * KPL + g * KPL + (a % KPL);
-}
-
 struct VerifyParams {
     const void* q_lat;
     const void* q_pe;
@@ -125,7 +216,7 @@ struct VerifyParams {
     const uint64_t* mask;
     void* out;
     float* lse;
-    float* ws_o;    // [slot][NW][NCT][4][64][4] fp32, normalised partial outputs
+    float* ws_o;    // [slot][NW][NCTW][4][64][4] fp32, normalised partial outputs
     float* ws_lse;  // [slot][ROWS_WG] fp32, log2-domain partial log-sum-exp
     int64_t ld_ql, ld_qp, ld_ckv, ld_kpe;
     int B, H, N, W, rows, row_tiles, chunk, total_wg;
@@ -140,23 +231,23 @@ struct Shape {
     using Tr = Traits<T>;
     static constexpr int KPL = Tr::KPL;
     static constexpr int DQK = DL + DR;
-    static constexpr int KSTEP = 2 * KPL;        // k per MFMA
-    static constexpr int NKS = DQK / KSTEP;      // score MFMAs per tile
-    static constexpr int NCT = DL / 32;          // 32-column output tiles
-    static constexpr int NPS = KT / KSTEP;       // value MFMA k-steps per tile
-    static constexpr int VEC = 16 / sizeof(T);   // elements per 16-byte chunk
-    static constexpr int KSTR = DQK + VEC;       // K-layout row stride (16-byte pad)
-    static constexpr int VSTR = KT + VEC;        // V^T row stride (16-byte pad)
-    static constexpr int KBUF = KT * KSTR;
-    static constexpr int VBUF = DL * VSTR;
-    static constexpr int STAGE = KBUF + VBUF;    // elements per pipeline stage
-    static constexpr int NU_C = (KT / 4) * (DL / VEC);  // c_kv staging units (4 keys x 16 B)
-    static constexpr int NU_R = KT * (DR / VEC);        // k_pe staging units (1 key x 16 B)
-    static constexpr int UC = (NU_C + kThreads - 1) / kThreads;
-    static constexpr int UR = (NU_R + kThreads - 1) / kThreads;
-    static constexpr int WS_SLOT = NW * 32 * DL;  // floats of partial output per work item
+    static constexpr int KSTEP = 2 * KPL;          // k per MFMA
+    static constexpr int NKS = DQK / KSTEP;        // score MFMAs per tile and wavefront
+    static constexpr int NCTW = DL / 64;           // 32-column output tiles per wavefront (half the columns)
+    static constexpr int NPSH = 32 / KSTEP;        // value k-steps per 32-key half
+    static constexpr int VEC = 16 / sizeof(T);     // elements per 16-byte chunk
+    static constexpr int CA = DL / VEC, CB = DR / VEC;      // chunks per row, regions A / B
+    static constexpr int RPI_A = 64 / CA, RPI_B = 64 / CB;  // rows per DMA instruction
+    static constexpr int NI_A = KT * CA / 64, NI_B = KT * CB / 64;  // DMA instructions per tile
+    static constexpr int NI = NI_A + NI_B;
+    static constexpr int DPW = NI / NW;            // DMA instructions per wavefront per tile
+    static constexpr int STAGE_BYTES = NI * 64 * 16;
+    static constexpr int XCH_BYTES = NW * NPSH * 64 * (int)sizeof(typename Tr::Frag);  // probability exchange
+    static constexpr int WS_SLOT = NW * 32 * (DL / 2);   // floats of partial output per work item
     static_assert(DL % KSTEP == 0 && DR % KSTEP == 0, "head dims must be multiples of the MFMA k");
-    static_assert(DL % 32 == 0 && DL % VEC == 0 && DR % VEC == 0, "head dims must tile");
+    static_assert(DL % 64 == 0, "each wavefront of a pair owns whole 32-column tiles");
+    static_assert(CA <= 64 && CB <= 64 && 64 % CA == 0 && 64 % CB == 0, "rows must tile DMA instructions");
+    static_assert((KT * CA) % 64 == 0 && (KT * CB) % 64 == 0 && NI % NW == 0, "regions must be whole instructions");
 };
 
 template <typename T, int DL, int DR>
@@ -165,10 +256,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     using S = Shape<T, DL, DR>;
     using Tr = typename S::Tr;
     using Frag = typename Tr::Frag;
-    constexpr int KPL = S::KPL, VEC = S::VEC;
-    __shared__ __attribute__((aligned(16))) T smem[2 * S::STAGE];
+    constexpr int KPL = S::KPL;
+    __shared__ __attribute__((aligned(16))) char smem[NSTAGE * S::STAGE_BYTES + S::XCH_BYTES];
+    __shared__ float s_stat[NW][32];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int pair = wave >> 1, h = wave & 1, partner = wave ^ 1;
+    Frag* xch = reinterpret_cast<Frag*>(smem + NSTAGE * S::STAGE_BYTES);
 
     // ---- work item: (request, key split, row tile), XCD-contiguous ----
     const int wl = ddt::xcd_logical_block(blockIdx.x, gridDim.x);
@@ -189,16 +284,58 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const int kend = min(kbeg + p.chunk, P + p.N);
     const int ntiles = (kend - kbeg + KT - 1) / KT;
     const int64_t kvb = p.kv_base[b];
-    const T* __restrict__ ckv = static_cast<const T*>(p.ckv);
-    const T* __restrict__ kpe = static_cast<const T*>(p.kpe);
+    const T* ckv = static_cast<const T*>(p.ckv);
+    const T* kpe = static_cast<const T*>(p.kpe);
+    const int64_t ldA = p.ld_ckv * (int64_t)sizeof(T), ldB = p.ld_kpe * (int64_t)sizeof(T);
 
-    const int wrow0 = rt * ROWS_WG + wave * 32;
-    const bool wave_active = wrow0 < p.rows;
-    const int row = wrow0 + l32;  // this lane's query row within the request
-    const bool row_ok = row < p.rows;
-    const int node = row_ok ? row / p.H : 0;
-    const int64_t qrow = (int64_t)b * p.rows + (row_ok ? row : 0);
+    // ---- LDS-DMA of the key tile starting at t0 into ring slot `slot` ----
+    // Instruction j of a tile writes chunks [64j, 64j+64) of the slot: rows
+    // [j*RPI, (j+1)*RPI) of region A or B.  Rows at or past the split end
+    // fall outside the descriptor's range and read as zeros (their scores
+    // are masked).
+    // Wavefront w issues instructions j = w + NW*i; with NI_A a multiple of
+    // NW the first NI_A/NW of them are region A, the rest region B, so each
+    // source pointer is a per-wavefront base plus a constant stride.
+    static_assert(S::NI_A % NW == 0, "region boundary must fall between instruction rounds");
+    constexpr int IA = S::NI_A / NW;  // region-A instructions per wavefront
+    const char* ckv_b = uniform_ptr(reinterpret_cast<const char*>(ckv + (kvb + wave * S::RPI_A) * p.ld_ckv));
+    const char* kpe_b = uniform_ptr(reinterpret_cast<const char*>(kpe + (kvb + wave * S::RPI_B) * p.ld_kpe));
+    const int ldA32 = (int)ldA, ldB32 = (int)ldB;
+    const uint32_t voffA = (uint32_t)((lane / S::CA) * ldA32);
+    const uint32_t voffB = (uint32_t)((lane / S::CB) * ldB32);
+    auto issue_tile = [&](int t0, int slot) {
+        char* sbase = smem + slot * S::STAGE_BYTES;
+        const int valid = kend - t0;
+#pragma unroll
+        for (int i = 0; i < S::DPW; ++i) {
+            const bool ra = i < IA;
+            const int jj = ra ? wave + NW * i : wave + NW * (i - IA);
+            const int rpi = ra ? S::RPI_A : S::RPI_B;
+            const int row0 = jj * rpi;
+            const int ld = ra ? ldA32 : ldB32;
+            const char* src = (ra ? ckv_b + (int64_t)(t0 + NW * rpi * i) * ld
+                                  : kpe_b + (int64_t)(t0 + NW * rpi * (i - IA)) * ld);
+            int nrows = valid - row0;
+            nrows = nrows < 0 ? 0 : (nrows > rpi ? rpi : nrows);
+            const int r = row0 + lane / (ra ? S::CA : S::CB);
+            const int chunk = ra ? (lane % S::CA) ^ Tr::swA(r) : (lane % S::CB) ^ Tr::swB(r);
+            const uint32_t voff = (ra ? voffA : voffB) + (uint32_t)(chunk * 16);
+            const __amdgpu_buffer_rsrc_t rsrc =
+                __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, nrows * ld, kRsrcFlags);
+            char* dst = sbase + ((ra ? 0 : KT * S::CA) + jj * 64) * 16;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 16, voff, 0, 0, 0);
+        }
+    };
+
+    const int wrow0 = rt * ROWS_WG + pair * 32;
+    const bool active = wrow0 < p.rows;          // same for both wavefronts of a pair
+    const bool row_ok = wrow0 + l32 < p.rows;
+    const int row = min(wrow0 + l32, p.rows - 1);  // padded rows recompute the last row, never stored
+    const int node = row / p.H;
+    const int64_t qrow = (int64_t)b * p.rows + row;
     const uint64_t* __restrict__ mrow = p.mask + ((int64_t)b * p.N + node) * p.W;
+
+    issue_tile(kbeg, 0);
 
     // ---- queries: B operand of the score MFMA, resident for the whole split ----
     Frag q[S::NKS];
@@ -207,161 +344,127 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         const int d0 = s * S::KSTEP + g * KPL;
         const T* src = d0 < DL ? static_cast<const T*>(p.q_lat) + qrow * p.ld_ql + d0
                                : static_cast<const T*>(p.q_pe) + qrow * p.ld_qp + (d0 - DL);
-        q[s] = row_ok ? Tr::load(src) : Tr::zero();
+        q[s] = Tr::global_frag(src);
     }
 
-    floatx16 o[S::NCT];
+    const typename Tr::Lane LO = Tr::template lane_offsets<DL, DR>(lane, h);
+    floatx16 o[S::NCTW];
 #pragma unroll
-    for (int c = 0; c < S::NCT; ++c) o[c] = floatx16{};
-    float m_run = -INFINITY, l_run = 0.f;
+    for (int c = 0; c < S::NCTW; ++c) o[c] = floatx16{};
+    float m_run = -INFINITY, l_run = 0.f;  // l_run: this wavefront's keys only
 
-    // ---- staging: global -> registers -> LDS (K layout + transposed V^T) ----
-    uint4 rc[S::UC][4];
-    uint4 rr[S::UR];
-    auto stage_load = [&](int t0) {
-#pragma unroll
-        for (int x = 0; x < S::UC; ++x) {
-            const int u = tid + x * kThreads;
-            const int kg = u % (KT / 4), c = u / (KT / 4);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int t = t0 + 4 * kg + j;
-                rc[x][j] = (u < S::NU_C && t < kend)
-                               ? *reinterpret_cast<const uint4*>(ckv + (kvb + t) * p.ld_ckv + c * VEC)
-                               : make_uint4(0, 0, 0, 0);
-            }
-        }
-#pragma unroll
-        for (int x = 0; x < S::UR; ++x) {
-            const int u = tid + x * kThreads;
-            const int c = u % (DR / VEC), key = u / (DR / VEC);
-            const int t = t0 + key;
-            rr[x] = (u < S::NU_R && t < kend)
-                        ? *reinterpret_cast<const uint4*>(kpe + (kvb + t) * p.ld_kpe + c * VEC)
-                        : make_uint4(0, 0, 0, 0);
-        }
-    };
-    auto stage_store = [&](int buf) {
-        T* sK = smem + buf * S::STAGE;
-        T* sV = sK + S::KBUF;
-#pragma unroll
-        for (int x = 0; x < S::UC; ++x) {
-            const int u = tid + x * kThreads;
-            if (u < S::NU_C) {
-                const int kg = u % (KT / 4), c = u / (KT / 4);
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    *reinterpret_cast<uint4*>(sK + (4 * kg + j) * S::KSTR + c * VEC) = rc[x][j];
-                if constexpr (KPL == 8) {
-                    // 4 consecutive keys land at 4 consecutive V^T positions: one 8-byte write per column
-                    const int pos = vt_pos<KPL>(4 * kg);
-#pragma unroll
-                    for (int e = 0; e < VEC; ++e) {
-                        const int sh = (e & 1) * 16;
-                        const uint32_t v0 = ((reinterpret_cast<const uint32_t*>(&rc[x][0]))[e >> 1] >> sh) & 0xffffu;
-                        const uint32_t v1 = ((reinterpret_cast<const uint32_t*>(&rc[x][1]))[e >> 1] >> sh) & 0xffffu;
-                        const uint32_t v2 = ((reinterpret_cast<const uint32_t*>(&rc[x][2]))[e >> 1] >> sh) & 0xffffu;
-                        const uint32_t v3 = ((reinterpret_cast<const uint32_t*>(&rc[x][3]))[e >> 1] >> sh) & 0xffffu;
-                        *reinterpret_cast<uint2*>(sV + (c * VEC + e) * S::VSTR + pos) =
-                            make_uint2(v0 | (v1 << 16), v2 | (v3 << 16));
-                    }
-                } else {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const T* vals = reinterpret_cast<const T*>(&rc[x][j]);
-                        const int pos = vt_pos<KPL>(4 * kg + j);
-#pragma unroll
-                        for (int e = 0; e < VEC; ++e) sV[(c * VEC + e) * S::VSTR + pos] = vals[e];
-                    }
-                }
-            }
-        }
-#pragma unroll
-        for (int x = 0; x < S::UR; ++x) {
-            const int u = tid + x * kThreads;
-            if (u < S::NU_R) {
-                const int c = u % (DR / VEC), key = u / (DR / VEC);
-                *reinterpret_cast<uint4*>(sK + key * S::KSTR + DL + c * VEC) = rr[x];
-            }
-        }
-    };
-
-    // ---- one key tile: scores, online softmax, value product ----
-    auto compute = [&](int buf, int t0) {
-        const T* sK = smem + buf * S::STAGE;
-        const T* sV = sK + S::KBUF;
-        floatx16 s = floatx16{};
-#pragma unroll
-        for (int ks = 0; ks < S::NKS; ++ks)
-            s = Tr::mfma(Tr::load(sK + l32 * S::KSTR + ks * S::KSTEP + g * KPL), q[ks], s);
-
-        float x[16];
-#pragma unroll
-        for (int v = 0; v < 16; ++v) x[v] = s[v] * p.scale_log2;
-        if (t0 + KT > P || t0 + KT > kend) {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int t = t0 + (v >> 2) * 8 + g * 4 + (v & 3);
-                bool vis = t < kend;
-                if (vis && t >= P) {
-                    const int j = t - P;
-                    vis = (mrow[j >> 6] >> (j & 63)) & 1ull;
-                }
-                if (!vis) x[v] = -INFINITY;
-            }
-        }
-        float mx = x[0];
-#pragma unroll
-        for (int v = 1; v < 16; ++v) mx = fmaxf(mx, x[v]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run, mx);
-        const float base = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - base);
-        float ps[16];
-        float rs = 0.f;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            ps[v] = __builtin_amdgcn_exp2f(x[v] - base);
-            rs += ps[v];
-        }
-        rs += __shfl_xor(rs, 32, 64);
-        l_run = l_run * alpha + rs;
-        m_run = m_new;
-        if (__ballot(alpha != 1.f) != 0) {
-#pragma unroll
-            for (int c = 0; c < S::NCT; ++c) o[c] *= alpha;
-        }
-        Frag pb[S::NPS];
-#pragma unroll
-        for (int ks = 0; ks < S::NPS; ++ks) pb[ks] = Tr::from_f32(ps + ks * KPL);
-#pragma unroll
-        for (int c = 0; c < S::NCT; ++c) {
-#pragma unroll
-            for (int ks = 0; ks < S::NPS; ++ks)
-                o[c] = Tr::mfma(Tr::load(sV + (c * 32 + l32) * S::VSTR + ks * S::KSTEP + g * KPL), pb[ks], o[c]);
-        }
-    };
-
-    stage_load(kbeg);
-    stage_store(0);
-    __syncthreads();
     for (int it = 0; it < ntiles; ++it) {
         const int t0 = kbeg + it * KT;
-        const bool more = it + 1 < ntiles;
-        if (more) stage_load(t0 + KT);
-        if (wave_active) compute(it & 1, t0);
-        if (more) stage_store((it + 1) & 1);
-        __syncthreads();
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();  // tile `it` resident; every wavefront is done with the other slot
+        if (it + 1 < ntiles) issue_tile(t0 + KT, (it + 1) & 1);
+        const char* slot = smem + (it & 1) * S::STAGE_BYTES;
+
+        // scores S^T = K . Q^T for this wavefront's 32 keys x the pair's 32 rows
+        float x[16];
+        float mx = -INFINITY;
+        if (active) {
+            // S^T over the full depth; fragment reads run 3 MFMAs ahead (one
+            // wavefront per SIMD: nothing else hides the LDS latency)
+            floatx16 s = floatx16{};
+            constexpr int AH = 3;
+            Frag f[AH + 1];
+#pragma unroll
+            for (int k = 0; k < AH; ++k) f[k] = Tr::template k_frag<DL, DR>(slot, LO, k);
+#pragma unroll
+            for (int ks = 0; ks < S::NKS; ++ks) {
+                if (ks + AH < S::NKS) f[(ks + AH) % (AH + 1)] = Tr::template k_frag<DL, DR>(slot, LO, ks + AH);
+                s = Tr::mfma(f[ks % (AH + 1)], q[ks], s);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int v = 0; v < 16; ++v) x[v] = s[v] * p.scale_log2;
+            const int th = t0 + 32 * h;
+            if (th + 32 > P || th + 32 > kend) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int t = th + (v >> 2) * 8 + g * 4 + (v & 3);
+                    bool vis = t < kend;
+                    if (vis && t >= P) {
+                        const int jn = t - P;
+                        vis = (mrow[jn >> 6] >> (jn & 63)) & 1ull;
+                    }
+                    if (!vis) x[v] = -INFINITY;
+                }
+            }
+#pragma unroll
+            for (int v = 0; v < 16; ++v) mx = fmaxf(mx, x[v]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            if (g == 0) s_stat[wave][l32] = mx;
+        }
+        __syncthreads();  // row maxima of both key halves visible
+
+        Frag pb[S::NPSH];
+        float alpha = 1.f;
+        if (active) {
+            // online softmax over the pair's 64 keys; identical m in both wavefronts
+            const float m_new = fmaxf(m_run, fmaxf(mx, s_stat[partner][l32]));
+            const float base = m_new == -INFINITY ? 0.f : m_new;
+            alpha = __builtin_amdgcn_exp2f(m_run - base);
+            float rs = 0.f;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                x[v] = __builtin_amdgcn_exp2f(x[v] - base);
+                rs += x[v];
+            }
+            rs += __shfl_xor(rs, 32, 64);
+            l_run = l_run * alpha + rs;
+            m_run = m_new;
+#pragma unroll
+            for (int j = 0; j < S::NPSH; ++j) {
+                pb[j] = Tr::from_f32(x + j * KPL);
+                xch[(wave * S::NPSH + j) * 64 + lane] = pb[j];
+            }
+        }
+        __syncthreads();  // probabilities of both key halves visible
+
+        if (active) {
+            Frag pp[S::NPSH];
+#pragma unroll
+            for (int j = 0; j < S::NPSH; ++j) pp[j] = xch[(partner * S::NPSH + j) * 64 + lane];
+            if (__ballot(alpha != 1.f) != 0) {
+#pragma unroll
+                for (int c = 0; c < S::NCTW; ++c) o[c] *= alpha;
+            }
+            // O^T (this wavefront's columns) += V^T . P^T over all 64 keys;
+            // value fragments (two transposed reads each) run 2 MFMAs ahead
+            constexpr int NM = S::NCTW * 2 * S::NPSH;
+            constexpr int AV = 2;
+            Frag vf[AV + 1];
+#pragma unroll
+            for (int m = 0; m < AV; ++m)
+                vf[m] = Tr::template v_frag<DL, DR>(slot, LO, h * S::NCTW + m / (2 * S::NPSH), m % (2 * S::NPSH));
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                const int c = m / (2 * S::NPSH), kk = m % (2 * S::NPSH);
+                if (m + AV < NM)
+                    vf[(m + AV) % (AV + 1)] = Tr::template v_frag<DL, DR>(
+                        slot, LO, h * S::NCTW + (m + AV) / (2 * S::NPSH), (m + AV) % (2 * S::NPSH));
+                const int kh = kk / S::NPSH, j = kk % S::NPSH;
+                o[c] = Tr::mfma(vf[m % (AV + 1)], kh == h ? pb[j] : pp[j], o[c]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
     }
 
-    // ---- epilogue ----
-    if (!row_ok) return;
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    const float lse2 = l_run > 0.f ? m_run + __log2f(l_run) : -INFINITY;
+    // ---- epilogue: combine the two wavefronts' sums, normalise, store ----
+    __syncthreads();
+    if (g == 0) s_stat[wave][l32] = l_run;
+    __syncthreads();
+    if (!active || !row_ok) return;
+    const float l_tot = l_run + s_stat[partner][l32];
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float lse2 = l_tot > 0.f ? m_run + __log2f(l_tot) : -INFINITY;
+    const int col0 = h * (DL / 2);
     if (p.nsplit[b] == 1) {
-        T* dst = static_cast<T*>(p.out) + qrow * DL;
+        T* dst = static_cast<T*>(p.out) + qrow * DL + col0;
 #pragma unroll
-        for (int c = 0; c < S::NCT; ++c) {
+        for (int c = 0; c < S::NCTW; ++c) {
 #pragma unroll
             for (int grp = 0; grp < 4; ++grp) {
                 float v[4];
@@ -370,11 +473,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 store4<T>(dst + c * 32 + grp * 8 + g * 4, v);
             }
         }
-        if (g == 0) p.lse[qrow] = lse2 * kLn2;
+        if (g == 0 && h == 0) p.lse[qrow] = lse2 * kLn2;
     } else {
-        float* ws = p.ws_o + ((size_t)wl * NW + wave) * (S::NCT * 4 * 64 * 4);
+        float* ws = p.ws_o + ((size_t)wl * NW + wave) * (S::NCTW * 4 * 64 * 4);
 #pragma unroll
-        for (int c = 0; c < S::NCT; ++c) {
+        for (int c = 0; c < S::NCTW; ++c) {
 #pragma unroll
             for (int grp = 0; grp < 4; ++grp) {
                 const float4 v = make_float4(o[c][grp * 4 + 0] * inv, o[c][grp * 4 + 1] * inv,
@@ -382,44 +485,45 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 *reinterpret_cast<float4*>(ws + ((c * 4 + grp) * 64 + lane) * 4) = v;
             }
         }
-        if (g == 0) p.ws_lse[(size_t)wl * ROWS_WG + wave * 32 + l32] = lse2;
+        if (g == 0 && h == 0) p.ws_lse[(size_t)wl * ROWS_WG + pair * 32 + l32] = lse2;
     }
 }
 
 // Merge the key splits of every row of multi-split requests:
 //   M = max_s lse_s, w_s = 2^(lse_s - M), out = sum_s w_s o_s / sum_s w_s,
 //   lse = (M + log2 sum_s w_s) ln 2.
-// One workgroup per (request, row tile, wavefront, 32-column tile); thread
-// (grp, lane) owns the 4 consecutive outputs the split kernel's lane `lane`
-// stored at group `grp`.
+// One workgroup per (request, row tile, wavefront, 32-column tile of that
+// wavefront); thread (grp, lane) owns the 4 consecutive outputs that the
+// split kernel's lane `lane` stored at group `grp`.
 template <typename T, int DL>
 __global__ __launch_bounds__(256) void verify_combine(const VerifyParams p) {
-    constexpr int NCT = DL / 32;
-    const int per_b = p.row_tiles * NW * NCT;
+    constexpr int NCTW = DL / 64;
+    const int per_b = p.row_tiles * NW * NCTW;
     const int b = blockIdx.x / per_b;
     const int ns = p.nsplit[b];
     if (ns <= 1) return;
     int rem = blockIdx.x - b * per_b;
-    const int rt = rem / (NW * NCT);
-    rem -= rt * (NW * NCT);
-    const int wave = rem / NCT, c = rem - (rem / NCT) * NCT;
+    const int rt = rem / (NW * NCTW);
+    rem -= rt * (NW * NCTW);
+    const int wave = rem / NCTW, c = rem - (rem / NCTW) * NCTW;
     const int grp = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 5, l32 = lane & 31;
-    const int row = rt * ROWS_WG + wave * 32 + l32;
+    const int prow = (wave >> 1) * 32 + l32;
+    const int row = rt * ROWS_WG + prow;
     if (row >= p.rows) return;
     const int64_t qrow = (int64_t)b * p.rows + row;
     float M = -INFINITY;
     for (int s = 0; s < ns; ++s) {
         const int slot = p.wg_begin[b] + s * p.row_tiles + rt;
-        M = fmaxf(M, p.ws_lse[(size_t)slot * ROWS_WG + wave * 32 + l32]);
+        M = fmaxf(M, p.ws_lse[(size_t)slot * ROWS_WG + prow]);
     }
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     float wsum = 0.f;
     for (int s = 0; s < ns; ++s) {
         const int slot = p.wg_begin[b] + s * p.row_tiles + rt;
-        const float ls = p.ws_lse[(size_t)slot * ROWS_WG + wave * 32 + l32];
+        const float ls = p.ws_lse[(size_t)slot * ROWS_WG + prow];
         const float w = ls == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ls - M);
         const float4 v = *reinterpret_cast<const float4*>(
-            p.ws_o + ((size_t)slot * NW + wave) * (NCT * 4 * 64 * 4) + ((c * 4 + grp) * 64 + lane) * 4);
+            p.ws_o + ((size_t)slot * NW + wave) * (NCTW * 4 * 64 * 4) + ((c * 4 + grp) * 64 + lane) * 4);
         acc[0] += w * v.x;
         acc[1] += w * v.y;
         acc[2] += w * v.z;
@@ -429,8 +533,8 @@ __global__ __launch_bounds__(256) void verify_combine(const VerifyParams p) {
     const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[e] *= inv;
-    store4<T>(static_cast<T*>(p.out) + qrow * DL + c * 32 + grp * 8 + g * 4, acc);
-    if (c == 0 && grp == 0 && g == 0) p.lse[qrow] = (M + __log2f(wsum)) * kLn2;
+    store4<T>(static_cast<T*>(p.out) + qrow * DL + (wave & 1) * (DL / 2) + c * 32 + grp * 8 + g * 4, acc);
+    if (c == 0 && grp == 0 && g == 0 && (wave & 1) == 0) p.lse[qrow] = (M + __log2f(wsum)) * kLn2;
 }
 
 int num_cus() {
@@ -499,7 +603,7 @@ Plan make_plan(const ddt_attn_desc* d, const int32_t* P, VerifyParams* vp) {
     pl.total_wg = (int)total;
     if (vp) vp->wg_begin[d->B] = pl.total_wg;
     if (pl.any_split) {
-        const size_t o = (size_t)pl.total_wg * NW * 32 * d->d_lat * sizeof(float);
+        const size_t o = (size_t)pl.total_wg * ROWS_WG * d->d_lat * sizeof(float);
         pl.ws_lse_off = ddt::round_up(o, 256);
         pl.ws_bytes = pl.ws_lse_off + ddt::round_up((size_t)pl.total_wg * ROWS_WG * sizeof(float), 256);
     }
@@ -511,7 +615,7 @@ int launch(const VerifyParams& vp, const Plan& pl, hipStream_t stream) {
     hipLaunchKernelGGL((verify_split<T, DL, DR>), dim3(pl.total_wg), dim3(kThreads), 0, stream, vp);
     DDT_CHECK_LAUNCH();
     if (pl.any_split) {
-        const int nblk = vp.B * pl.row_tiles * NW * (DL / 32);
+        const int nblk = vp.B * pl.row_tiles * NW * (DL / 64);
         hipLaunchKernelGGL((verify_combine<T, DL>), dim3(nblk), dim3(256), 0, stream, vp);
         DDT_CHECK_LAUNCH();
     }
