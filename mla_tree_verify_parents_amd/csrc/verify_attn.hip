@@ -51,15 +51,16 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) short4v lds_short4v;
 
-constexpr int KT = 64;               // keys per tile: 32 per wavefront of a pair
+constexpr int KT = 32;               // keys per tile
 constexpr int NW = 4;                // wavefronts per workgroup: 2 pairs
 constexpr int ROWS_WG = 64;          // query rows per workgroup: 32 per pair
 constexpr int kThreads = 64 * NW;
-constexpr int NSTAGE = 2;            // LDS ring depth
+constexpr int NSTAGE = 4;            // LDS ring depth (tiles resident or in flight)
 constexpr int kMinChunk = 256;       // smallest automatic split (keys)
 constexpr int kRsrcFlags = 0x00020000;  // raw 32-bit buffer descriptor word 3
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kSpan = 64.f;         // log2 headroom of the fixed softmax reference
 
 // A key tile in LDS is two regions, each row-major with 16-byte chunks:
 //   A: c_kv,  KT rows x CA chunks    (CA = d_lat * elem / 16)
@@ -101,12 +102,11 @@ struct Traits<uint16_t> {
         uint32_t kb[4];     // score A operand, k_pe depth chunk 2m+g
         uint32_t v[2][4];   // value A operand: v[hi][c & 3] + 16*CA*16*kk + 256*(c >> 2)
     };
-    // h: which 32-key half of the tile this wavefront scores
     template <int DL, int DR>
-    __device__ static Lane lane_offsets(int lane, int h) {
+    __device__ static Lane lane_offsets(int lane) {
         constexpr int CA = DL / 8, CB = DR / 8;
         static_assert(CA % 16 == 0 && CB == 8, "bf16 layout: c_kv rows of whole 16-chunk groups, 8-chunk k_pe rows");
-        const int g = lane >> 5, l32 = lane & 31, r = 32 * h + l32;
+        const int g = lane >> 5, l32 = lane & 31, r = l32;
         Lane L;
 #pragma unroll
         for (int m = 0; m < 8; ++m) L.ka[m] = (uint32_t)((r * CA + ((2 * m + g) ^ swA(r))) * 16);
@@ -134,7 +134,7 @@ struct Traits<uint16_t> {
         const char* p = ks < NKA ? slot + L.ka[ks & 7] + 256 * (ks >> 3) : slot + L.kb[ks - NKA];
         return *reinterpret_cast<const bf16x8*>(p);
     }
-    // value A operand, 32 output columns [32c, 32c+32), key k-step kk (16 keys)
+    // value A operand, 32 output columns [32c, 32c+32), key k-step kk (keys 16kk .. 16kk+15)
     template <int DL, int DR>
     __device__ static Frag v_frag(const char* slot, const Lane& L, int c, int kk) {
         constexpr int CA = DL / 8;
@@ -161,12 +161,12 @@ struct Traits<float> {
         uint32_t ka, kb, v;
     };
     template <int DL, int DR>
-    __device__ static Lane lane_offsets(int lane, int h) {
-        const int g = lane >> 5, l32 = lane & 31, r = 32 * h + l32;
-        return Lane{(uint32_t)((r * DL + g) * 4), (uint32_t)((KT * DL + r * DR + g) * 4),
+    __device__ static Lane lane_offsets(int lane) {
+        const int g = lane >> 5, l32 = lane & 31;
+        return Lane{(uint32_t)((l32 * DL + g) * 4), (uint32_t)((KT * DL + l32 * DR + g) * 4),
                     (uint32_t)((4 * g * DL + l32) * 4)};
     }
-    // score A operand: key 32h + l32, depth 2ks + g
+    // score A operand: key l32, depth 2ks + g
     template <int DL, int DR>
     __device__ static Frag k_frag(const char* slot, const Lane& L, int ks) {
         constexpr int NKA = DL / 2;
@@ -174,14 +174,42 @@ struct Traits<float> {
         return *reinterpret_cast<const float*>(p);
     }
     // value A operand: column 32c + l32 of the key whose score sits at
-    // accumulator index a = kk % 16 of lane half g in key half kk / 16:
-    // key = 32*(kk/16) + 8*(a/4) + 4g + a%4.
+    // accumulator index kk of lane half g: key = 8*(kk/4) + 4g + kk%4.
     template <int DL, int DR>
     __device__ static Frag v_frag(const char* slot, const Lane& L, int c, int kk) {
-        const int key = 32 * (kk >> 4) + 8 * ((kk & 15) >> 2) + (kk & 3);
+        const int key = 8 * (kk >> 2) + (kk & 3);
         return *reinterpret_cast<const float*>(slot + L.v + (key * DL + 32 * c) * 4);
     }
 };
+
+// acc *= a, element by element, without moving the accumulator out of the
+// registers it lives in (accumulation registers are not VALU operands).
+__device__ inline void scale_acc(floatx16& acc, float a) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        float e = acc[k];
+        float t;
+        asm volatile(
+            "v_accvgpr_read_b32 %1, %0\n\t"
+            "v_mul_f32 %1, %2, %1\n\t"
+            "v_accvgpr_write_b32 %0, %1"
+            : "+a"(e), "=&v"(t)
+            : "v"(a));
+        acc[k] = e;
+    }
+}
+
+// An opaque (empty) redefinition of a register value.
+template <typename V>
+__device__ inline void pin_reg(V& v) {
+    asm volatile("" : "+v"(v));
+}
+// The same, defining the value in accumulation registers (MFMA operands can
+// be read from there directly).
+template <typename V>
+__device__ inline void pin_acc(V& v) {
+    asm volatile("" : "+a"(v));
+}
 
 // A wave-uniform pointer, pinned to scalar registers.
 __device__ inline const char* uniform_ptr(const char* p) {
@@ -232,23 +260,37 @@ struct Shape {
     static constexpr int KPL = Tr::KPL;
     static constexpr int DQK = DL + DR;
     static constexpr int KSTEP = 2 * KPL;          // k per MFMA
-    static constexpr int NKS = DQK / KSTEP;        // score MFMAs per tile and wavefront
+    static constexpr int NKS = DQK / KSTEP;        // score MFMAs per tile
     static constexpr int NCTW = DL / 64;           // 32-column output tiles per wavefront (half the columns)
-    static constexpr int NPSH = 32 / KSTEP;        // value k-steps per 32-key half
+    static constexpr int NPS = KT / KSTEP;         // value k-steps per tile
     static constexpr int VEC = 16 / sizeof(T);     // elements per 16-byte chunk
     static constexpr int CA = DL / VEC, CB = DR / VEC;      // chunks per row, regions A / B
     static constexpr int RPI_A = 64 / CA, RPI_B = 64 / CB;  // rows per DMA instruction
     static constexpr int NI_A = KT * CA / 64, NI_B = KT * CB / 64;  // DMA instructions per tile
     static constexpr int NI = NI_A + NI_B;
-    static constexpr int DPW = NI / NW;            // DMA instructions per wavefront per tile
-    static constexpr int STAGE_BYTES = NI * 64 * 16;
-    static constexpr int XCH_BYTES = NW * NPSH * 64 * (int)sizeof(typename Tr::Frag);  // probability exchange
+    static constexpr int IA = (NI_A + NW - 1) / NW, IB = (NI_B + NW - 1) / NW;
+    static constexpr int DPW = IA + IB;            // DMA instructions per wavefront per tile
+    static constexpr int STAGE_BYTES = (NI + 1) * 64 * 16;  // + a spare 1 KB that surplus instructions target
     static constexpr int WS_SLOT = NW * 32 * (DL / 2);   // floats of partial output per work item
     static_assert(DL % KSTEP == 0 && DR % KSTEP == 0, "head dims must be multiples of the MFMA k");
     static_assert(DL % 64 == 0, "each wavefront of a pair owns whole 32-column tiles");
     static_assert(CA <= 64 && CB <= 64 && 64 % CA == 0 && 64 % CB == 0, "rows must tile DMA instructions");
-    static_assert((KT * CA) % 64 == 0 && (KT * CB) % 64 == 0 && NI % NW == 0, "regions must be whole instructions");
+    static_assert((KT * CA) % 64 == 0 && (KT * CB) % 64 == 0, "regions must be whole instructions");
+    static_assert(DPW * (NSTAGE - 2) < 64, "vmcnt range");
 };
+
+// Wait until at most `n` of this wavefront's vector-memory loads are
+// outstanding (the LDS-DMA loads of later tiles; loads complete in order).
+__device__ inline void wait_vmem(int n) {
+    switch (n) {
+        case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+        case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
+        case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+        case 9: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
+        case 18: asm volatile("s_waitcnt vmcnt(18)" ::: "memory"); break;
+        default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    }
+}
 
 template <typename T, int DL, int DR>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void verify_split(
@@ -257,13 +299,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     using Tr = typename S::Tr;
     using Frag = typename Tr::Frag;
     constexpr int KPL = S::KPL;
-    __shared__ __attribute__((aligned(16))) char smem[NSTAGE * S::STAGE_BYTES + S::XCH_BYTES];
-    __shared__ float s_stat[NW][32];
+    __shared__ __attribute__((aligned(16))) char smem[NSTAGE * S::STAGE_BYTES];
+    __shared__ int s_redo;
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int pair = wave >> 1, h = wave & 1, partner = wave ^ 1;
-    Frag* xch = reinterpret_cast<Frag*>(smem + NSTAGE * S::STAGE_BYTES);
+    const int pair = wave >> 1, h = wave & 1;
 
     // ---- work item: (request, key split, row tile), XCD-contiguous ----
     const int wl = ddt::xcd_logical_block(blockIdx.x, gridDim.x);
@@ -289,15 +330,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const int64_t ldA = p.ld_ckv * (int64_t)sizeof(T), ldB = p.ld_kpe * (int64_t)sizeof(T);
 
     // ---- LDS-DMA of the key tile starting at t0 into ring slot `slot` ----
-    // Instruction j of a tile writes chunks [64j, 64j+64) of the slot: rows
-    // [j*RPI, (j+1)*RPI) of region A or B.  Rows at or past the split end
-    // fall outside the descriptor's range and read as zeros (their scores
-    // are masked).
-    // Wavefront w issues instructions j = w + NW*i; with NI_A a multiple of
-    // NW the first NI_A/NW of them are region A, the rest region B, so each
-    // source pointer is a per-wavefront base plus a constant stride.
-    static_assert(S::NI_A % NW == 0, "region boundary must fall between instruction rounds");
-    constexpr int IA = S::NI_A / NW;  // region-A instructions per wavefront
+    // Instruction j of a region writes chunks [64j, 64j+64) of it: rows
+    // [j*RPI, (j+1)*RPI).  Wavefront w issues region-A instructions
+    // w, w+NW, ... then region-B instructions w, w+NW, ...; a surplus
+    // instruction (past the region's count) reads nothing into the spare
+    // 1 KB, so every wavefront issues DPW loads per tile.  Rows at or past the
+    // split end fall outside the descriptor's range and read as zeros (their
+    // scores are masked).
     const char* ckv_b = uniform_ptr(reinterpret_cast<const char*>(ckv + (kvb + wave * S::RPI_A) * p.ld_ckv));
     const char* kpe_b = uniform_ptr(reinterpret_cast<const char*>(kpe + (kvb + wave * S::RPI_B) * p.ld_kpe));
     const int ldA32 = (int)ldA, ldB32 = (int)ldB;
@@ -308,21 +347,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         const int valid = kend - t0;
 #pragma unroll
         for (int i = 0; i < S::DPW; ++i) {
-            const bool ra = i < IA;
-            const int jj = ra ? wave + NW * i : wave + NW * (i - IA);
+            const bool ra = i < S::IA;
+            const int ii = ra ? i : i - S::IA;
+            const int jj = wave + NW * ii;
+            const bool real = jj < (ra ? S::NI_A : S::NI_B);
             const int rpi = ra ? S::RPI_A : S::RPI_B;
             const int row0 = jj * rpi;
             const int ld = ra ? ldA32 : ldB32;
-            const char* src = (ra ? ckv_b + (int64_t)(t0 + NW * rpi * i) * ld
-                                  : kpe_b + (int64_t)(t0 + NW * rpi * (i - IA)) * ld);
+            const char* src = ra ? ckv_b + (int64_t)(t0 + NW * rpi * ii) * ld : kpe_b + (int64_t)(t0 + NW * rpi * ii) * ld;
             int nrows = valid - row0;
             nrows = nrows < 0 ? 0 : (nrows > rpi ? rpi : nrows);
+            if (!real) nrows = 0;
             const int r = row0 + lane / (ra ? S::CA : S::CB);
             const int chunk = ra ? (lane % S::CA) ^ Tr::swA(r) : (lane % S::CB) ^ Tr::swB(r);
             const uint32_t voff = (ra ? voffA : voffB) + (uint32_t)(chunk * 16);
             const __amdgpu_buffer_rsrc_t rsrc =
                 __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, nrows * ld, kRsrcFlags);
-            char* dst = sbase + ((ra ? 0 : KT * S::CA) + jj * 64) * 16;
+            char* dst = !real ? sbase + S::NI * 64 * 16 : sbase + ((ra ? 0 : KT * S::CA) + jj * 64) * 16;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 16, voff, 0, 0, 0);
         }
     };
@@ -335,7 +376,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const int64_t qrow = (int64_t)b * p.rows + row;
     const uint64_t* __restrict__ mrow = p.mask + ((int64_t)b * p.N + node) * p.W;
 
-    issue_tile(kbeg, 0);
+    if (tid == 0) s_redo = 0;  // read only after the loop's barriers
+    // prologue: tiles 0 .. NSTAGE-2 in flight
+#pragma unroll
+    for (int s = 0; s < NSTAGE - 1; ++s)
+        if (s < ntiles) issue_tile(kbeg + s * KT, s);
 
     // ---- queries: B operand of the score MFMA, resident for the whole split ----
     Frag q[S::NKS];
@@ -346,121 +391,152 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                                : static_cast<const T*>(p.q_pe) + qrow * p.ld_qp + (d0 - DL);
         q[s] = Tr::global_frag(src);
     }
+    // the first two mask words of this row (trees up to 128 nodes) stay in
+    // registers; larger trees fetch words per tile
+    uint64_t mreg[2] = {0, 0};
+    if (active && kend > P) {
+#pragma unroll
+        for (int w = 0; w < 2; ++w)
+            if (w < p.W) mreg[w] = mrow[w];
+    }
+    // Settle the query and mask loads here, once: passing the values through
+    // an opaque definition makes the loop's uses depend on it rather than on
+    // the loads, so no wait inside the loop can drain the tiles in flight.
+#pragma unroll
+    for (int s = 0; s < S::NKS; ++s) pin_acc(q[s]);
+#pragma unroll
+    for (int w = 0; w < 2; ++w) pin_reg(mreg[w]);
 
-    const typename Tr::Lane LO = Tr::template lane_offsets<DL, DR>(lane, h);
+    const typename Tr::Lane LO = Tr::template lane_offsets<DL, DR>(lane);
     floatx16 o[S::NCTW];
+    float m_ref = -INFINITY;   // per-row softmax reference (log2 domain)
+    float m_seen = -INFINITY;  // per-row maximum of the scores seen so far
+    float l_run = 0.f;
+    bool overflow = false;
+    for (int pass = 0;; ++pass) {
 #pragma unroll
     for (int c = 0; c < S::NCTW; ++c) o[c] = floatx16{};
-    float m_run = -INFINITY, l_run = 0.f;  // l_run: this wavefront's keys only
-
+    l_run = 0.f;
     for (int it = 0; it < ntiles; ++it) {
         const int t0 = kbeg + it * KT;
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();  // tile `it` resident; every wavefront is done with the other slot
-        if (it + 1 < ntiles) issue_tile(t0 + KT, (it + 1) & 1);
-        const char* slot = smem + (it & 1) * S::STAGE_BYTES;
+        wait_vmem(min(NSTAGE - 2, ntiles - 1 - it) * S::DPW);
+        __syncthreads();  // tile `it` resident in every wavefront's view; slot (it-1) free
+        if (it + NSTAGE - 1 < ntiles) issue_tile(t0 + (NSTAGE - 1) * KT, (it + NSTAGE - 1) % NSTAGE);
+        if (!active) continue;
+        const char* slot = smem + (it % NSTAGE) * S::STAGE_BYTES;
 
-        // scores S^T = K . Q^T for this wavefront's 32 keys x the pair's 32 rows
-        float x[16];
-        float mx = -INFINITY;
-        if (active) {
-            // S^T over the full depth; fragment reads run 3 MFMAs ahead (one
-            // wavefront per SIMD: nothing else hides the LDS latency)
-            floatx16 s = floatx16{};
-            constexpr int AH = 3;
-            Frag f[AH + 1];
+        // scores S^T = K . Q^T (32 keys x the pair's 32 rows), both
+        // wavefronts of the pair alike.  NACC interleaved accumulators keep
+        // consecutive MFMAs independent; fragment reads run 3 MFMAs ahead.
+        constexpr int NACC = 2;
+        floatx16 sa[NACC];
 #pragma unroll
-            for (int k = 0; k < AH; ++k) f[k] = Tr::template k_frag<DL, DR>(slot, LO, k);
+        for (int a = 0; a < NACC; ++a) sa[a] = floatx16{};
+        constexpr int AH = 3;
+        Frag f[AH + 1];
 #pragma unroll
-            for (int ks = 0; ks < S::NKS; ++ks) {
-                if (ks + AH < S::NKS) f[(ks + AH) % (AH + 1)] = Tr::template k_frag<DL, DR>(slot, LO, ks + AH);
-                s = Tr::mfma(f[ks % (AH + 1)], q[ks], s);
-                __builtin_amdgcn_sched_barrier(0);
-            }
+        for (int k = 0; k < AH; ++k) f[k] = Tr::template k_frag<DL, DR>(slot, LO, k);
 #pragma unroll
-            for (int v = 0; v < 16; ++v) x[v] = s[v] * p.scale_log2;
-            const int th = t0 + 32 * h;
-            if (th + 32 > P || th + 32 > kend) {
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int t = th + (v >> 2) * 8 + g * 4 + (v & 3);
-                    bool vis = t < kend;
-                    if (vis && t >= P) {
-                        const int jn = t - P;
-                        vis = (mrow[jn >> 6] >> (jn & 63)) & 1ull;
-                    }
-                    if (!vis) x[v] = -INFINITY;
-                }
-            }
-#pragma unroll
-            for (int v = 0; v < 16; ++v) mx = fmaxf(mx, x[v]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            if (g == 0) s_stat[wave][l32] = mx;
+        for (int ks = 0; ks < S::NKS; ++ks) {
+            if (ks + AH < S::NKS) f[(ks + AH) % (AH + 1)] = Tr::template k_frag<DL, DR>(slot, LO, ks + AH);
+            sa[ks % NACC] = Tr::mfma(f[ks % (AH + 1)], q[ks], sa[ks % NACC]);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        __syncthreads();  // row maxima of both key halves visible
+        float x[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) x[v] = (sa[0][v] + sa[1][v]) * p.scale_log2;
 
-        Frag pb[S::NPSH];
-        float alpha = 1.f;
-        if (active) {
-            // online softmax over the pair's 64 keys; identical m in both wavefronts
-            const float m_new = fmaxf(m_run, fmaxf(mx, s_stat[partner][l32]));
-            const float base = m_new == -INFINITY ? 0.f : m_new;
-            alpha = __builtin_amdgcn_exp2f(m_run - base);
-            float rs = 0.f;
+        // tree part and split tail: keys [t0, t0+32) touch at most two mask words
+        if (t0 + KT > P || t0 + KT > kend) {
+            const int wlo = (t0 - P > 0 ? t0 - P : 0) >> 6;
+            uint64_t mw0, mw1;
+            if (wlo == 0) {
+                mw0 = mreg[0];
+                mw1 = mreg[1];
+            } else {
+                mw0 = mrow[wlo < p.W ? wlo : p.W - 1];
+                mw1 = mrow[wlo + 1 < p.W ? wlo + 1 : p.W - 1];
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            }
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                x[v] = __builtin_amdgcn_exp2f(x[v] - base);
-                rs += x[v];
-            }
-            rs += __shfl_xor(rs, 32, 64);
-            l_run = l_run * alpha + rs;
-            m_run = m_new;
-#pragma unroll
-            for (int j = 0; j < S::NPSH; ++j) {
-                pb[j] = Tr::from_f32(x + j * KPL);
-                xch[(wave * S::NPSH + j) * 64 + lane] = pb[j];
+                const int t = t0 + (v >> 2) * 8 + g * 4 + (v & 3);
+                const int jn = t - P;
+                // bit (jn mod 64) of the word holding jn, tested with 32-bit operations
+                const uint64_t word = (jn >> 6) == wlo ? mw0 : mw1;
+                const uint32_t half = (jn & 32) ? (uint32_t)(word >> 32) : (uint32_t)word;
+                const uint32_t vis = (uint32_t)(t < kend) & ((uint32_t)(t < P) | ((half >> (jn & 31)) & 1u));
+                x[v] = vis ? x[v] : -INFINITY;
             }
         }
-        __syncthreads();  // probabilities of both key halves visible
+        // softmax against a fixed per-row reference m_ref: the max of the
+        // first tile in which the row sees any key (O is still zero then).
+        // Probabilities 2^(x - m_ref) stay finite unless a later score
+        // exceeds m_ref by more than kSpan; then the wavefront pair flags
+        // the split and it is recomputed with the split's maximum as the
+        // reference.  No accumulator is ever rescaled in the loop.
+        float mx = fmaxf(x[0], x[1]);
+#pragma unroll
+        for (int v = 2; v < 16; ++v) mx = fmaxf(mx, x[v]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        m_seen = fmaxf(m_seen, mx);
+        if (m_ref == -INFINITY) m_ref = mx;          // first visible keys of this row
+        overflow |= mx > m_ref + kSpan;
+        const float base = m_ref == -INFINITY ? 0.f : m_ref;
+        float rs = 0.f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            x[v] = __builtin_amdgcn_exp2f(x[v] - base);
+            rs += x[v];
+        }
+        rs += __shfl_xor(rs, 32, 64);
+        l_run += rs;
+        Frag pb[S::NPS];
+#pragma unroll
+        for (int j = 0; j < S::NPS; ++j) pb[j] = Tr::from_f32(x + j * KPL);
 
-        if (active) {
-            Frag pp[S::NPSH];
+        // O^T (this wavefront's 256 columns) += V^T . P^T, key step outer
+        // and column tile inner so consecutive MFMAs are independent; value
+        // fragments (two transposed reads each) run 2 MFMAs ahead
+        constexpr int NM = S::NCTW * S::NPS;
+        constexpr int AV = 2;
+        Frag vf[AV + 1];
 #pragma unroll
-            for (int j = 0; j < S::NPSH; ++j) pp[j] = xch[(partner * S::NPSH + j) * 64 + lane];
-            if (__ballot(alpha != 1.f) != 0) {
+        for (int m = 0; m < AV; ++m) vf[m] = Tr::template v_frag<DL, DR>(slot, LO, h * S::NCTW + m % S::NCTW, m / S::NCTW);
 #pragma unroll
-                for (int c = 0; c < S::NCTW; ++c) o[c] *= alpha;
-            }
-            // O^T (this wavefront's columns) += V^T . P^T over all 64 keys;
-            // value fragments (two transposed reads each) run 2 MFMAs ahead
-            constexpr int NM = S::NCTW * 2 * S::NPSH;
-            constexpr int AV = 2;
-            Frag vf[AV + 1];
-#pragma unroll
-            for (int m = 0; m < AV; ++m)
-                vf[m] = Tr::template v_frag<DL, DR>(slot, LO, h * S::NCTW + m / (2 * S::NPSH), m % (2 * S::NPSH));
-#pragma unroll
-            for (int m = 0; m < NM; ++m) {
-                const int c = m / (2 * S::NPSH), kk = m % (2 * S::NPSH);
-                if (m + AV < NM)
-                    vf[(m + AV) % (AV + 1)] = Tr::template v_frag<DL, DR>(
-                        slot, LO, h * S::NCTW + (m + AV) / (2 * S::NPSH), (m + AV) % (2 * S::NPSH));
-                const int kh = kk / S::NPSH, j = kk % S::NPSH;
-                o[c] = Tr::mfma(vf[m % (AV + 1)], kh == h ? pb[j] : pp[j], o[c]);
-                __builtin_amdgcn_sched_barrier(0);
-            }
+        for (int m = 0; m < NM; ++m) {
+            if (m + AV < NM)
+                vf[(m + AV) % (AV + 1)] =
+                    Tr::template v_frag<DL, DR>(slot, LO, h * S::NCTW + (m + AV) % S::NCTW, (m + AV) / S::NCTW);
+            o[m % S::NCTW] = Tr::mfma(vf[m % (AV + 1)], pb[m / S::NCTW], o[m % S::NCTW]);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
-    // ---- epilogue: combine the two wavefronts' sums, normalise, store ----
+    // A second pass only if some wavefront saw a score too far above its
+    // reference; the decision is workgroup-wide (the tile loop has barriers).
+    if (pass == 1) break;
+    if (__ballot(overflow) != 0 && lane == 0) s_redo = 1;
     __syncthreads();
-    if (g == 0) s_stat[wave][l32] = l_run;
-    __syncthreads();
+    if (s_redo == 0) break;
+    m_ref = m_seen;
+    overflow = false;
+#pragma unroll
+    for (int s = 0; s < NSTAGE - 1; ++s)
+        if (s < ntiles) issue_tile(kbeg + s * KT, s);
+    }
+
+    // ---- epilogue: normalise and store this wavefront's columns ----
     if (!active || !row_ok) return;
-    const float l_tot = l_run + s_stat[partner][l32];
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const float lse2 = l_tot > 0.f ? m_run + __log2f(l_tot) : -INFINITY;
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    const float lse2 = l_run > 0.f ? m_ref + __log2f(l_run) : -INFINITY;
     const int col0 = h * (DL / 2);
+    // normalise in the accumulator registers first, so the loop never has to
+    // keep a second copy of O ready for this point
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+    for (int c = 0; c < S::NCTW; ++c) scale_acc(o[c], inv);
+    asm volatile("s_nop 7" ::: "memory");
     if (p.nsplit[b] == 1) {
         T* dst = static_cast<T*>(p.out) + qrow * DL + col0;
 #pragma unroll
@@ -469,7 +545,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             for (int grp = 0; grp < 4; ++grp) {
                 float v[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = o[c][grp * 4 + e] * inv;
+                for (int e = 0; e < 4; ++e) v[e] = o[c][grp * 4 + e];
                 store4<T>(dst + c * 32 + grp * 8 + g * 4, v);
             }
         }
@@ -480,8 +556,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         for (int c = 0; c < S::NCTW; ++c) {
 #pragma unroll
             for (int grp = 0; grp < 4; ++grp) {
-                const float4 v = make_float4(o[c][grp * 4 + 0] * inv, o[c][grp * 4 + 1] * inv,
-                                             o[c][grp * 4 + 2] * inv, o[c][grp * 4 + 3] * inv);
+                const float4 v = make_float4(o[c][grp * 4 + 0], o[c][grp * 4 + 1], o[c][grp * 4 + 2], o[c][grp * 4 + 3]);
                 *reinterpret_cast<float4*>(ws + ((c * 4 + grp) * 64 + lane) * 4) = v;
             }
         }

@@ -231,3 +231,17 @@ def test_attn_config3_full_sampled(orc):
     rng = np.random.default_rng(0)
     rows = np.sort(rng.choice(w.rows, 96, replace=False))
     _attn_check(orc, w, rows=rows)
+
+
+@pytest.mark.parametrize("factor", [100.0, 1e4])
+def test_attn_large_score_range(orc, factor):
+    """Some cache rows far into each request scaled up so their scores exceed
+    the first tiles' by many orders of magnitude: the kernel's fixed softmax
+    reference must be abandoned (second pass) without losing accuracy."""
+    w = synth.workload(3, B=3, prefix_range=(600, 2000))
+    rng = np.random.default_rng(int(factor))
+    for b in range(w.B):
+        rows = w.kv_base[b] + rng.choice(np.arange(300, int(w.prefix_len[b])), 3, replace=False)
+        big = synth.bf16_bits_to_f32(w.pool[rows]) * np.float32(factor)
+        w.pool[rows] = synth.to_bf16_bits(big)
+    _attn_check(orc, w, kv_chunks=(0, 256, 1 << 20))
