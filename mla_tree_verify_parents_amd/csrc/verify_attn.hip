@@ -41,6 +41,8 @@
 //    reuse its L2.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace {
@@ -52,8 +54,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) short4v lds_short4v;
 
 constexpr int KT = 32;               // keys per tile
-constexpr int NW = 4;                // wavefronts per workgroup: 2 pairs
-constexpr int ROWS_WG = 64;          // query rows per workgroup: 32 per pair
+constexpr int NW = 4;                // wavefronts per workgroup
+constexpr int NGRP = 2;              // row groups of 32 query rows per workgroup
+constexpr int ROWS_WG = 32 * NGRP;   // query rows per workgroup
 constexpr int kThreads = 64 * NW;
 constexpr int NSTAGE = 4;            // LDS ring depth (tiles resident or in flight)
 constexpr int kMinChunk = 256;       // smallest automatic split (keys)
@@ -244,7 +247,7 @@ struct VerifyParams {
     const uint64_t* mask;
     void* out;
     float* lse;
-    float* ws_o;    // [slot][NW][NCTW][4][64][4] fp32, normalised partial outputs
+    float* ws_o;    // [slot][row group][DL/32][4][64][4] fp32, normalised partial outputs
     float* ws_lse;  // [slot][ROWS_WG] fp32, log2-domain partial log-sum-exp
     int64_t ld_ql, ld_qp, ld_ckv, ld_kpe;
     int B, H, N, W, rows, row_tiles, chunk, total_wg;
@@ -257,41 +260,54 @@ struct VerifyParams {
 template <typename T, int DL, int DR>
 struct Shape {
     using Tr = Traits<T>;
+    using Frag = typename Tr::Frag;
     static constexpr int KPL = Tr::KPL;
     static constexpr int DQK = DL + DR;
     static constexpr int KSTEP = 2 * KPL;          // k per MFMA
     static constexpr int NKS = DQK / KSTEP;        // score MFMAs per tile
-    static constexpr int NCTW = DL / 64;           // 32-column output tiles per wavefront (half the columns)
+    static constexpr int NCT = DL / 32;            // 32-column output tiles of a value wavefront
     static constexpr int NPS = KT / KSTEP;         // value k-steps per tile
     static constexpr int VEC = 16 / sizeof(T);     // elements per 16-byte chunk
     static constexpr int CA = DL / VEC, CB = DR / VEC;      // chunks per row, regions A / B
     static constexpr int RPI_A = 64 / CA, RPI_B = 64 / CB;  // rows per DMA instruction
     static constexpr int NI_A = KT * CA / 64, NI_B = KT * CB / 64;  // DMA instructions per tile
     static constexpr int NI = NI_A + NI_B;
-    static constexpr int IA = (NI_A + NW - 1) / NW, IB = (NI_B + NW - 1) / NW;
-    static constexpr int DPW = IA + IB;            // DMA instructions per wavefront per tile
-    static constexpr int STAGE_BYTES = (NI + 1) * 64 * 16;  // + a spare 1 KB that surplus instructions target
-    static constexpr int WS_SLOT = NW * 32 * (DL / 2);   // floats of partial output per work item
+    static constexpr int NDW = NGRP;               // wavefronts that issue the DMA (the value wavefronts)
+    static constexpr int IA = NI_A / NDW, IB = NI_B / NDW;
+    static constexpr int DPW = IA + IB;            // DMA instructions per value wavefront per tile
+    static constexpr int STAGE_BYTES = NI * 64 * 16;
+    static constexpr int RING = NSTAGE * STAGE_BYTES;
+    static constexpr int PBUF = NPS * 64 * (int)sizeof(Frag);  // one row group's probabilities of one tile
+    static constexpr int SPARE = RING + 2 * NGRP * PBUF;       // 1 KB target of empty DMA instructions
+    static constexpr int LDS_BYTES = SPARE + 64 * 16;
     static_assert(DL % KSTEP == 0 && DR % KSTEP == 0, "head dims must be multiples of the MFMA k");
-    static_assert(DL % 64 == 0, "each wavefront of a pair owns whole 32-column tiles");
+    static_assert(DL % 32 == 0, "value columns come in 32-column tiles");
     static_assert(CA <= 64 && CB <= 64 && 64 % CA == 0 && 64 % CB == 0, "rows must tile DMA instructions");
     static_assert((KT * CA) % 64 == 0 && (KT * CB) % 64 == 0, "regions must be whole instructions");
-    static_assert(DPW * (NSTAGE - 2) < 64, "vmcnt range");
+    static_assert(NI_A % NDW == 0 && NI_B % NDW == 0, "value wavefronts split each region evenly");
+    static_assert(DPW <= NCT * NPS, "DMA instructions interleave with the value MFMAs");
+    static_assert(LDS_BYTES + ROWS_WG * 4 + 4 <= 160 * 1024, "LDS budget");
 };
 
 // Wait until at most `n` of this wavefront's vector-memory loads are
 // outstanding (the LDS-DMA loads of later tiles; loads complete in order).
 __device__ inline void wait_vmem(int n) {
     switch (n) {
-        case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-        case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
-        case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
-        case 9: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
+        case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
         case 18: asm volatile("s_waitcnt vmcnt(18)" ::: "memory"); break;
         default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
     }
 }
 
+// One workgroup = one work item (request b, key split, tile of 64 query
+// rows).  Wavefronts 0 and 1 are score wavefronts (row groups 0 and 1: S^T,
+// mask, softmax, probabilities to LDS); wavefronts 2 and 3 are value
+// wavefronts (row groups 0 and 1: O^T += V^T P^T, and the LDS-DMA of the key
+// tiles).  Every wavefront takes the same sequence of workgroup barriers:
+// per pass, one before the first phase and one after each of ntiles + 1
+// phases.  In phase j (between barriers j and j+1) the score wavefronts work
+// on tile j and the value wavefronts on tile j-1; tile j+2 is loaded into
+// the ring slot of tile j-2.
 template <typename T, int DL, int DR>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void verify_split(
     const VerifyParams p) {
@@ -299,12 +315,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     using Tr = typename S::Tr;
     using Frag = typename Tr::Frag;
     constexpr int KPL = S::KPL;
-    __shared__ __attribute__((aligned(16))) char smem[NSTAGE * S::STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) char smem[S::LDS_BYTES];
+    __shared__ float s_inv[ROWS_WG];
     __shared__ int s_redo;
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int pair = wave >> 1, h = wave & 1;
+    const int grp = wave % NGRP;
 
     // ---- work item: (request, key split, row tile), XCD-contiguous ----
     const int wl = ddt::xcd_logical_block(blockIdx.x, gridDim.x);
@@ -324,243 +341,286 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const int kbeg = split * p.chunk;
     const int kend = min(kbeg + p.chunk, P + p.N);
     const int ntiles = (kend - kbeg + KT - 1) / KT;
-    const int64_t kvb = p.kv_base[b];
-    const T* ckv = static_cast<const T*>(p.ckv);
-    const T* kpe = static_cast<const T*>(p.kpe);
-    const int64_t ldA = p.ld_ckv * (int64_t)sizeof(T), ldB = p.ld_kpe * (int64_t)sizeof(T);
 
-    // ---- LDS-DMA of the key tile starting at t0 into ring slot `slot` ----
-    // Instruction j of a region writes chunks [64j, 64j+64) of it: rows
-    // [j*RPI, (j+1)*RPI).  Wavefront w issues region-A instructions
-    // w, w+NW, ... then region-B instructions w, w+NW, ...; a surplus
-    // instruction (past the region's count) reads nothing into the spare
-    // 1 KB, so every wavefront issues DPW loads per tile.  Rows at or past the
-    // split end fall outside the descriptor's range and read as zeros (their
-    // scores are masked).
-    const char* ckv_b = uniform_ptr(reinterpret_cast<const char*>(ckv + (kvb + wave * S::RPI_A) * p.ld_ckv));
-    const char* kpe_b = uniform_ptr(reinterpret_cast<const char*>(kpe + (kvb + wave * S::RPI_B) * p.ld_kpe));
-    const int ldA32 = (int)ldA, ldB32 = (int)ldB;
-    const uint32_t voffA = (uint32_t)((lane / S::CA) * ldA32);
-    const uint32_t voffB = (uint32_t)((lane / S::CB) * ldB32);
-    auto issue_tile = [&](int t0, int slot) {
-        char* sbase = smem + slot * S::STAGE_BYTES;
-        const int valid = kend - t0;
-#pragma unroll
-        for (int i = 0; i < S::DPW; ++i) {
-            const bool ra = i < S::IA;
-            const int ii = ra ? i : i - S::IA;
-            const int jj = wave + NW * ii;
-            const bool real = jj < (ra ? S::NI_A : S::NI_B);
-            const int rpi = ra ? S::RPI_A : S::RPI_B;
-            const int row0 = jj * rpi;
-            const int ld = ra ? ldA32 : ldB32;
-            const char* src = ra ? ckv_b + (int64_t)(t0 + NW * rpi * ii) * ld : kpe_b + (int64_t)(t0 + NW * rpi * ii) * ld;
-            int nrows = valid - row0;
-            nrows = nrows < 0 ? 0 : (nrows > rpi ? rpi : nrows);
-            if (!real) nrows = 0;
-            const int r = row0 + lane / (ra ? S::CA : S::CB);
-            const int chunk = ra ? (lane % S::CA) ^ Tr::swA(r) : (lane % S::CB) ^ Tr::swB(r);
-            const uint32_t voff = (ra ? voffA : voffB) + (uint32_t)(chunk * 16);
-            const __amdgpu_buffer_rsrc_t rsrc =
-                __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, nrows * ld, kRsrcFlags);
-            char* dst = !real ? sbase + S::NI * 64 * 16 : sbase + ((ra ? 0 : KT * S::CA) + jj * 64) * 16;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 16, voff, 0, 0, 0);
-        }
-    };
-
-    const int wrow0 = rt * ROWS_WG + pair * 32;
-    const bool active = wrow0 < p.rows;          // same for both wavefronts of a pair
+    const int wrow0 = rt * ROWS_WG + grp * 32;
+    const bool active = wrow0 < p.rows;            // the row group has real rows
     const bool row_ok = wrow0 + l32 < p.rows;
     const int row = min(wrow0 + l32, p.rows - 1);  // padded rows recompute the last row, never stored
-    const int node = row / p.H;
     const int64_t qrow = (int64_t)b * p.rows + row;
-    const uint64_t* __restrict__ mrow = p.mask + ((int64_t)b * p.N + node) * p.W;
+    // probabilities of tile j for row group grp: pbuf0 + (j & 1) * NGRP * PBUF
+    char* const pbuf0 = smem + S::RING + grp * S::PBUF;
 
-    if (tid == 0) s_redo = 0;  // read only after the loop's barriers
-    // prologue: tiles 0 .. NSTAGE-2 in flight
-#pragma unroll
-    for (int s = 0; s < NSTAGE - 1; ++s)
-        if (s < ntiles) issue_tile(kbeg + s * KT, s);
+    if (tid == 0) s_redo = 0;  // read only after the first pass's barriers
 
-    // ---- queries: B operand of the score MFMA, resident for the whole split ----
-    Frag q[S::NKS];
+    if (wave < NGRP) {
+        // =========================== score wavefront ===========================
+        const int node = row / p.H;
+        const uint64_t* __restrict__ mrow = p.mask + ((int64_t)b * p.N + node) * p.W;
+        // queries: B operand of the score MFMA, resident for the whole split
+        Frag q[S::NKS];
 #pragma unroll
-    for (int s = 0; s < S::NKS; ++s) {
-        const int d0 = s * S::KSTEP + g * KPL;
-        const T* src = d0 < DL ? static_cast<const T*>(p.q_lat) + qrow * p.ld_ql + d0
-                               : static_cast<const T*>(p.q_pe) + qrow * p.ld_qp + (d0 - DL);
-        q[s] = Tr::global_frag(src);
+        for (int s = 0; s < S::NKS; ++s) {
+            const int d0 = s * S::KSTEP + g * KPL;
+            const T* src = d0 < DL ? static_cast<const T*>(p.q_lat) + qrow * p.ld_ql + d0
+                                   : static_cast<const T*>(p.q_pe) + qrow * p.ld_qp + (d0 - DL);
+            q[s] = Tr::global_frag(src);
+        }
+        // the first two mask words of this row (trees up to 128 nodes) stay in
+        // registers; larger trees fetch words per tile
+        uint64_t mreg[2] = {0, 0};
+        if (kend > P) {
+#pragma unroll
+            for (int w = 0; w < 2; ++w)
+                if (w < p.W) mreg[w] = mrow[w];
+        }
+        // Settle the query and mask loads here, once, behind an opaque
+        // definition, so no wait inside the loop is tied to them.
+#pragma unroll
+        for (int s = 0; s < S::NKS; ++s) pin_acc(q[s]);
+#pragma unroll
+        for (int w = 0; w < 2; ++w) pin_reg(mreg[w]);
+
+        const typename Tr::Lane LO = Tr::template lane_offsets<DL, DR>(lane);
+        float m_ref = -INFINITY;   // per-row softmax reference (log2 domain)
+        float m_seen = -INFINITY;  // per-row maximum of the scores seen so far
+        float l_run = 0.f;
+        bool overflow = false;
+        for (int pass = 0;; ++pass) {
+            l_run = 0.f;
+            __syncthreads();  // tile 0 resident
+            for (int it = 0; it < ntiles; ++it) {
+                if (active) {
+                    const int t0 = kbeg + it * KT;
+                    const char* slot = smem + (it % NSTAGE) * S::STAGE_BYTES;
+                    // scores S^T = K . Q^T (32 keys x 32 rows); NACC interleaved
+                    // accumulators keep consecutive MFMAs independent; fragment
+                    // reads run AH MFMAs ahead
+                    constexpr int NACC = 2;
+                    floatx16 sa[NACC];
+#pragma unroll
+                    for (int a = 0; a < NACC; ++a) sa[a] = floatx16{};
+                    constexpr int AH = 3;
+                    Frag f[AH + 1];
+#pragma unroll
+                    for (int k = 0; k < AH; ++k) f[k] = Tr::template k_frag<DL, DR>(slot, LO, k);
+#pragma unroll
+                    for (int ks = 0; ks < S::NKS; ++ks) {
+                        if (ks + AH < S::NKS) f[(ks + AH) % (AH + 1)] = Tr::template k_frag<DL, DR>(slot, LO, ks + AH);
+                        sa[ks % NACC] = Tr::mfma(f[ks % (AH + 1)], q[ks], sa[ks % NACC]);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    float x[16];
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) x[v] = (sa[0][v] + sa[1][v]) * p.scale_log2;
+
+                    // tree part and split tail: keys [t0, t0+32) touch at most two mask words
+                    if (t0 + KT > P || t0 + KT > kend) {
+                        const int wlo = (t0 - P > 0 ? t0 - P : 0) >> 6;
+                        uint64_t mw0, mw1;
+                        if (wlo == 0) {
+                            mw0 = mreg[0];
+                            mw1 = mreg[1];
+                        } else {
+                            mw0 = mrow[wlo < p.W ? wlo : p.W - 1];
+                            mw1 = mrow[wlo + 1 < p.W ? wlo + 1 : p.W - 1];
+                            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                        }
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) {
+                            const int t = t0 + (v >> 2) * 8 + g * 4 + (v & 3);
+                            const int jn = t - P;
+                            // bit (jn mod 64) of the word holding jn, tested with 32-bit operations
+                            const uint64_t word = (jn >> 6) == wlo ? mw0 : mw1;
+                            const uint32_t half = (jn & 32) ? (uint32_t)(word >> 32) : (uint32_t)word;
+                            const uint32_t vis =
+                                (uint32_t)(t < kend) & ((uint32_t)(t < P) | ((half >> (jn & 31)) & 1u));
+                            x[v] = vis ? x[v] : -INFINITY;
+                        }
+                    }
+                    // Softmax against a fixed per-row reference m_ref: the max
+                    // of the first tile in which the row sees any key.
+                    // Probabilities 2^(x - m_ref) stay finite unless a later
+                    // score exceeds m_ref by more than kSpan; then the split is
+                    // recomputed with the split's maximum as the reference, so
+                    // no accumulator is ever rescaled.
+                    float mx = fmaxf(x[0], x[1]);
+#pragma unroll
+                    for (int v = 2; v < 16; ++v) mx = fmaxf(mx, x[v]);
+                    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+                    m_seen = fmaxf(m_seen, mx);
+                    if (m_ref == -INFINITY) m_ref = mx;
+                    overflow |= mx > m_ref + kSpan;
+                    const float base = m_ref == -INFINITY ? 0.f : m_ref;
+                    float rs = 0.f;
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        x[v] = __builtin_amdgcn_exp2f(x[v] - base);
+                        rs += x[v];
+                    }
+                    rs += __shfl_xor(rs, 32, 64);
+                    l_run += rs;
+                    // publish P^T in the value MFMA's B-operand order
+                    char* pw = pbuf0 + (it & 1) * (NGRP * S::PBUF);
+#pragma unroll
+                    for (int j = 0; j < S::NPS; ++j)
+                        *reinterpret_cast<Frag*>(pw + (j * 64 + lane) * (int)sizeof(Frag)) = Tr::from_f32(x + j * KPL);
+                }
+                __syncthreads();  // probabilities of tile `it` published; tile it+1 resident
+            }
+            if (active && g == 0) s_inv[grp * 32 + l32] = l_run > 0.f ? 1.f / l_run : 0.f;
+            if (pass == 0 && __ballot(overflow) != 0 && lane == 0) s_redo = 1;
+            __syncthreads();  // last value phase done
+            if (pass == 1 || s_redo == 0) break;
+            m_ref = m_seen;
+            overflow = false;
+        }
+        if (active && row_ok && g == 0) {
+            const float lse2 = l_run > 0.f ? m_ref + __log2f(l_run) : -INFINITY;
+            if (p.nsplit[b] == 1)
+                p.lse[qrow] = lse2 * kLn2;
+            else
+                p.ws_lse[(size_t)wl * ROWS_WG + grp * 32 + l32] = lse2;
+        }
+        return;
     }
-    // the first two mask words of this row (trees up to 128 nodes) stay in
-    // registers; larger trees fetch words per tile
-    uint64_t mreg[2] = {0, 0};
-    if (active && kend > P) {
+
+    // ============================= value wavefront =============================
+    // LDS-DMA of tile `tile` into its ring slot.  Each region (A: c_kv, B:
+    // k_pe) of a tile is NI_A / NI_B instructions of 64 16-byte chunks;
+    // value wavefront grp issues instructions grp, grp + NDW, ...  Rows at or
+    // past the split end fall outside the buffer descriptor's range and read
+    // as zeros (their probabilities are zero).  A tile index past the split
+    // issues the same instructions with an empty range into a spare 1 KB, so
+    // every phase issues DPW loads and the loop body has no branches.
+    const int64_t kvb = p.kv_base[b];
+    const char* ckv_b = uniform_ptr(reinterpret_cast<const char*>(static_cast<const T*>(p.ckv) + kvb * p.ld_ckv));
+    const char* kpe_b = uniform_ptr(reinterpret_cast<const char*>(static_cast<const T*>(p.kpe) + kvb * p.ld_kpe));
+    const int ldA = (int)(p.ld_ckv * (int64_t)sizeof(T)), ldB = (int)(p.ld_kpe * (int64_t)sizeof(T));
+    uint32_t voff[S::DPW];
 #pragma unroll
-        for (int w = 0; w < 2; ++w)
-            if (w < p.W) mreg[w] = mrow[w];
+    for (int i = 0; i < S::DPW; ++i) {
+        const bool ra = i < S::IA;
+        const int jj = grp + S::NDW * (ra ? i : i - S::IA);
+        const int r = jj * (ra ? S::RPI_A : S::RPI_B) + lane / (ra ? S::CA : S::CB);
+        const int chunk = ra ? (lane % S::CA) ^ Tr::swA(r) : (lane % S::CB) ^ Tr::swB(r);
+        voff[i] = (uint32_t)(r * (ra ? ldA : ldB) + chunk * 16);
+        pin_reg(voff[i]);
     }
-    // Settle the query and mask loads here, once: passing the values through
-    // an opaque definition makes the loop's uses depend on it rather than on
-    // the loads, so no wait inside the loop can drain the tiles in flight.
+    auto issue = [&](int i, int tile) {
+        const bool ra = i < S::IA;
+        const int jj = grp + S::NDW * (ra ? i : i - S::IA);
+        const bool real = tile < ntiles;
+        const int t0 = kbeg + (real ? tile : 0) * KT;
+        const int ld = ra ? ldA : ldB;
+        const char* src = (ra ? ckv_b : kpe_b) + (int64_t)t0 * ld;
+        int nrows = kend - t0;
+        nrows = real ? (nrows > KT ? KT : nrows) : 0;
+        const __amdgpu_buffer_rsrc_t rsrc =
+            __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, nrows * ld, kRsrcFlags);
+        char* dst = real ? smem + (tile % NSTAGE) * S::STAGE_BYTES + ((ra ? 0 : KT * S::CA) + jj * 64) * 16
+                         : smem + S::SPARE;
+        const uint32_t vo = voff[i];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 16, vo, 0, 0, 0);
+    };
+    auto issue_tile = [&](int tile) {
 #pragma unroll
-    for (int s = 0; s < S::NKS; ++s) pin_acc(q[s]);
-#pragma unroll
-    for (int w = 0; w < 2; ++w) pin_reg(mreg[w]);
+        for (int i = 0; i < S::DPW; ++i) issue(i, tile);
+    };
+
+    if (!active) {
+        // no rows here: keep loading tiles for the other row group
+        for (int pass = 0;; ++pass) {
+            issue_tile(0);
+            issue_tile(1);
+            wait_vmem(S::DPW);
+            __syncthreads();  // tile 0 resident
+            for (int it = 0; it <= ntiles; ++it) {
+                issue_tile(it + 2);
+                wait_vmem(S::DPW);
+                __syncthreads();
+            }
+            if (pass == 1 || s_redo == 0) break;
+        }
+        wait_vmem(0);
+        return;
+    }
 
     const typename Tr::Lane LO = Tr::template lane_offsets<DL, DR>(lane);
-    floatx16 o[S::NCTW];
-    float m_ref = -INFINITY;   // per-row softmax reference (log2 domain)
-    float m_seen = -INFINITY;  // per-row maximum of the scores seen so far
-    float l_run = 0.f;
-    bool overflow = false;
+    floatx16 o[S::NCT];
     for (int pass = 0;; ++pass) {
 #pragma unroll
-    for (int c = 0; c < S::NCTW; ++c) o[c] = floatx16{};
-    l_run = 0.f;
-    for (int it = 0; it < ntiles; ++it) {
-        const int t0 = kbeg + it * KT;
-        wait_vmem(min(NSTAGE - 2, ntiles - 1 - it) * S::DPW);
-        __syncthreads();  // tile `it` resident in every wavefront's view; slot (it-1) free
-        if (it + NSTAGE - 1 < ntiles) issue_tile(t0 + (NSTAGE - 1) * KT, (it + NSTAGE - 1) % NSTAGE);
-        if (!active) continue;
-        const char* slot = smem + (it % NSTAGE) * S::STAGE_BYTES;
-
-        // scores S^T = K . Q^T (32 keys x the pair's 32 rows), both
-        // wavefronts of the pair alike.  NACC interleaved accumulators keep
-        // consecutive MFMAs independent; fragment reads run 3 MFMAs ahead.
-        constexpr int NACC = 2;
-        floatx16 sa[NACC];
+        for (int c = 0; c < S::NCT; ++c) o[c] = floatx16{};
+        issue_tile(0);
+        issue_tile(1);
+        wait_vmem(S::DPW);
+        __syncthreads();  // tile 0 resident
+        issue_tile(2);    // phase 0: no probabilities yet
+        wait_vmem(S::DPW);
+        __syncthreads();  // tile 1 resident; probabilities of tile 0 published
+        for (int it = 1; it <= ntiles; ++it) {
+            // phase it: O^T (32 rows x DL columns) += V^T . P^T for tile it-1,
+            // key step outer and column tile inner so consecutive MFMAs are
+            // independent; value fragments run AV MFMAs ahead; the loads of
+            // tile it+2 (into the slot of tile it-2) ride between the MFMAs
+            const int tv = it - 1;
+            const char* slot = smem + (tv % NSTAGE) * S::STAGE_BYTES;
+            const char* pr = pbuf0 + (tv & 1) * (NGRP * S::PBUF);
+            Frag pb[S::NPS];
 #pragma unroll
-        for (int a = 0; a < NACC; ++a) sa[a] = floatx16{};
-        constexpr int AH = 3;
-        Frag f[AH + 1];
+            for (int j = 0; j < S::NPS; ++j)
+                pb[j] = *reinterpret_cast<const Frag*>(pr + (j * 64 + lane) * (int)sizeof(Frag));
+            constexpr int NM = S::NCT * S::NPS;
+            constexpr int AV = 2;
+            Frag vf[AV + 1];
 #pragma unroll
-        for (int k = 0; k < AH; ++k) f[k] = Tr::template k_frag<DL, DR>(slot, LO, k);
+            for (int m = 0; m < AV; ++m) vf[m] = Tr::template v_frag<DL, DR>(slot, LO, m % S::NCT, m / S::NCT);
 #pragma unroll
-        for (int ks = 0; ks < S::NKS; ++ks) {
-            if (ks + AH < S::NKS) f[(ks + AH) % (AH + 1)] = Tr::template k_frag<DL, DR>(slot, LO, ks + AH);
-            sa[ks % NACC] = Tr::mfma(f[ks % (AH + 1)], q[ks], sa[ks % NACC]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        float x[16];
-#pragma unroll
-        for (int v = 0; v < 16; ++v) x[v] = (sa[0][v] + sa[1][v]) * p.scale_log2;
-
-        // tree part and split tail: keys [t0, t0+32) touch at most two mask words
-        if (t0 + KT > P || t0 + KT > kend) {
-            const int wlo = (t0 - P > 0 ? t0 - P : 0) >> 6;
-            uint64_t mw0, mw1;
-            if (wlo == 0) {
-                mw0 = mreg[0];
-                mw1 = mreg[1];
-            } else {
-                mw0 = mrow[wlo < p.W ? wlo : p.W - 1];
-                mw1 = mrow[wlo + 1 < p.W ? wlo + 1 : p.W - 1];
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            for (int m = 0; m < NM; ++m) {
+                if (m + AV < NM)
+                    vf[(m + AV) % (AV + 1)] =
+                        Tr::template v_frag<DL, DR>(slot, LO, (m + AV) % S::NCT, (m + AV) / S::NCT);
+                o[m % S::NCT] = Tr::mfma(vf[m % (AV + 1)], pb[m / S::NCT], o[m % S::NCT]);
+                if (m < S::DPW) issue(m, it + 2);
+                __builtin_amdgcn_sched_barrier(0);
             }
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int t = t0 + (v >> 2) * 8 + g * 4 + (v & 3);
-                const int jn = t - P;
-                // bit (jn mod 64) of the word holding jn, tested with 32-bit operations
-                const uint64_t word = (jn >> 6) == wlo ? mw0 : mw1;
-                const uint32_t half = (jn & 32) ? (uint32_t)(word >> 32) : (uint32_t)word;
-                const uint32_t vis = (uint32_t)(t < kend) & ((uint32_t)(t < P) | ((half >> (jn & 31)) & 1u));
-                x[v] = vis ? x[v] : -INFINITY;
-            }
+            wait_vmem(S::DPW);
+            __syncthreads();  // tile it+1 resident; tile it-1 and probabilities it-1 consumed
         }
-        // softmax against a fixed per-row reference m_ref: the max of the
-        // first tile in which the row sees any key (O is still zero then).
-        // Probabilities 2^(x - m_ref) stay finite unless a later score
-        // exceeds m_ref by more than kSpan; then the wavefront pair flags
-        // the split and it is recomputed with the split's maximum as the
-        // reference.  No accumulator is ever rescaled in the loop.
-        float mx = fmaxf(x[0], x[1]);
-#pragma unroll
-        for (int v = 2; v < 16; ++v) mx = fmaxf(mx, x[v]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        m_seen = fmaxf(m_seen, mx);
-        if (m_ref == -INFINITY) m_ref = mx;          // first visible keys of this row
-        overflow |= mx > m_ref + kSpan;
-        const float base = m_ref == -INFINITY ? 0.f : m_ref;
-        float rs = 0.f;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            x[v] = __builtin_amdgcn_exp2f(x[v] - base);
-            rs += x[v];
-        }
-        rs += __shfl_xor(rs, 32, 64);
-        l_run += rs;
-        Frag pb[S::NPS];
-#pragma unroll
-        for (int j = 0; j < S::NPS; ++j) pb[j] = Tr::from_f32(x + j * KPL);
-
-        // O^T (this wavefront's 256 columns) += V^T . P^T, key step outer
-        // and column tile inner so consecutive MFMAs are independent; value
-        // fragments (two transposed reads each) run 2 MFMAs ahead
-        constexpr int NM = S::NCTW * S::NPS;
-        constexpr int AV = 2;
-        Frag vf[AV + 1];
-#pragma unroll
-        for (int m = 0; m < AV; ++m) vf[m] = Tr::template v_frag<DL, DR>(slot, LO, h * S::NCTW + m % S::NCTW, m / S::NCTW);
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
-            if (m + AV < NM)
-                vf[(m + AV) % (AV + 1)] =
-                    Tr::template v_frag<DL, DR>(slot, LO, h * S::NCTW + (m + AV) % S::NCTW, (m + AV) / S::NCTW);
-            o[m % S::NCTW] = Tr::mfma(vf[m % (AV + 1)], pb[m / S::NCTW], o[m % S::NCTW]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
+        if (pass == 1 || s_redo == 0) break;
     }
+    wait_vmem(0);
 
-    // A second pass only if some wavefront saw a score too far above its
-    // reference; the decision is workgroup-wide (the tile loop has barriers).
-    if (pass == 1) break;
-    if (__ballot(overflow) != 0 && lane == 0) s_redo = 1;
-    __syncthreads();
-    if (s_redo == 0) break;
-    m_ref = m_seen;
-    overflow = false;
-#pragma unroll
-    for (int s = 0; s < NSTAGE - 1; ++s)
-        if (s < ntiles) issue_tile(kbeg + s * KT, s);
-    }
-
-    // ---- epilogue: normalise and store this wavefront's columns ----
-    if (!active || !row_ok) return;
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    const float lse2 = l_run > 0.f ? m_ref + __log2f(l_run) : -INFINITY;
-    const int col0 = h * (DL / 2);
-    // normalise in the accumulator registers first, so the loop never has to
-    // keep a second copy of O ready for this point
+    // ---- epilogue: normalise and store this row group's 32 rows ----
+    if (!row_ok) return;
+    const float inv = s_inv[grp * 32 + l32];
+    // normalise in the accumulator registers, so the loop never keeps a
+    // second copy of O ready for this point
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
-    for (int c = 0; c < S::NCTW; ++c) scale_acc(o[c], inv);
+    for (int c = 0; c < S::NCT; ++c) scale_acc(o[c], inv);
     asm volatile("s_nop 7" ::: "memory");
     if (p.nsplit[b] == 1) {
-        T* dst = static_cast<T*>(p.out) + qrow * DL + col0;
+        T* dst = static_cast<T*>(p.out) + qrow * DL;
 #pragma unroll
-        for (int c = 0; c < S::NCTW; ++c) {
+        for (int c = 0; c < S::NCT; ++c) {
 #pragma unroll
-            for (int grp = 0; grp < 4; ++grp) {
+            for (int v4 = 0; v4 < 4; ++v4) {
                 float v[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = o[c][grp * 4 + e];
-                store4<T>(dst + c * 32 + grp * 8 + g * 4, v);
+                for (int e = 0; e < 4; ++e) v[e] = o[c][v4 * 4 + e];
+                store4<T>(dst + c * 32 + v4 * 8 + g * 4, v);
             }
         }
-        if (g == 0 && h == 0) p.lse[qrow] = lse2 * kLn2;
     } else {
-        float* ws = p.ws_o + ((size_t)wl * NW + wave) * (S::NCTW * 4 * 64 * 4);
+        float* ws = p.ws_o + (size_t)wl * (ROWS_WG * DL) + (size_t)grp * (32 * DL);
 #pragma unroll
-        for (int c = 0; c < S::NCTW; ++c) {
+        for (int c = 0; c < S::NCT; ++c) {
 #pragma unroll
-            for (int grp = 0; grp < 4; ++grp) {
-                const float4 v = make_float4(o[c][grp * 4 + 0], o[c][grp * 4 + 1], o[c][grp * 4 + 2], o[c][grp * 4 + 3]);
-                *reinterpret_cast<float4*>(ws + ((c * 4 + grp) * 64 + lane) * 4) = v;
+            for (int v4 = 0; v4 < 4; ++v4) {
+                const float4 v = make_float4(o[c][v4 * 4 + 0], o[c][v4 * 4 + 1], o[c][v4 * 4 + 2], o[c][v4 * 4 + 3]);
+                *reinterpret_cast<float4*>(ws + ((c * 4 + v4) * 64 + lane) * 4) = v;
             }
         }
-        if (g == 0 && h == 0) p.ws_lse[(size_t)wl * ROWS_WG + pair * 32 + l32] = lse2;
     }
 }
 
