@@ -8,6 +8,7 @@ and links them into mla_tree_verify_parents_amd/libddt.so.
 from __future__ import annotations
 
 import concurrent.futures as cf
+import ctypes
 import glob
 import os
 import shutil
@@ -27,6 +28,9 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 VALU ops are kept out of generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs unless a kernel pins an accumulator to AGPRs
+    # itself: the attention scores are read by VALU code right away
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", INCLUDE, "-I", CSRC,
 ]
 
@@ -55,6 +59,13 @@ def build(extra=(), jobs: int = 8) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
+    # a library with unresolved symbols (e.g. a kernel whose host launch stub
+    # the compiler dropped) links fine but cannot be loaded: refuse it here
+    try:
+        ctypes.CDLL(tmp)
+    except OSError as e:
+        os.remove(tmp)
+        raise RuntimeError(f"built library does not load: {e}") from None
     os.replace(tmp, LIB)
     return LIB
 

@@ -88,6 +88,12 @@ struct Traits<uint16_t> {
     __device__ static floatx16 mfma(Frag a, Frag b, floatx16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
     }
+    // c += a.b with c pinned to AGPRs (the value accumulators take all of
+    // them); VALU reads of c need mfma_settle() first, VALU writes of c
+    // need it before the next product.
+    __device__ static void mfma_acc(Frag a, Frag b, floatx16& c) {
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+    }
     __device__ static Frag global_frag(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
     __device__ static Frag from_f32(const float* v) {
         Frag r;
@@ -156,6 +162,9 @@ struct Traits<float> {
     __device__ static floatx16 mfma(Frag a, Frag b, floatx16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
     }
+    __device__ static void mfma_acc(Frag a, Frag b, floatx16& c) {
+        asm volatile("v_mfma_f32_32x32x2_f32 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+    }
     __device__ static Frag global_frag(const float* p) { return *p; }
     __device__ static Frag from_f32(const float* v) { return v[0]; }
     __device__ static constexpr int swA(int) { return 0; }
@@ -200,6 +209,57 @@ __device__ inline void scale_acc(floatx16& acc, float a) {
             : "v"(a));
         acc[k] = e;
     }
+}
+
+// 24 wait states: more than any MFMA result needs before a VALU access of
+// its registers, and more than any VALU write needs before an MFMA reads it.
+__device__ inline void mfma_settle() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+
+// max(a, b, c) without the NaN-quieting the compiler puts in front of
+// fmaxf on values it cannot prove canonical (MFMA results).  Inline asm:
+// an MFMA result needs mfma_settle() before it gets here.
+__device__ inline float max3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+// The maximum of v over the lane pair (l, l xor 32): v_permlane32_swap
+// hands every lane both v[l mod 32] and v[l mod 32 + 32].
+__device__ inline float pair_max(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return max3f(__uint_as_float(r[0]), __uint_as_float(r[1]), __uint_as_float(r[1]));
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// A raw buffer descriptor (stride 0) over [base, base + bytes): loads past
+// the range return zeros.
+__device__ inline u32x4 buffer_rsrc(const void* base, int bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    u32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
+    r[2] = __builtin_amdgcn_readfirstlane((uint32_t)bytes);
+    r[3] = (uint32_t)kRsrcFlags;
+    return r;
+}
+__device__ inline uint32_t lds_addr(const void* p) {
+    return (uint32_t)reinterpret_cast<uintptr_t>((const lds_void*)p);
+}
+// LDS-DMA of 16 bytes per lane: lane l's chunk at byte voff of the buffer
+// goes to LDS address lds + 16 l.  Issued as inline asm, so the compiler
+// neither orders it against LDS reads of other addresses (its alias
+// analysis of LDS-DMA is conservative and would wait for every load) nor
+// counts it: the callers wait for it with explicit vmcnt waits before the
+// workgroup barrier that publishes the tile.
+__device__ inline void dma16(u32x4 rsrc, uint32_t lds, uint32_t voff) {
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %0, %1, 0 offen lds"
+        :
+        : "v"(voff), "s"(rsrc), "s"(lds)
+        : "m0");
 }
 
 // An opaque (empty) redefinition of a register value.
@@ -278,14 +338,13 @@ struct Shape {
     static constexpr int STAGE_BYTES = NI * 64 * 16;
     static constexpr int RING = NSTAGE * STAGE_BYTES;
     static constexpr int PBUF = NPS * 64 * (int)sizeof(Frag);  // one row group's probabilities of one tile
-    static constexpr int SPARE = RING + 2 * NGRP * PBUF;       // 1 KB target of empty DMA instructions
-    static constexpr int LDS_BYTES = SPARE + 64 * 16;
+    static constexpr int LDS_BYTES = RING + 2 * NGRP * PBUF;
     static_assert(DL % KSTEP == 0 && DR % KSTEP == 0, "head dims must be multiples of the MFMA k");
     static_assert(DL % 32 == 0, "value columns come in 32-column tiles");
     static_assert(CA <= 64 && CB <= 64 && 64 % CA == 0 && 64 % CB == 0, "rows must tile DMA instructions");
     static_assert((KT * CA) % 64 == 0 && (KT * CB) % 64 == 0, "regions must be whole instructions");
     static_assert(NI_A % NDW == 0 && NI_B % NDW == 0, "value wavefronts split each region evenly");
-    static_assert(DPW <= NCT * NPS, "DMA instructions interleave with the value MFMAs");
+    static_assert(DPW <= 2 * NCT * NPS, "DMA instructions interleave with the value MFMAs");
     static_assert(LDS_BYTES + ROWS_WG * 4 + 4 <= 160 * 1024, "LDS budget");
 };
 
@@ -304,10 +363,11 @@ __device__ inline void wait_vmem(int n) {
 // mask, softmax, probabilities to LDS); wavefronts 2 and 3 are value
 // wavefronts (row groups 0 and 1: O^T += V^T P^T, and the LDS-DMA of the key
 // tiles).  Every wavefront takes the same sequence of workgroup barriers:
-// per pass, one before the first phase and one after each of ntiles + 1
-// phases.  In phase j (between barriers j and j+1) the score wavefronts work
-// on tile j and the value wavefronts on tile j-1; tile j+2 is loaded into
-// the ring slot of tile j-2.
+// per pass, one before phase 0 and one after each of the ntiles + 2 phases.
+// In phase j (between barriers j and j+1) the score wavefronts run the
+// MFMAs of tile j together with the softmax of tile j-1, and the value
+// wavefronts multiply tile j-2 while loading tile j+1 into the ring slot of
+// tile j-3.
 template <typename T, int DL, int DR>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void verify_split(
     const VerifyParams p) {
@@ -316,7 +376,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     using Frag = typename Tr::Frag;
     constexpr int KPL = S::KPL;
     __shared__ __attribute__((aligned(16))) char smem[S::LDS_BYTES];
-    __shared__ float s_inv[ROWS_WG];
+    __shared__ float s_mref[ROWS_WG];  // per-row softmax reference, for the log-sum-exp
     __shared__ int s_redo;
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
@@ -383,103 +443,148 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         const typename Tr::Lane LO = Tr::template lane_offsets<DL, DR>(lane);
         float m_ref = -INFINITY;   // per-row softmax reference (log2 domain)
         float m_seen = -INFINITY;  // per-row maximum of the scores seen so far
-        float l_run = 0.f;
         bool overflow = false;
-        for (int pass = 0;; ++pass) {
-            l_run = 0.f;
-            __syncthreads();  // tile 0 resident
-            for (int it = 0; it < ntiles; ++it) {
-                if (active) {
-                    const int t0 = kbeg + it * KT;
-                    const char* slot = smem + (it % NSTAGE) * S::STAGE_BYTES;
-                    // scores S^T = K . Q^T (32 keys x 32 rows); NACC interleaved
-                    // accumulators keep consecutive MFMAs independent; fragment
-                    // reads run AH MFMAs ahead
-                    constexpr int NACC = 2;
-                    floatx16 sa[NACC];
-#pragma unroll
-                    for (int a = 0; a < NACC; ++a) sa[a] = floatx16{};
-                    constexpr int AH = 3;
-                    Frag f[AH + 1];
-#pragma unroll
-                    for (int k = 0; k < AH; ++k) f[k] = Tr::template k_frag<DL, DR>(slot, LO, k);
-#pragma unroll
-                    for (int ks = 0; ks < S::NKS; ++ks) {
-                        if (ks + AH < S::NKS) f[(ks + AH) % (AH + 1)] = Tr::template k_frag<DL, DR>(slot, LO, ks + AH);
-                        sa[ks % NACC] = Tr::mfma(f[ks % (AH + 1)], q[ks], sa[ks % NACC]);
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
-                    float x[16];
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) x[v] = (sa[0][v] + sa[1][v]) * p.scale_log2;
+        float x[16];               // raw dot products, then probabilities, of the tile in softmax
+        float mx = 0.f, nb = 0.f;
 
-                    // tree part and split tail: keys [t0, t0+32) touch at most two mask words
-                    if (t0 + KT > P || t0 + KT > kend) {
-                        const int wlo = (t0 - P > 0 ? t0 - P : 0) >> 6;
-                        uint64_t mw0, mw1;
-                        if (wlo == 0) {
-                            mw0 = mreg[0];
-                            mw1 = mreg[1];
-                        } else {
-                            mw0 = mrow[wlo < p.W ? wlo : p.W - 1];
-                            mw1 = mrow[wlo + 1 < p.W ? wlo + 1 : p.W - 1];
-                            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                        }
-#pragma unroll
-                        for (int v = 0; v < 16; ++v) {
-                            const int t = t0 + (v >> 2) * 8 + g * 4 + (v & 3);
-                            const int jn = t - P;
-                            // bit (jn mod 64) of the word holding jn, tested with 32-bit operations
-                            const uint64_t word = (jn >> 6) == wlo ? mw0 : mw1;
-                            const uint32_t half = (jn & 32) ? (uint32_t)(word >> 32) : (uint32_t)word;
-                            const uint32_t vis =
-                                (uint32_t)(t < kend) & ((uint32_t)(t < P) | ((half >> (jn & 31)) & 1u));
-                            x[v] = vis ? x[v] : -INFINITY;
-                        }
-                    }
-                    // Softmax against a fixed per-row reference m_ref: the max
-                    // of the first tile in which the row sees any key.
-                    // Probabilities 2^(x - m_ref) stay finite unless a later
-                    // score exceeds m_ref by more than kSpan; then the split is
-                    // recomputed with the split's maximum as the reference, so
-                    // no accumulator is ever rescaled.
-                    float mx = fmaxf(x[0], x[1]);
-#pragma unroll
-                    for (int v = 2; v < 16; ++v) mx = fmaxf(mx, x[v]);
-                    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-                    m_seen = fmaxf(m_seen, mx);
-                    if (m_ref == -INFINITY) m_ref = mx;
-                    overflow |= mx > m_ref + kSpan;
-                    const float base = m_ref == -INFINITY ? 0.f : m_ref;
-                    float rs = 0.f;
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        x[v] = __builtin_amdgcn_exp2f(x[v] - base);
-                        rs += x[v];
-                    }
-                    rs += __shfl_xor(rs, 32, 64);
-                    l_run += rs;
-                    // publish P^T in the value MFMA's B-operand order
-                    char* pw = pbuf0 + (it & 1) * (NGRP * S::PBUF);
-#pragma unroll
-                    for (int j = 0; j < S::NPS; ++j)
-                        *reinterpret_cast<Frag*>(pw + (j * 64 + lane) * (int)sizeof(Frag)) = Tr::from_f32(x + j * KPL);
-                }
-                __syncthreads();  // probabilities of tile `it` published; tile it+1 resident
+        // tiles reaching into the tree part or past the split end need the mask
+        auto tile_masked = [&](int tp) {
+            const int t0 = kbeg + tp * KT;
+            return t0 + KT > P || t0 + KT > kend;
+        };
+        auto mask_x = [&](int tp) {
+            // keys [t0, t0+32) touch at most two mask words
+            const int t0 = kbeg + tp * KT;
+            const int wlo = (t0 - P > 0 ? t0 - P : 0) >> 6;
+            uint64_t mw0, mw1;
+            if (wlo == 0) {
+                mw0 = mreg[0];
+                mw1 = mreg[1];
+            } else {
+                mw0 = mrow[wlo < p.W ? wlo : p.W - 1];
+                mw1 = mrow[wlo + 1 < p.W ? wlo + 1 : p.W - 1];
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             }
-            if (active && g == 0) s_inv[grp * 32 + l32] = l_run > 0.f ? 1.f / l_run : 0.f;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int t = t0 + (v >> 2) * 8 + g * 4 + (v & 3);
+                const int jn = t - P;
+                // bit (jn mod 64) of the word holding jn, tested with 32-bit operations
+                const uint64_t word = (jn >> 6) == wlo ? mw0 : mw1;
+                const uint32_t half = (jn & 32) ? (uint32_t)(word >> 32) : (uint32_t)word;
+                const uint32_t vis = (uint32_t)(t < kend) & ((uint32_t)(t < P) | ((half >> (jn & 31)) & 1u));
+                x[v] = vis ? x[v] : -INFINITY;
+            }
+        };
+        // Step `st` of the softmax of tile tp (raw dot products in acc, or
+        // already masked in x when HaveX).  The steps ride on the MFMA stream
+        // of the next tile, at most one exponential and two other VALU
+        // operations per MFMA, which is what one wavefront hides under a
+        // 32x32x16 product.
+        // Softmax against a fixed per-row reference m_ref: the max of the
+        // first tile in which the row sees any key.  Probabilities
+        // 2^(scale*s - m_ref) stay finite unless a later score exceeds m_ref
+        // by more than kSpan; then the split is recomputed with the split's
+        // maximum as the reference, so no accumulator is ever rescaled.  The
+        // row sums are taken by the value wavefronts (an MFMA against ones).
+        auto sm_step = [&](int st, const floatx16& acc, auto have_x, int tp) {
+            if (st < 8) {
+                if constexpr (!decltype(have_x)::value) {
+                    x[2 * st] = acc[2 * st];
+                    x[2 * st + 1] = acc[2 * st + 1];
+                }
+                mx = max3f(st == 0 ? x[0] : mx, x[2 * st], x[2 * st + 1]);
+            }
+            if (st == 8) mx *= p.scale_log2;  // scale > 0
+            if (st == 9) mx = pair_max(mx);
+            if (st == 10) m_seen = max3f(m_seen, mx, mx);
+            if (st == 11 && m_ref == -INFINITY) m_ref = mx;
+            if (st == 12) overflow |= mx > m_ref + kSpan;
+            if (st == 13) nb = m_ref == -INFINITY ? 0.f : -m_ref;
+            if (st >= 14 && st < 30) {
+                const int e = st - 14;
+                x[e] = __builtin_amdgcn_exp2f(fmaf(x[e], p.scale_log2, nb));
+            }
+            // publish P^T in the value MFMA's B-operand order
+            if (st == 30 || st == 32) {
+                char* pw = pbuf0 + (tp & 1) * (NGRP * S::PBUF);
+                constexpr int H2 = S::NPS / 2;
+                const int j0 = st == 30 ? 0 : H2;
+#pragma unroll
+                for (int j = j0; j < j0 + H2; ++j)
+                    *reinterpret_cast<Frag*>(pw + (j * 64 + lane) * (int)sizeof(Frag)) = Tr::from_f32(x + j * KPL);
+            }
+        };
+        constexpr int NST = 33;  // softmax steps
+        static_assert(S::NKS >= NST, "softmax steps ride on the score MFMAs");
+        // Phase `it`: scores of tile it into cur (one accumulator chain:
+        // back-to-back dependent products issue without stalls; fragment
+        // reads run AH MFMAs ahead), with the softmax of tile it-1 (in prv)
+        // when WithSm.
+        auto qk_phase = [&](floatx16& cur, const floatx16& prv, int it, auto with_sm, auto have_x) {
+            const char* slot = smem + (it % NSTAGE) * S::STAGE_BYTES;
+            // the softmax reads the previous tile's MFMA results through inline asm
+            if constexpr (decltype(with_sm)::value && !decltype(have_x)::value) mfma_settle();
+            constexpr int AH = 3;
+            Frag f[AH + 1];
+#pragma unroll
+            for (int k = 0; k < AH; ++k) f[k] = Tr::template k_frag<DL, DR>(slot, LO, k);
+#pragma unroll
+            for (int ks = 0; ks < S::NKS; ++ks) {
+                if (ks + AH < S::NKS) f[(ks + AH) % (AH + 1)] = Tr::template k_frag<DL, DR>(slot, LO, ks + AH);
+                cur = Tr::mfma(f[ks % (AH + 1)], q[ks], ks == 0 ? floatx16{} : cur);
+                if constexpr (decltype(with_sm)::value) {
+                    if (ks < NST) sm_step(ks, prv, have_x, it - 1);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        auto run_phase = [&](floatx16& cur, const floatx16& prv, int it) {
+            if (tile_masked(it - 1)) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) x[v] = prv[v];
+                mask_x(it - 1);
+                qk_phase(cur, prv, it, std::true_type{}, std::true_type{});
+            } else {
+                qk_phase(cur, prv, it, std::true_type{}, std::false_type{});
+            }
+        };
+        auto sm_last = [&](const floatx16& acc, int tp) {
+            mfma_settle();
+#pragma unroll
+            for (int v = 0; v < 16; ++v) x[v] = acc[v];
+            if (tile_masked(tp)) mask_x(tp);
+#pragma unroll
+            for (int st = 0; st < NST; ++st) sm_step(st, acc, std::true_type{}, tp);
+        };
+
+        floatx16 sA, sB;  // raw dot products of even / odd tiles
+        for (int pass = 0;; ++pass) {
+            __syncthreads();  // tile 0 resident
+            if (active) qk_phase(sA, sB, 0, std::false_type{}, std::false_type{});
+            __syncthreads();  // tile 1 resident
+            int it = 1;
+            for (; it + 1 < ntiles; it += 2) {
+                if (active) run_phase(sB, sA, it);
+                __syncthreads();  // probabilities of tile it-1 published; tile it+1 resident
+                if (active) run_phase(sA, sB, it + 1);
+                __syncthreads();
+            }
+            if (it < ntiles) {
+                // one more tile (odd index); the last tile's scores end in sB
+                if (active) run_phase(sB, sA, it);
+                __syncthreads();
+                if (active) sm_last(sB, ntiles - 1);
+            } else {
+                if (active) sm_last(sA, ntiles - 1);
+            }
+            __syncthreads();  // probabilities of the last tile published
+            if (active && g == 0) s_mref[grp * 32 + l32] = m_ref;
             if (pass == 0 && __ballot(overflow) != 0 && lane == 0) s_redo = 1;
             __syncthreads();  // last value phase done
             if (pass == 1 || s_redo == 0) break;
             m_ref = m_seen;
             overflow = false;
-        }
-        if (active && row_ok && g == 0) {
-            const float lse2 = l_run > 0.f ? m_ref + __log2f(l_run) : -INFINITY;
-            if (p.nsplit[b] == 1)
-                p.lse[qrow] = lse2 * kLn2;
-            else
-                p.ws_lse[(size_t)wl * ROWS_WG + grp * 32 + l32] = lse2;
         }
         return;
     }
@@ -490,8 +595,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     // value wavefront grp issues instructions grp, grp + NDW, ...  Rows at or
     // past the split end fall outside the buffer descriptor's range and read
     // as zeros (their probabilities are zero).  A tile index past the split
-    // issues the same instructions with an empty range into a spare 1 KB, so
-    // every phase issues DPW loads and the loop body has no branches.
+    // loads an empty range, i.e. zeros, into its slot, which then holds a
+    // consumed tile; so every phase issues DPW loads and the loop body has
+    // no branches.
     const int64_t kvb = p.kv_base[b];
     const char* ckv_b = uniform_ptr(reinterpret_cast<const char*>(static_cast<const T*>(p.ckv) + kvb * p.ld_ckv));
     const char* kpe_b = uniform_ptr(reinterpret_cast<const char*>(static_cast<const T*>(p.kpe) + kvb * p.ld_kpe));
@@ -506,65 +612,85 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         voff[i] = (uint32_t)(r * (ra ? ldA : ldB) + chunk * 16);
         pin_reg(voff[i]);
     }
-    auto issue = [&](int i, int tile) {
-        const bool ra = i < S::IA;
-        const int jj = grp + S::NDW * (ra ? i : i - S::IA);
+    // per-tile descriptors of the two regions (rows [t0, min(t0 + KT, kend)))
+    struct TileDma {
+        u32x4 ra, rb;    // raw buffer descriptors of the tile's rows in c_kv / k_pe
+        uint32_t lds;    // LDS byte address of the tile's ring slot
+    };
+    auto tile_dma = [&](int tile) {
         const bool real = tile < ntiles;
         const int t0 = kbeg + (real ? tile : 0) * KT;
-        const int ld = ra ? ldA : ldB;
-        const char* src = (ra ? ckv_b : kpe_b) + (int64_t)t0 * ld;
         int nrows = kend - t0;
         nrows = real ? (nrows > KT ? KT : nrows) : 0;
-        const __amdgpu_buffer_rsrc_t rsrc =
-            __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, nrows * ld, kRsrcFlags);
-        char* dst = real ? smem + (tile % NSTAGE) * S::STAGE_BYTES + ((ra ? 0 : KT * S::CA) + jj * 64) * 16
-                         : smem + S::SPARE;
-        const uint32_t vo = voff[i];
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 16, vo, 0, 0, 0);
+        TileDma d;
+        d.ra = buffer_rsrc(ckv_b + (int64_t)t0 * ldA, nrows * ldA);
+        d.rb = buffer_rsrc(kpe_b + (int64_t)t0 * ldB, nrows * ldB);
+        d.lds = lds_addr(smem) + (uint32_t)((tile % NSTAGE) * S::STAGE_BYTES);
+        return d;
+    };
+    auto issue = [&](const TileDma& d, int i) {
+        const bool ra = i < S::IA;
+        const int jj = grp + S::NDW * (ra ? i : i - S::IA);
+        dma16(ra ? d.ra : d.rb, d.lds + (uint32_t)(((ra ? 0 : KT * S::CA) + jj * 64) * 16), voff[i]);
     };
     auto issue_tile = [&](int tile) {
+        const TileDma d = tile_dma(tile);
 #pragma unroll
-        for (int i = 0; i < S::DPW; ++i) issue(i, tile);
+        for (int i = 0; i < S::DPW; ++i) issue(d, i);
     };
 
     if (!active) {
         // no rows here: keep loading tiles for the other row group
         for (int pass = 0;; ++pass) {
             issue_tile(0);
-            issue_tile(1);
-            wait_vmem(S::DPW);
+            wait_vmem(0);
             __syncthreads();  // tile 0 resident
-            for (int it = 0; it <= ntiles; ++it) {
-                issue_tile(it + 2);
-                wait_vmem(S::DPW);
+            for (int it = 0; it <= ntiles + 1; ++it) {
+                issue_tile(it + 1);
+                wait_vmem(0);
                 __syncthreads();
             }
             if (pass == 1 || s_redo == 0) break;
         }
-        wait_vmem(0);
         return;
     }
 
     const typename Tr::Lane LO = Tr::template lane_offsets<DL, DR>(lane);
+    Frag ones;  // A operand of the row-sum product: every key weighs 1
+    {
+        float one[KPL];
+#pragma unroll
+        for (int e = 0; e < KPL; ++e) one[e] = 1.f;
+        ones = Tr::from_f32(one);
+    }
     floatx16 o[S::NCT];
+    floatx16 lsum;  // every element: the row's sum of (rounded) probabilities
     for (int pass = 0;; ++pass) {
 #pragma unroll
-        for (int c = 0; c < S::NCT; ++c) o[c] = floatx16{};
+        for (int c = 0; c < S::NCT; ++c) {
+            o[c] = floatx16{};
+            pin_acc(o[c]);
+        }
+        lsum = floatx16{};
+        mfma_settle();  // the zeroing writes above precede the first product
         issue_tile(0);
-        issue_tile(1);
-        wait_vmem(S::DPW);
+        wait_vmem(0);
         __syncthreads();  // tile 0 resident
-        issue_tile(2);    // phase 0: no probabilities yet
-        wait_vmem(S::DPW);
-        __syncthreads();  // tile 1 resident; probabilities of tile 0 published
-        for (int it = 1; it <= ntiles; ++it) {
-            // phase it: O^T (32 rows x DL columns) += V^T . P^T for tile it-1,
+        issue_tile(1);    // phase 0: scores of tile 0
+        wait_vmem(0);
+        __syncthreads();  // tile 1 resident
+        issue_tile(2);    // phase 1: scores of tile 1, softmax of tile 0
+        wait_vmem(0);
+        __syncthreads();  // tile 2 resident; probabilities of tile 0 published
+        for (int it = 2; it <= ntiles + 1; ++it) {
+            // phase it: O^T (32 rows x DL columns) += V^T . P^T for tile it-2,
             // key step outer and column tile inner so consecutive MFMAs are
             // independent; value fragments run AV MFMAs ahead; the loads of
-            // tile it+2 (into the slot of tile it-2) ride between the MFMAs
-            const int tv = it - 1;
+            // tile it+1 (into the slot of tile it-3) ride one per MFMA
+            const int tv = it - 2;
             const char* slot = smem + (tv % NSTAGE) * S::STAGE_BYTES;
             const char* pr = pbuf0 + (tv & 1) * (NGRP * S::PBUF);
+            const TileDma d = tile_dma(it + 1);
             Frag pb[S::NPS];
 #pragma unroll
             for (int j = 0; j < S::NPS; ++j)
@@ -579,12 +705,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 if (m + AV < NM)
                     vf[(m + AV) % (AV + 1)] =
                         Tr::template v_frag<DL, DR>(slot, LO, (m + AV) % S::NCT, (m + AV) / S::NCT);
-                o[m % S::NCT] = Tr::mfma(vf[m % (AV + 1)], pb[m / S::NCT], o[m % S::NCT]);
-                if (m < S::DPW) issue(m, it + 2);
+                Tr::mfma_acc(vf[m % (AV + 1)], pb[m / S::NCT], o[m % S::NCT]);
+                if (m < S::DPW) issue(d, m);
+                // row sums ride at the end of each key step
+                if (m % S::NCT == S::NCT - 1) lsum = Tr::mfma(ones, pb[m / S::NCT], lsum);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            wait_vmem(S::DPW);
-            __syncthreads();  // tile it+1 resident; tile it-1 and probabilities it-1 consumed
+            wait_vmem(0);
+            __syncthreads();  // tile it+1 resident; tile it-2 and probabilities it-2 consumed
         }
         if (pass == 1 || s_redo == 0) break;
     }
@@ -592,10 +720,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
     // ---- epilogue: normalise and store this row group's 32 rows ----
     if (!row_ok) return;
-    const float inv = s_inv[grp * 32 + l32];
+    const float l = lsum[0];
+    const float m_ref = s_mref[grp * 32 + l32];
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const float lse2 = l > 0.f ? m_ref + __log2f(l) : -INFINITY;
+    if (g == 0) {
+        if (p.nsplit[b] == 1)
+            p.lse[qrow] = lse2 * kLn2;
+        else
+            p.ws_lse[(size_t)wl * ROWS_WG + grp * 32 + l32] = lse2;
+    }
     // normalise in the accumulator registers, so the loop never keeps a
     // second copy of O ready for this point
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    mfma_settle();
 #pragma unroll
     for (int c = 0; c < S::NCT; ++c) scale_acc(o[c], inv);
     asm volatile("s_nop 7" ::: "memory");
