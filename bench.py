@@ -14,10 +14,19 @@ Prints ONE JSON line.  `value` is verify-attention TFLOP/s over the whole
 step (attention FLOPs / step time); `roofline` is the verify-attention
 launch (split-KV kernel + combine) against the bf16 MFMA peak;
 `cpu_baseline` times the fp64 oracle on the host for the same workload.
+
+`--traffic-probe` runs a few attention launches of the workload and one
+device-to-device copy of known size, and exits: it is the program that the
+HBM-traffic counter runs (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE) profile.
+The per-launch traffic they measured is read back from
+profiles/verify_attn_<workload>_traffic.md, and reported only while the
+kernel source still has the hash recorded there.
 """
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -40,7 +49,35 @@ def parse():
     ap.add_argument("--attn-reps", type=int, default=200, help="back-to-back attention launches timed for the roofline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget for the oracle timing")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="run 5 attention launches and a 256 MiB calibration copy, then exit")
     return ap.parse_args()
+
+
+KERNEL_SRC = os.path.join(ROOT, "mla_tree_verify_parents_amd", "csrc", "verify_attn.hip")
+CALIB_BYTES = 256 << 20   # the calibration copy reads and writes this many bytes
+
+
+def kernel_sha256():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def recorded_traffic(cfg):
+    """Per-launch HBM bytes (fetch + write, calibrated) of the attention
+    launch from the committed counter summary, or None when there is none or
+    the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"verify_attn_config{cfg}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    vals = dict(re.findall(r"^- (\w+): (\S+)$", text, re.M))
+    if vals.get("kernel_source_sha256") != kernel_sha256():
+        return None
+    try:
+        return int(vals["fetch_bytes_per_launch"]) + int(vals["write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def workload_for(cfg):
@@ -129,6 +166,18 @@ def main():
         ddt.greedy_accept(t, draft, parents, acc, path, tok)
         ddt.compact_kv(ckv, kpe, kv_base, prefix, path, acc)
 
+    if args.traffic_probe:
+        ddt.build_mask(parents, mask, depth, terr)
+        for _ in range(5):
+            attn()
+        src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"traffic_probe": f"config{args.config}", "attn_launches": 5,
+                          "calibration_copy_bytes": CALIB_BYTES}), flush=True)
+        return
+
     side = torch.cuda.Stream()
     with torch.cuda.stream(side):
         for _ in range(3):
@@ -191,7 +240,7 @@ def main():
         "verify_attn_cache_tokens_per_s": round(keys / (ms_attn * 1e-3), 1),
         "roofline": {"bound": "mfma", "kernel": "verify_split+verify_combine (ddt_verify_attn)",
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": recorded_traffic(args.config),
                      "algorithmic_bytes": attn_bytes,
                      "achieved_GBps": round(attn_bytes / (ms_attn * 1e-3) / 1e9, 1)},
     }
@@ -200,19 +249,42 @@ def main():
     print(json.dumps(res), flush=True)
 
 
+def row_pairs(w):
+    """Visible keys of every flat query row (prefix plus ancestors and self)."""
+    per = np.empty((w.B, w.N), np.int64)
+    for b in range(w.B):
+        d = np.zeros(w.N, np.int64)
+        for i in range(1, w.N):
+            d[i] = d[w.parents[b, i]] + 1
+        per[b] = int(w.prefix_len[b]) + d + 1
+    return np.repeat(per.reshape(-1), w.H)
+
+
 def cpu_baseline(w, budget_s, flops):
-    """Time the fp64 oracle on the host for the same verify step (all rows of
-    the attention, mask, argmax, accept, compaction), repeated while within
-    the time budget (at least once)."""
+    """Time the fp64 oracle on the host for the same verify step: mask,
+    attention, argmax, acceptance, compaction.  The attention runs on every
+    query row when that fits the time budget, else on a seeded random sample
+    of rows sized to it, and its time is scaled by visible pairs."""
     from oracle import oracle
 
     oracle.lib()
+    pairs = row_pairs(w)
+    total = int(pairs.sum())
+    rng = np.random.default_rng(0)
+    # rate probe on a few rows decides the sample size
+    probe = np.sort(rng.choice(w.rows, min(w.rows, 16), replace=False))
+    t0 = time.perf_counter()
+    oracle.verify_attn(w.q_lat(), w.q_pe(), w.ckv(), w.kpe(), w.kv_base, w.prefix_len, w.parents,
+                       H=w.H, scale=w.scale, rows=probe)
+    rate = pairs[probe].sum() / max(time.perf_counter() - t0, 1e-6)   # pairs per second
+    n = w.rows if total / rate <= 0.8 * budget_s else max(16, int(w.rows * 0.8 * budget_s * rate / total))
+    rows = None if n >= w.rows else np.sort(rng.choice(w.rows, n, replace=False))
     reps, t_att, t_rest = 0, 0.0, 0.0
-    while True:
+    while True:   # whole steps, repeated while within the budget (at most 20)
         t0 = time.perf_counter()
         oracle.build_mask(w.parents)
         oracle.verify_attn(w.q_lat(), w.q_pe(), w.ckv(), w.kpe(), w.kv_base, w.prefix_len, w.parents,
-                           H=w.H, scale=w.scale)
+                           H=w.H, scale=w.scale, rows=rows)
         t1 = time.perf_counter()
         t = oracle.argmax(w.logits).reshape(w.B, w.N) if w.logits is not None else w.target_ids
         a, pth, _ = oracle.greedy_accept(t, w.draft_ids, w.parents)
@@ -224,11 +296,14 @@ def cpu_baseline(w, budget_s, flops):
         t_rest += t2 - t1
         if t_att + t_rest >= budget_s or reps >= 20:
             break
-    step_s = (t_att + t_rest) / reps
+    sampled = total if rows is None else int(pairs[rows].sum())
+    att = t_att / reps * total / sampled
+    step_s = att + t_rest / reps
+    what = "all query rows" if rows is None else f"{n} of {w.rows} query rows (seeded), time scaled by visible pairs"
     return {"value": round(flops / step_s / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"full verify step of the same workload, {reps} rep(s); "
-                      f"{step_s * 1e3:.1f} ms/step ({t_att / reps * 1e3:.1f} ms attention)"}
+            "sample": f"{reps} verify step(s) of the same workload, attention on {what}; "
+                      f"{step_s * 1e3:.1f} ms/step ({att * 1e3:.1f} ms attention)"}
 
 
 if __name__ == "__main__":
