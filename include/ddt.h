@@ -97,10 +97,12 @@ int ddt_build_mask(const int32_t* parents, int B, int N, uint64_t* mask, int32_t
  * (root = last committed token, recomputed) occupy rows P_b .. P_b+N-1, so
  * node j is key P_b + j and a request has T_b = P_b + N keys.
  *
- * scale multiplies the full score q_lat.c_kv + q_pe.k_pe before softmax.
+ * scale multiplies the full score q_lat.c_kv + q_pe.k_pe before softmax;
+ * it must be positive and finite (DDT_EINVAL otherwise).
  * kv_chunk: keys per split of the key range (rounded up to a multiple of
  * 32); 0 lets the library choose.  Results do not depend on it beyond
- * rounding.
+ * rounding: the partial outputs of a split request pass through the
+ * workspace in the input dtype.
  *
  * Built instances (d_lat, d_rope, dtype): (512, 64, BF16), (64, 16, F32).
  * Alignment: q_lat, q_pe, ckv, kpe 16-byte aligned; every row stride times

@@ -64,6 +64,14 @@ constexpr int kRsrcFlags = 0x00020000;  // raw 32-bit buffer descriptor word 3
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kSpan = 64.f;         // log2 headroom of the fixed softmax reference
+#ifndef DDT_SCORE_AHEAD
+#define DDT_SCORE_AHEAD 3
+#endif
+#ifndef DDT_VALUE_AHEAD
+#define DDT_VALUE_AHEAD 2
+#endif
+constexpr int kScoreAhead = DDT_SCORE_AHEAD;  // score fragment reads run this many MFMAs ahead
+constexpr int kValueAhead = DDT_VALUE_AHEAD;  // value fragments are read this many fragments ahead
 
 // A key tile in LDS is two regions, each row-major with 16-byte chunks:
 //   A: c_kv,  KT rows x CA chunks    (CA = d_lat * elem / 16)
@@ -297,6 +305,19 @@ template <>
 __device__ inline void store4<float>(float* dst, const float* v) {
     *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
 }
+// four consecutive elements widened to fp32
+template <typename T>
+__device__ inline float4 load4(const T* src);
+template <>
+__device__ inline float4 load4<uint16_t>(const uint16_t* src) {
+    const uint2 w = *reinterpret_cast<const uint2*>(src);
+    return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), __uint_as_float(w.y << 16),
+                       __uint_as_float(w.y & 0xffff0000u));
+}
+template <>
+__device__ inline float4 load4<float>(const float* src) {
+    return *reinterpret_cast<const float4*>(src);
+}
 
 struct VerifyParams {
     const void* q_lat;
@@ -307,7 +328,7 @@ struct VerifyParams {
     const uint64_t* mask;
     void* out;
     float* lse;
-    float* ws_o;    // [slot][row group][DL/32][4][64][4] fp32, normalised partial outputs
+    void* ws_o;     // [slot][row group][DL/32][4][64][4] in the input dtype, normalised partial outputs
     float* ws_lse;  // [slot][ROWS_WG] fp32, log2-domain partial log-sum-exp
     int64_t ld_ql, ld_qp, ld_ckv, ld_kpe;
     int B, H, N, W, rows, row_tiles, chunk, total_wg;
@@ -344,19 +365,13 @@ struct Shape {
     static_assert(CA <= 64 && CB <= 64 && 64 % CA == 0 && 64 % CB == 0, "rows must tile DMA instructions");
     static_assert((KT * CA) % 64 == 0 && (KT * CB) % 64 == 0, "regions must be whole instructions");
     static_assert(NI_A % NDW == 0 && NI_B % NDW == 0, "value wavefronts split each region evenly");
-    static_assert(DPW <= 2 * NCT * NPS, "DMA instructions interleave with the value MFMAs");
+    static_assert(DPW <= NCT * NPS, "DMA instructions interleave with the value MFMAs");
     static_assert(LDS_BYTES + ROWS_WG * 4 + 4 <= 160 * 1024, "LDS budget");
 };
 
-// Wait until at most `n` of this wavefront's vector-memory loads are
-// outstanding (the LDS-DMA loads of later tiles; loads complete in order).
-__device__ inline void wait_vmem(int n) {
-    switch (n) {
-        case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
-        case 18: asm volatile("s_waitcnt vmcnt(18)" ::: "memory"); break;
-        default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-    }
-}
+// Wait until this wavefront's vector-memory loads (the LDS-DMA of later
+// tiles, issued as inline asm the compiler does not count) have landed.
+__device__ inline void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // One workgroup = one work item (request b, key split, tile of 64 query
 // rows).  Wavefronts 0 and 1 are score wavefronts (row groups 0 and 1: S^T,
@@ -525,7 +540,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             const char* slot = smem + (it % NSTAGE) * S::STAGE_BYTES;
             // the softmax reads the previous tile's MFMA results through inline asm
             if constexpr (decltype(with_sm)::value && !decltype(have_x)::value) mfma_settle();
-            constexpr int AH = 3;
+            constexpr int AH = kScoreAhead;
             Frag f[AH + 1];
 #pragma unroll
             for (int k = 0; k < AH; ++k) f[k] = Tr::template k_frag<DL, DR>(slot, LO, k);
@@ -638,23 +653,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
         for (int i = 0; i < S::DPW; ++i) issue(d, i);
     };
-
-    if (!active) {
-        // no rows here: keep loading tiles for the other row group
-        for (int pass = 0;; ++pass) {
-            issue_tile(0);
-            wait_vmem(0);
-            __syncthreads();  // tile 0 resident
-            for (int it = 0; it <= ntiles + 1; ++it) {
-                issue_tile(it + 1);
-                wait_vmem(0);
-                __syncthreads();
-            }
-            if (pass == 1 || s_redo == 0) break;
-        }
-        return;
-    }
-
+    // Value wavefront `half` (= grp) owns output columns [half*DL/2,
+    // (half+1)*DL/2) of all 64 rows: every V^T fragment read from LDS feeds
+    // the products of both row groups.  Row group 0 always has real rows;
+    // row group 1 may not (last row tile), and then its products run on
+    // stale probabilities and are never stored.
+    const int half = grp;
+    constexpr int NCH = S::NCT / 2;  // 32-column tiles of this wavefront
     const typename Tr::Lane LO = Tr::template lane_offsets<DL, DR>(lane);
     Frag ones;  // A operand of the row-sum product: every key weighs 1
     {
@@ -663,99 +668,120 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         for (int e = 0; e < KPL; ++e) one[e] = 1.f;
         ones = Tr::from_f32(one);
     }
-    floatx16 o[S::NCT];
-    floatx16 lsum;  // every element: the row's sum of (rounded) probabilities
+    floatx16 o[NGRP][NCH];
+    floatx16 lsum[NGRP];  // every element: the row's sum of (rounded) probabilities
     for (int pass = 0;; ++pass) {
 #pragma unroll
-        for (int c = 0; c < S::NCT; ++c) {
-            o[c] = floatx16{};
-            pin_acc(o[c]);
+        for (int rb = 0; rb < NGRP; ++rb) {
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                o[rb][c] = floatx16{};
+                pin_acc(o[rb][c]);
+            }
+            lsum[rb] = floatx16{};
         }
-        lsum = floatx16{};
         mfma_settle();  // the zeroing writes above precede the first product
         issue_tile(0);
-        wait_vmem(0);
+        wait_vmem_all();
         __syncthreads();  // tile 0 resident
         issue_tile(1);    // phase 0: scores of tile 0
-        wait_vmem(0);
+        wait_vmem_all();
         __syncthreads();  // tile 1 resident
         issue_tile(2);    // phase 1: scores of tile 1, softmax of tile 0
-        wait_vmem(0);
+        wait_vmem_all();
         __syncthreads();  // tile 2 resident; probabilities of tile 0 published
         for (int it = 2; it <= ntiles + 1; ++it) {
-            // phase it: O^T (32 rows x DL columns) += V^T . P^T for tile it-2,
-            // key step outer and column tile inner so consecutive MFMAs are
-            // independent; value fragments run AV MFMAs ahead; the loads of
-            // tile it+1 (into the slot of tile it-3) ride one per MFMA
+            // phase it: O^T (this wavefront's columns x 64 rows) += V^T . P^T
+            // for tile it-2: key step outer, column tile inner, row group
+            // innermost (the two products of a fragment are independent);
+            // value fragments run AV fragments ahead; the loads of tile it+1
+            // (into the slot of tile it-3) ride one per MFMA
             const int tv = it - 2;
             const char* slot = smem + (tv % NSTAGE) * S::STAGE_BYTES;
-            const char* pr = pbuf0 + (tv & 1) * (NGRP * S::PBUF);
             const TileDma d = tile_dma(it + 1);
-            Frag pb[S::NPS];
+            Frag pb[NGRP][S::NPS];
 #pragma unroll
-            for (int j = 0; j < S::NPS; ++j)
-                pb[j] = *reinterpret_cast<const Frag*>(pr + (j * 64 + lane) * (int)sizeof(Frag));
-            constexpr int NM = S::NCT * S::NPS;
-            constexpr int AV = 2;
+            for (int rb = 0; rb < NGRP; ++rb) {
+                const char* pr = smem + S::RING + rb * S::PBUF + (tv & 1) * (NGRP * S::PBUF);
+#pragma unroll
+                for (int j = 0; j < S::NPS; ++j)
+                    pb[rb][j] = *reinterpret_cast<const Frag*>(pr + (j * 64 + lane) * (int)sizeof(Frag));
+            }
+            constexpr int NQ = NCH * S::NPS;  // fragments per tile
+            constexpr int AV = kValueAhead;
             Frag vf[AV + 1];
 #pragma unroll
-            for (int m = 0; m < AV; ++m) vf[m] = Tr::template v_frag<DL, DR>(slot, LO, m % S::NCT, m / S::NCT);
+            for (int q = 0; q < AV; ++q) vf[q] = Tr::template v_frag<DL, DR>(slot, LO, half * NCH + q % NCH, q / NCH);
 #pragma unroll
-            for (int m = 0; m < NM; ++m) {
-                if (m + AV < NM)
-                    vf[(m + AV) % (AV + 1)] =
-                        Tr::template v_frag<DL, DR>(slot, LO, (m + AV) % S::NCT, (m + AV) / S::NCT);
-                Tr::mfma_acc(vf[m % (AV + 1)], pb[m / S::NCT], o[m % S::NCT]);
-                if (m < S::DPW) issue(d, m);
-                // row sums ride at the end of each key step
-                if (m % S::NCT == S::NCT - 1) lsum = Tr::mfma(ones, pb[m / S::NCT], lsum);
-                __builtin_amdgcn_sched_barrier(0);
+            for (int q = 0; q < NQ; ++q) {
+                if (q + AV < NQ)
+                    vf[(q + AV) % (AV + 1)] =
+                        Tr::template v_frag<DL, DR>(slot, LO, half * NCH + (q + AV) % NCH, (q + AV) / NCH);
+#pragma unroll
+                for (int rb = 0; rb < NGRP; ++rb) {
+                    const int m = q * NGRP + rb;
+                    Tr::mfma_acc(vf[q % (AV + 1)], pb[rb][q / NCH], o[rb][q % NCH]);
+                    if (m < S::DPW) issue(d, m);
+                    // row sums ride at the end of each key step
+                    if (q % NCH == NCH - 1) lsum[rb] = Tr::mfma(ones, pb[rb][q / NCH], lsum[rb]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
-            wait_vmem(0);
+            wait_vmem_all();
             __syncthreads();  // tile it+1 resident; tile it-2 and probabilities it-2 consumed
         }
         if (pass == 1 || s_redo == 0) break;
     }
-    wait_vmem(0);
+    wait_vmem_all();
 
-    // ---- epilogue: normalise and store this row group's 32 rows ----
-    if (!row_ok) return;
-    const float l = lsum[0];
-    const float m_ref = s_mref[grp * 32 + l32];
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    const float lse2 = l > 0.f ? m_ref + __log2f(l) : -INFINITY;
-    if (g == 0) {
-        if (p.nsplit[b] == 1)
-            p.lse[qrow] = lse2 * kLn2;
-        else
-            p.ws_lse[(size_t)wl * ROWS_WG + grp * 32 + l32] = lse2;
-    }
+    // ---- epilogue: normalise and store this wavefront's columns of the 64 rows ----
     // normalise in the accumulator registers, so the loop never keeps a
     // second copy of O ready for this point
     mfma_settle();
 #pragma unroll
-    for (int c = 0; c < S::NCT; ++c) scale_acc(o[c], inv);
-    asm volatile("s_nop 7" ::: "memory");
-    if (p.nsplit[b] == 1) {
-        T* dst = static_cast<T*>(p.out) + qrow * DL;
-#pragma unroll
-        for (int c = 0; c < S::NCT; ++c) {
-#pragma unroll
-            for (int v4 = 0; v4 < 4; ++v4) {
-                float v[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = o[c][v4 * 4 + e];
-                store4<T>(dst + c * 32 + v4 * 8 + g * 4, v);
-            }
+    for (int rb = 0; rb < NGRP; ++rb) {
+        const int r = rt * ROWS_WG + rb * 32 + l32;
+        const bool ok = r < p.rows;
+        const int64_t qr = (int64_t)b * p.rows + (ok ? r : 0);
+        const float l = lsum[rb][0];
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        if (half == rb && g == 0 && ok) {
+            const float lse2 = l > 0.f ? s_mref[rb * 32 + l32] + __log2f(l) : -INFINITY;
+            if (p.nsplit[b] == 1)
+                p.lse[qr] = lse2 * kLn2;
+            else
+                p.ws_lse[(size_t)wl * ROWS_WG + rb * 32 + l32] = lse2;
         }
-    } else {
-        float* ws = p.ws_o + (size_t)wl * (ROWS_WG * DL) + (size_t)grp * (32 * DL);
 #pragma unroll
-        for (int c = 0; c < S::NCT; ++c) {
+        for (int c = 0; c < NCH; ++c) scale_acc(o[rb][c], inv);
+        asm volatile("s_nop 7" ::: "memory");
+        if (!ok) continue;
+        if (p.nsplit[b] == 1) {
+            T* dst = static_cast<T*>(p.out) + qr * DL + half * (DL / 2);
 #pragma unroll
-            for (int v4 = 0; v4 < 4; ++v4) {
-                const float4 v = make_float4(o[c][v4 * 4 + 0], o[c][v4 * 4 + 1], o[c][v4 * 4 + 2], o[c][v4 * 4 + 3]);
-                *reinterpret_cast<float4*>(ws + ((c * 4 + v4) * 64 + lane) * 4) = v;
+            for (int c = 0; c < NCH; ++c) {
+#pragma unroll
+                for (int v4 = 0; v4 < 4; ++v4) {
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = o[rb][c][v4 * 4 + e];
+                    store4<T>(dst + c * 32 + v4 * 8 + g * 4, v);
+                }
+            }
+        } else {
+            // partials in the input dtype: one 64-lane store writes 64 x 4
+            // consecutive elements
+            T* ws = static_cast<T*>(p.ws_o) + (size_t)wl * (ROWS_WG * DL) + (size_t)rb * (32 * DL) +
+                    (size_t)half * NCH * (4 * 64 * 4);
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+#pragma unroll
+                for (int v4 = 0; v4 < 4; ++v4) {
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = o[rb][c][v4 * 4 + e];
+                    store4<T>(ws + ((c * 4 + v4) * 64 + lane) * 4, v);
+                }
             }
         }
     }
@@ -783,24 +809,40 @@ __global__ __launch_bounds__(256) void verify_combine(const VerifyParams p) {
     const int row = rt * ROWS_WG + prow;
     if (row >= p.rows) return;
     const int64_t qrow = (int64_t)b * p.rows + row;
+    // splits in batches of KB with all loads of a batch issued together (the
+    // partials sit in L2 / last-level cache: latency, not bandwidth, decides);
+    // indices past the last split repeat it with weight zero
+    constexpr int KB = 8;
+    auto slot_of = [&](int s) { return p.wg_begin[b] + min(s, ns - 1) * p.row_tiles + rt; };
     float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) {
-        const int slot = p.wg_begin[b] + s * p.row_tiles + rt;
-        M = fmaxf(M, p.ws_lse[(size_t)slot * ROWS_WG + prow]);
+    for (int s0 = 0; s0 < ns; s0 += KB) {
+        float l[KB];
+#pragma unroll
+        for (int k = 0; k < KB; ++k) l[k] = p.ws_lse[(size_t)slot_of(s0 + k) * ROWS_WG + prow];
+#pragma unroll
+        for (int k = 0; k < KB; ++k) M = fmaxf(M, l[k]);
     }
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     float wsum = 0.f;
-    for (int s = 0; s < ns; ++s) {
-        const int slot = p.wg_begin[b] + s * p.row_tiles + rt;
-        const float ls = p.ws_lse[(size_t)slot * ROWS_WG + prow];
-        const float w = ls == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ls - M);
-        const float4 v = *reinterpret_cast<const float4*>(
-            p.ws_o + ((size_t)slot * NW + wave) * (NCTW * 4 * 64 * 4) + ((c * 4 + grp) * 64 + lane) * 4);
-        acc[0] += w * v.x;
-        acc[1] += w * v.y;
-        acc[2] += w * v.z;
-        acc[3] += w * v.w;
-        wsum += w;
+    for (int s0 = 0; s0 < ns; s0 += KB) {
+        float l[KB];
+        float4 v[KB];
+#pragma unroll
+        for (int k = 0; k < KB; ++k) {
+            const int slot = slot_of(s0 + k);
+            l[k] = p.ws_lse[(size_t)slot * ROWS_WG + prow];
+            v[k] = load4<T>(static_cast<const T*>(p.ws_o) + ((size_t)slot * NW + wave) * (NCTW * 4 * 64 * 4) +
+                            ((c * 4 + grp) * 64 + lane) * 4);
+        }
+#pragma unroll
+        for (int k = 0; k < KB; ++k) {
+            const float w = (s0 + k >= ns || l[k] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(l[k] - M);
+            acc[0] += w * v[k].x;
+            acc[1] += w * v[k].y;
+            acc[2] += w * v[k].z;
+            acc[3] += w * v[k].w;
+            wsum += w;
+        }
     }
     const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
 #pragma unroll
@@ -831,6 +873,7 @@ int check_desc(const ddt_attn_desc* d, const int32_t* prefix_len_host) {
     if (d == nullptr || prefix_len_host == nullptr) return DDT_EINVAL;
     if (d->B < 1 || d->B > DDT_MAX_BATCH || d->H < 1 || d->N < 1 || d->N > DDT_MAX_NODES) return DDT_EINVAL;
     if (d->kv_chunk < 0) return DDT_EINVAL;
+    if (!(d->scale > 0.f) || !isfinite(d->scale)) return DDT_EINVAL;  // the softmax takes maxima of unscaled dots
     const bool k2 = d->d_lat == 512 && d->d_rope == 64 && d->dtype == DDT_BF16;
     const bool tiny = d->d_lat == 64 && d->d_rope == 16 && d->dtype == DDT_F32;
     if (!k2 && !tiny) return DDT_EUNSUPPORTED;
@@ -875,7 +918,7 @@ Plan make_plan(const ddt_attn_desc* d, const int32_t* P, VerifyParams* vp) {
     pl.total_wg = (int)total;
     if (vp) vp->wg_begin[d->B] = pl.total_wg;
     if (pl.any_split) {
-        const size_t o = (size_t)pl.total_wg * ROWS_WG * d->d_lat * sizeof(float);
+        const size_t o = (size_t)pl.total_wg * ROWS_WG * d->d_lat * (size_t)ddt::elem_bytes(d->dtype);
         pl.ws_lse_off = ddt::round_up(o, 256);
         pl.ws_bytes = pl.ws_lse_off + ddt::round_up((size_t)pl.total_wg * ROWS_WG * sizeof(float), 256);
     }
@@ -919,7 +962,7 @@ extern "C" int ddt_verify_attn(const ddt_attn_desc* d, const void* q_lat, const 
     if (pl.ws_bytes > 0) {
         if (workspace == nullptr || workspace_bytes < pl.ws_bytes || !ddt::aligned(workspace, 256))
             return DDT_EWORKSPACE;
-        vp.ws_o = static_cast<float*>(workspace);
+        vp.ws_o = workspace;
         vp.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.ws_lse_off);
     }
     vp.q_lat = q_lat;

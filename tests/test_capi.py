@@ -63,5 +63,9 @@ def test_host_side_validation(lib):
     assert lib.ddt_verify_workspace(ctypes.byref(bad), pl, ctypes.byref(n)) == -1   # stride alignment
     bad = ddt.AttnDesc(129, 8, 64, 512, 64, ddt.DDT_BF16, 0.04, 0, 576, 576, 576, 576)
     assert lib.ddt_verify_workspace(ctypes.byref(bad), pl, ctypes.byref(n)) == -1   # batch limit
+    for scale in (0.0, -0.04, float("inf"), float("nan")):                         # scale must be > 0
+        bad = ddt.AttnDesc(1, 8, 64, 512, 64, ddt.DDT_BF16, scale, 0, 576, 576, 576, 576)
+        assert lib.ddt_verify_workspace(ctypes.byref(bad), pl, ctypes.byref(n)) == -1, scale
+    assert lib.ddt_verify_workspace(ctypes.byref(d), pl, ctypes.byref(n)) == 0
     assert lib.ddt_verify_attn(ctypes.byref(d), null, null, null, null, null, pl, null, null, null,
                                null, 0, null) == -1
