@@ -4,7 +4,7 @@ A step is one pass of the whole hot path over one batch of synthetic input
 already resident in HBM:
     parents -> ancestor mask -> tree-verify MLA attention (absorbed, bf16,
     fp32 accumulate) -> argmax over the target logits -> greedy acceptance
-    -> KV compaction (+ length update).
+    + KV compaction (+ length update), the last two in one launch.
 The default workload is the K2-like single-GPU head share: 1 request,
 8 heads, kv_lora_rank 512 + rope 64, prefix 4096, 64 tree nodes (a
 best-first tree from seeded top-4 draft candidates), target logits over a
@@ -143,7 +143,7 @@ def main():
     am_ws = None
     if logits is not None:
         n = ddt.argmax_workspace_bytes(B * N, logits.shape[1])
-        am_ws = torch.empty((max(n, 1),), dtype=torch.uint8, device=dev)
+        am_ws = torch.zeros((max(n, 16),), dtype=torch.uint8, device=dev)   # zero before first use
     acc = torch.empty((B,), dtype=torch.int32, device=dev)
     path = torch.empty((B, N), dtype=torch.int32, device=dev)
     tok = torch.empty((B, N), dtype=torch.int32, device=dev)
@@ -163,8 +163,8 @@ def main():
             t = tids.view(B, N)
         else:
             t = target
-        ddt.greedy_accept(t, draft, parents, acc, path, tok)
-        ddt.compact_kv(ckv, kpe, kv_base, prefix, path, acc)
+        # acceptance + compaction (and the length update) in one launch
+        ddt.accept_compact(t, draft, parents, ckv, kpe, kv_base, prefix, acc, path, tok)
 
     if args.traffic_probe:
         ddt.build_mask(parents, mask, depth, terr)

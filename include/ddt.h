@@ -146,6 +146,10 @@ int ddt_verify_attn(const ddt_attn_desc* d, const void* q_lat, const void* q_pe,
  * r of logits (row r at logits + r*ld, V entries, dtype fp32 or bf16).  -0
  * and +0 compare equal; a NaN counts as larger than every number, so the
  * first NaN wins.  rows >= 0, 1 <= V <= 2^31-1, ld >= V.
+ * Workspace: ddt_argmax_workspace bytes (16-byte aligned), which must be
+ * zero-filled before the first call; every call leaves it zero-filled
+ * again, so it can be reused without clearing.  Concurrent calls must not
+ * share one workspace.
  */
 int ddt_argmax_workspace(int64_t rows, int64_t V, size_t* bytes);
 int ddt_argmax(const void* logits, int dtype, int64_t rows, int64_t V, int64_t ld, int32_t* idx,
@@ -188,6 +192,21 @@ int ddt_greedy_accept(const int32_t* target_ids, const int32_t* draft_ids, const
 int ddt_compact_kv(void* ckv, int64_t ld_ckv, void* kpe, int64_t ld_kpe, int dtype, int d_lat,
                    int d_rope, const int64_t* kv_base, int32_t* prefix_len, const int32_t* path,
                    const int32_t* accept_len, int B, int N, int32_t* src_slot, hipStream_t stream);
+
+/*
+ * Acceptance and compaction in one launch.  [Ambition], section "The
+ * Knowledge Architecture"; [Keystone], sections "The Reasoning That
+ * Preceded the Header" and "Mistakes and Iterative Refinement".  The same
+ * results as ddt_greedy_accept followed by ddt_compact_kv on the path it
+ * found: one workgroup per request walks the tree, writes accept_len, path
+ * and tokens, then moves the accepted rows and advances prefix_len.
+ * Arguments, layouts and errors as for those two calls (the walk's path is
+ * always a valid compaction path).
+ */
+int ddt_accept_compact(const int32_t* target_ids, const int32_t* draft_ids, const int32_t* parents, int B, int N,
+                       int32_t* accept_len, int32_t* path, int32_t* tokens, void* ckv, int64_t ld_ckv, void* kpe,
+                       int64_t ld_kpe, int dtype, int d_lat, int d_rope, const int64_t* kv_base, int32_t* prefix_len,
+                       int32_t* src_slot, hipStream_t stream);
 
 #ifdef __cplusplus
 }

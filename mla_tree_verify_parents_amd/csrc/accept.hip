@@ -2,13 +2,10 @@
 // "The Knowledge Architecture": walk the verified tree greedily for the
 // longest path matching the target's predictions).
 //
-// One wavefront per request.  The tree is staged in LDS; each step of the
-// walk is a wavefront-wide search for the lowest-numbered child k > c of the
-// current node c whose draft token equals the target token after c: 64
-// candidate nodes are tested at once and the ballot's lowest set bit is the
-// answer.  The current node strictly increases, so the walk ends after at
-// most N steps even for a malformed tree.
+// One wavefront per request, the tree staged in LDS; the walk itself is
+// ddt::greedy_walk (tree_tail.h).
 #include "common.h"
+#include "tree_tail.h"
 
 namespace {
 
@@ -29,36 +26,9 @@ __global__ __launch_bounds__(ddt::kWave) void accept_kernel(const int32_t* __res
         sdraft[i] = draft[off + i];
     }
     __syncthreads();
-    int c = 0, n = 1;
-    if (lane == 0) spath[0] = 0;
-    for (;;) {
-        const int want = target[off + c];
-        int next = -1;
-        for (int base = c + 1; base < N; base += ddt::kWave) {
-            const int k = base + lane;
-            const bool hit = k < N && spar[k] == c && sdraft[k] == want;
-            const uint64_t m = __ballot(hit);
-            if (m != 0) {
-                next = base + __builtin_ctzll(m);
-                break;
-            }
-        }
-        if (next < 0) break;
-        c = next;
-        if (lane == 0) spath[n] = c;
-        ++n;
-    }
+    const int n = ddt::greedy_walk(target, off, spar, sdraft, N, spath, lane);
     __syncthreads();
-    const int bonus = target[off + c];
-    for (int j = lane; j < N; j += ddt::kWave) {
-        const int p = j < n ? spath[j] : -1;
-        path[off + j] = p;
-        int tok = -1;
-        if (j + 1 < n) tok = sdraft[spath[j + 1]];
-        else if (j + 1 == n) tok = bonus;
-        tokens[off + j] = tok;
-    }
-    if (lane == 0) accept_len[b] = n - 1;
+    ddt::write_accept(target, off, sdraft, spath, n, N, b, lane, accept_len, path, tokens);
 }
 
 }  // namespace

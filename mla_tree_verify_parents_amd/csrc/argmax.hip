@@ -8,8 +8,11 @@
 //   key = order(value) << 32 | (0xffffffff - index)
 // where order() maps fp32 bits to an unsigned integer with the same order
 // as the values (NaN above +inf, -0 equal to +0).  The maximum key is the
-// lowest index of the largest value.  With several chunks per row the
-// per-chunk keys go to the workspace and a second small kernel reduces them.
+// lowest index of the largest value.  With several chunks per row each
+// workgroup folds its key into the row's slot of the workspace with a 64-bit
+// atomic max and counts itself in; the row's last workgroup writes the index
+// and clears the slot, so one launch does the whole reduction and leaves the
+// workspace zeroed for the next call.
 #include "common.h"
 
 namespace {
@@ -88,11 +91,17 @@ __device__ inline uint64_t block_max(uint64_t v) {
     return v;  // valid in thread 0
 }
 
+// Per-row merge slot of the workspace (zero between calls).
+struct RowSlot {
+    unsigned long long key;  // running maximum key of the row
+    unsigned int done;       // workgroups of the row that have folded their key in
+    unsigned int pad;
+};
+
 template <typename T, bool kVec>
 __global__ __launch_bounds__(kArgThreads) void argmax_chunks(const T* __restrict__ logits, int64_t V,
                                                              int64_t ld, int nchunk, int64_t chunk,
-                                                             int32_t* __restrict__ idx,
-                                                             uint64_t* __restrict__ partial) {
+                                                             int32_t* __restrict__ idx, RowSlot* __restrict__ slots) {
     const int64_t r = blockIdx.x / nchunk;
     const int c = blockIdx.x - (int)(r * nchunk);
     const int64_t c0 = (int64_t)c * chunk;
@@ -100,21 +109,23 @@ __global__ __launch_bounds__(kArgThreads) void argmax_chunks(const T* __restrict
     uint64_t best = scan_chunk<T, kVec>(logits + r * ld, c0, c1);
     best = block_max(best);
     if (threadIdx.x == 0) {
-        if (nchunk == 1)
+        if (nchunk == 1) {
             idx[r] = (int32_t)(0xffffffffu - (uint32_t)best);
-        else
-            partial[blockIdx.x] = best;
+        } else {
+            RowSlot* s = slots + r;
+            // the max is performed (its old value has come back) before this
+            // workgroup counts itself in; no cache-wide fence is needed
+            const unsigned long long prev = atomicMax(&s->key, (unsigned long long)best);
+            asm volatile("s_waitcnt vmcnt(0)" :: "v"(prev) : "memory");
+            if (atomicAdd(&s->done, 1u) == (unsigned)nchunk - 1) {
+                // every other workgroup of the row has folded its key in
+                const unsigned long long k = atomicMax(&s->key, 0ull);
+                idx[r] = (int32_t)(0xffffffffu - (uint32_t)k);
+                atomicExch(&s->key, 0ull);
+                atomicExch(&s->done, 0u);
+            }
+        }
     }
-}
-
-__global__ __launch_bounds__(ddt::kWave) void argmax_merge(const uint64_t* __restrict__ partial,
-                                                           int nchunk, int32_t* __restrict__ idx) {
-    const int64_t r = blockIdx.x;
-    uint64_t best = 0;
-    for (int c = threadIdx.x; c < nchunk; c += ddt::kWave) best = umax64(best, partial[r * nchunk + c]);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) best = umax64(best, __shfl_xor(best, o, ddt::kWave));
-    if (threadIdx.x == 0) idx[r] = (int32_t)(0xffffffffu - (uint32_t)best);
 }
 
 // Chunks per row: enough rows x chunks to give ~2048 workgroups, chunks of at
@@ -137,18 +148,14 @@ int launch(const void* logits, int64_t rows, int64_t V, int64_t ld, int32_t* idx
     plan(rows, V, &nchunk, &chunk);
     const bool vec = ddt::aligned(logits, 16) && ((ld * (int64_t)sizeof(T)) % 16 == 0);
     const dim3 grid((unsigned)(rows * nchunk));
-    auto* part = static_cast<uint64_t*>(ws);
+    auto* slots = static_cast<RowSlot*>(ws);
     if (vec)
         hipLaunchKernelGGL((argmax_chunks<T, true>), grid, dim3(kArgThreads), 0, stream,
-                           static_cast<const T*>(logits), V, ld, nchunk, chunk, idx, part);
+                           static_cast<const T*>(logits), V, ld, nchunk, chunk, idx, slots);
     else
         hipLaunchKernelGGL((argmax_chunks<T, false>), grid, dim3(kArgThreads), 0, stream,
-                           static_cast<const T*>(logits), V, ld, nchunk, chunk, idx, part);
+                           static_cast<const T*>(logits), V, ld, nchunk, chunk, idx, slots);
     DDT_CHECK_LAUNCH();
-    if (nchunk > 1) {
-        hipLaunchKernelGGL(argmax_merge, dim3((unsigned)rows), dim3(ddt::kWave), 0, stream, part, nchunk, idx);
-        DDT_CHECK_LAUNCH();
-    }
     return DDT_OK;
 }
 
@@ -159,7 +166,7 @@ extern "C" int ddt_argmax_workspace(int64_t rows, int64_t V, size_t* bytes) {
     int nchunk;
     int64_t chunk;
     plan(rows > 0 ? rows : 1, V, &nchunk, &chunk);
-    *bytes = nchunk > 1 ? (size_t)rows * nchunk * sizeof(uint64_t) : 0;
+    *bytes = nchunk > 1 ? (size_t)rows * sizeof(RowSlot) : 0;
     return DDT_OK;
 }
 
@@ -172,7 +179,7 @@ extern "C" int ddt_argmax(const void* logits, int dtype, int64_t rows, int64_t V
     if (rows > 0x7fffffff / 64) return DDT_EINVAL;
     size_t need = 0;
     ddt_argmax_workspace(rows, V, &need);
-    if (need > 0 && (workspace == nullptr || workspace_bytes < need || !ddt::aligned(workspace, 8)))
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need || !ddt::aligned(workspace, 16)))
         return DDT_EWORKSPACE;
     int nchunk;
     int64_t chunk;

@@ -53,8 +53,10 @@ def lib():
         L.ddt_argmax.argtypes = [P, i32, i64, i64, i64, P, P, sz, P]
         L.ddt_greedy_accept.argtypes = [P, P, P, i32, i32, P, P, P, P]
         L.ddt_compact_kv.argtypes = [P, i64, P, i64, i32, i32, i32, P, P, P, P, i32, i32, P, P]
+        L.ddt_accept_compact.argtypes = [P, P, P, i32, i32, P, P, P, P, i64, P, i64, i32, i32, i32, P, P, P, P]
         for f in ("ddt_version", "ddt_build_mask", "ddt_verify_workspace", "ddt_verify_attn",
-                  "ddt_argmax_workspace", "ddt_argmax", "ddt_greedy_accept", "ddt_compact_kv"):
+                  "ddt_argmax_workspace", "ddt_argmax", "ddt_greedy_accept", "ddt_compact_kv",
+                  "ddt_accept_compact"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -175,7 +177,11 @@ def argmax_workspace_bytes(rows: int, V: int) -> int:
 
 
 def argmax(logits, idx=None, workspace=None, stream=None):
-    """logits [rows, V] fp32/bf16 (2-D view) -> idx [rows] int32."""
+    """logits [rows, V] fp32/bf16 (2-D view) -> idx [rows] int32.
+
+    workspace: argmax_workspace_bytes(rows, V) bytes of device memory,
+    zero-filled before its first use (every call leaves it zeroed again).
+    """
     _dev(logits, None, "logits")
     ld = _rows(logits, "logits")
     rows, V = logits.shape
@@ -184,7 +190,7 @@ def argmax(logits, idx=None, workspace=None, stream=None):
     _contig(idx, torch.int32, "idx")
     need = argmax_workspace_bytes(rows, V)
     if workspace is None and need > 0:
-        workspace = torch.empty((need,), dtype=torch.uint8, device=logits.device)
+        workspace = torch.zeros((need,), dtype=torch.uint8, device=logits.device)  # zero before first use
     ws_n = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().ddt_argmax(_p(logits), _dtype_code(logits), rows, V, ld, _p(idx), _p(workspace), ws_n,
                             _stream(stream)), "ddt_argmax")
@@ -221,3 +227,29 @@ def compact_kv(ckv, kpe, kv_base, prefix_len, path, accept_len, src_slot=None, s
                                 ckv.shape[1], kpe.shape[1], _p(kv_base), _p(prefix_len), _p(path),
                                 _p(accept_len), B, N, _p(src_slot), _stream(stream)), "ddt_compact_kv")
     return prefix_len, src_slot
+
+
+def accept_compact(target_ids, draft_ids, parents, ckv, kpe, kv_base, prefix_len, accept_len=None, path=None,
+                   tokens=None, src_slot=None, stream=None):
+    """greedy_accept + compact_kv in one launch -> (accept_len, path, tokens)."""
+    for t, n in ((target_ids, "target_ids"), (draft_ids, "draft_ids"), (parents, "parents")):
+        _contig(t, torch.int32, n)
+    _dev(ckv, None, "ckv")
+    _dev(kpe, ckv.dtype, "kpe")
+    _contig(kv_base, torch.int64, "kv_base")
+    _contig(prefix_len, torch.int32, "prefix_len")
+    B, N = parents.shape
+    dev = parents.device
+    if accept_len is None:
+        accept_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    if path is None:
+        path = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if tokens is None:
+        tokens = torch.empty((B, N), dtype=torch.int32, device=dev)
+    for t, n in ((accept_len, "accept_len"), (path, "path"), (tokens, "tokens")):
+        _contig(t, torch.int32, n)
+    _check(lib().ddt_accept_compact(_p(target_ids), _p(draft_ids), _p(parents), B, N, _p(accept_len), _p(path),
+                                    _p(tokens), _p(ckv), _rows(ckv, "ckv"), _p(kpe), _rows(kpe, "kpe"),
+                                    _dtype_code(ckv), ckv.shape[1], kpe.shape[1], _p(kv_base), _p(prefix_len),
+                                    _p(src_slot), _stream(stream)), "ddt_accept_compact")
+    return accept_len, path, tokens

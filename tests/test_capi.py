@@ -54,6 +54,12 @@ def test_host_side_validation(lib):
     assert lib.ddt_argmax(null, 0, 4, 10, 5, null, null, 0, null) == -1     # ld < V
     assert lib.ddt_argmax(null, 7, 4, 10, 10, null, null, 0, null) == -2    # dtype
     assert lib.ddt_compact_kv(null, 576, null, 576, 1, 512, 64, null, null, null, null, 1, 0, null, null) == -1
+    assert lib.ddt_accept_compact(null, null, null, 1, 0, null, null, null, null, 576, null, 576, 1, 512, 64,
+                                  null, null, null, null) == -1                    # N < 1
+    assert lib.ddt_accept_compact(null, null, null, 1, 8, null, null, null, null, 576, null, 576, 1, 512, 64,
+                                  null, null, null, null) == -1                    # null pointers
+    assert lib.ddt_accept_compact(null, null, null, 0, 8, null, null, null, null, 576, null, 576, 1, 512, 64,
+                                  null, null, null, null) == 0                     # nothing to do
     d = ddt.AttnDesc(1, 8, 64, 512, 64, ddt.DDT_BF16, 0.04, 0, 576, 576, 576, 576)
     pl = (ctypes.c_int32 * 1)(100)
     n = ctypes.c_size_t(0)

@@ -82,6 +82,19 @@ def test_accept_random(orc, N, V):
 
 # --------------------------------------------------------------- argmax ----
 
+def test_argmax_workspace_reuse(orc):
+    """One workspace across calls: each call must leave it ready for the next."""
+    rows, V = 64, 163840
+    ws = torch.zeros((ddt.argmax_workspace_bytes(rows, V),), dtype=torch.uint8, device="cuda")
+    rng = np.random.default_rng(7)
+    for k in range(3):
+        x = rng.standard_normal((rows, V)).astype(np.float32)
+        x[np.arange(rows), rng.integers(0, V, rows)] += 10.0 + k
+        got = to_host(ddt.argmax(to_dev(x), workspace=ws))
+        assert (got == orc.argmax(x)).all(), k
+    assert int(ws.sum().item()) == 0
+
+
 @pytest.mark.parametrize("rows,V", [(64, 163840), (3, 1), (5, 1000), (2100, 4099), (2048, 4096), (1, 300001)])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_argmax(orc, rows, V, dtype):
@@ -160,6 +173,34 @@ def test_compact_separate_arrays_and_invalid(orc):
     assert to_host(dpl).tolist() == [13, 20, 30]
     s = to_host(src)
     assert s[0].tolist() == [10, 12, 15, -1, -1, -1] and (s[1:] == -1).all()
+
+
+@pytest.mark.parametrize("dtype,dl,dr,N", [("bf16", 512, 64, 64), ("f32", 64, 16, 40), ("bf16", 512, 64, 1024)])
+def test_accept_compact_fused(orc, dtype, dl, dr, N):
+    """ddt_accept_compact == greedy acceptance then compaction (oracle), on
+    random and chain trees (a full chain moves every row onto itself)."""
+    rng = np.random.default_rng(N + dl)
+    B, V = 6, 3
+    par = synth.random_parents(rng, B, N)
+    par[0] = np.arange(-1, N - 1)
+    dr_ = rng.integers(0, V, size=(B, N)).astype(np.int32)
+    t = synth.planted_targets(rng, par, dr_, V, 0.8)
+    t[0, :-1] = dr_[0, 1:]                         # request 0 accepts its whole chain
+    P = rng.integers(0, 300, B).astype(np.int32)
+    cap = 300 + N + 8
+    base = np.array([3 + cap * b for b in range(B)], np.int64)
+    pool = _tagged(int(base[-1]) + cap, dl + dr, dtype)
+    dpool, dpl = to_dev(pool), to_dev(P)
+    src = torch.empty((B, N), dtype=torch.int32, device="cuda")
+    acc, path, tok = ddt.accept_compact(to_dev(t), to_dev(dr_), to_dev(par), dpool[:, :dl], dpool[:, dl:],
+                                        to_dev(base), dpl, src_slot=src)
+    oa, op, ot = orc.greedy_accept(t, dr_, par)
+    opool = pool.copy()
+    opl, osrc = orc.compact_kv(opool[:, :dl], opool[:, dl:], base, P, op, oa)
+    assert oa[0] == N - 1
+    assert (to_host(acc) == oa).all() and (to_host(path) == op).all() and (to_host(tok) == ot).all()
+    assert (to_host(dpl) == opl).all() and (to_host(src) == osrc).all()
+    assert (to_host(dpool) == opool).all()
 
 
 # ------------------------------------------------------------- attention ----
