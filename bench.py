@@ -3,8 +3,8 @@
 A step is one pass of the whole hot path over one batch of synthetic input
 already resident in HBM:
     parents -> ancestor mask -> tree-verify MLA attention (absorbed, bf16,
-    fp32 accumulate) -> argmax over the target logits -> greedy acceptance
-    + KV compaction (+ length update), the last two in one launch.
+    fp32 accumulate) and argmax over the target logits (one launch) ->
+    greedy acceptance + KV compaction (+ length update, one launch).
 The default workload is the K2-like single-GPU head share: 1 request,
 8 heads, kv_lora_rank 512 + rope 64, prefix 4096, 64 tree nodes (a
 best-first tree from seeded top-4 draft candidates), target logits over a
@@ -157,11 +157,14 @@ def main():
     def step():
         prefix.copy_(prefix0)                      # same committed length every step
         ddt.build_mask(parents, mask, depth, terr)
-        attn()
         if logits is not None:
-            ddt.argmax(logits, tids, am_ws)
+            # attention and the (independent) target argmax in one launch:
+            # the argmax workgroups take the CUs the attention leaves idle
+            ddt.verify_attn_argmax(q_lat, q_pe, ckv, kpe, kv_base, P_host, mask, logits, H=H, scale=w.scale,
+                                   out=out, lse=lse, workspace=ws, idx=tids, argmax_workspace=am_ws)
             t = tids.view(B, N)
         else:
+            attn()
             t = target
         # acceptance + compaction (and the length update) in one launch
         ddt.accept_compact(t, draft, parents, ckv, kpe, kv_base, prefix, acc, path, tok)

@@ -156,6 +156,26 @@ int ddt_argmax(const void* logits, int dtype, int64_t rows, int64_t V, int64_t l
                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Tree-verify attention and target argmax in one launch: the results of
+ * ddt_verify_attn and of ddt_argmax (same arguments, same outputs, same
+ * workspace contracts).  The two are independent; the argmax runs as extra
+ * workgroups dispatched after every attention workgroup, so on a small
+ * batch it fills the CUs the attention leaves idle instead of following it.
+ */
+typedef struct {
+    const void* logits;     /* [rows][ld], dtype fp32 or bf16                  */
+    int dtype;              /* ddt_dtype                                       */
+    int64_t rows, V, ld;
+    int32_t* idx;           /* [rows] device, lowest index of the row maximum  */
+    void* workspace;        /* ddt_argmax_workspace bytes, zero before first use */
+    size_t workspace_bytes;
+} ddt_argmax_task;
+int ddt_verify_attn_argmax(const ddt_attn_desc* d, const void* q_lat, const void* q_pe, const void* ckv,
+                           const void* kpe, const int64_t* kv_base, const int32_t* prefix_len_host,
+                           const uint64_t* mask, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                           const ddt_argmax_task* am, hipStream_t stream);
+
+/*
  * Greedy tree acceptance.  [Ambition], section "The Knowledge
  * Architecture": walk the verified tree greedily for the longest path that
  * matches the target's predictions.  target_ids[b][c] is the target's

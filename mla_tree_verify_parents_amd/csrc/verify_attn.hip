@@ -43,6 +43,7 @@
 
 #include <type_traits>
 
+#include "argmax_scan.h"
 #include "common.h"
 
 namespace {
@@ -319,6 +320,10 @@ __device__ inline float4 load4<float>(const float* src) {
     return *reinterpret_cast<const float4*>(src);
 }
 
+// Wait until this wavefront's vector-memory loads (the LDS-DMA of later
+// tiles, issued as inline asm the compiler does not count) have landed.
+__device__ inline void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 struct VerifyParams {
     const void* q_lat;
     const void* q_pe;
@@ -336,7 +341,165 @@ struct VerifyParams {
     int P[DDT_MAX_BATCH];
     int nsplit[DDT_MAX_BATCH];
     int wg_begin[DDT_MAX_BATCH + 1];
+    // target argmax riding along in the same launch (workgroups n_attn ..)
+    int n_attn;                 // attention workgroups (the rest are argmax workgroups)
+    int am_wgs, am_dtype, am_vec;
+    int64_t am_rows, am_V, am_ld, am_E;  // am_E: elements of the flattened rows x V range per workgroup
+    const void* am_logits;
+    int32_t* am_idx;
+    ddt::RowSlot* am_slots;
 };
+
+// Argmax workgroup `am_id` scans elements [am_id*E, (am_id+1)*E) of the
+// rows x V logits taken as one flat range (equal shares for every
+// workgroup); a row is split among the workgroups whose shares touch it and
+// they merge as in ddt_argmax.  With one wavefront per SIMD, loads alone
+// cannot keep enough bytes in flight, so the share streams through the
+// workgroup's LDS in stages by LDS-DMA (double buffered: the next stage
+// loads while this one is reduced).  One wavefront per SIMD also issues
+// VALU work slowly, so the reduction is kept lean: 32-bit offsets within
+// the row's segment, per 16-byte chunk the float maximum (v_max3) and an
+// unordered-compare NaN flag, and a search for the first index holding
+// the maximum only when a thread's maximum improves (first chunk whose
+// maximum equals it, then the element inside, re-read from LDS).  A thread
+// whose stage holds a NaN also reduces it the exact key way, which orders
+// NaN above every number.  Shares start at whole 16-byte chunks (rows of
+// a multiple of 16 bytes, V a multiple of the chunk), so a stage's valid
+// elements end on a chunk boundary.
+template <typename L, int kStageBytes>
+__device__ void argmax_stream(const VerifyParams& p, int am_id, char* lds) {
+    static_assert(kStageBytes % (16 * kThreads) == 0, "whole DMA instructions and 16-byte chunks per thread");
+    constexpr int VEC = 16 / (int)sizeof(L);
+    constexpr int kChunks = kStageBytes / 1024 / (kThreads / 64);  // DMA instructions per wavefront per stage
+    constexpr int kPerThread = kStageBytes / 16 / kThreads;        // 16-byte chunks a thread reduces per stage
+    constexpr int kStageElems = kStageBytes / (int)sizeof(L);
+    typedef uint32_t V4 __attribute__((ext_vector_type(4)));
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t V = p.am_V, E = p.am_E, total = p.am_rows * V;
+    const int64_t e0 = (int64_t)am_id * E;
+    const int64_t e1 = e0 + E < total ? e0 + E : total;
+    const uint32_t lds0 = lds_addr(lds);
+    for (int64_t r = e0 / V; r * V < e1; ++r) {
+        const int64_t c0 = e0 > r * V ? e0 - r * V : 0;
+        const int len = (int)((e1 < (r + 1) * V ? e1 - r * V : V) - c0);  // segment [c0, c0 + len) of row r
+        const char* seg = static_cast<const char*>(p.am_logits) + (r * p.am_ld + c0) * (int64_t)sizeof(L);
+        const int nst = (len + kStageElems - 1) / kStageElems;
+        auto issue = [&](int st) {
+            const int s0 = st * kStageElems;
+            const int n = len - s0 < kStageElems ? len - s0 : kStageElems;
+            const u32x4 rs = buffer_rsrc(seg + (int64_t)s0 * (int)sizeof(L), n * (int)sizeof(L));
+            const uint32_t buf = lds0 + (uint32_t)((st & 1) * kStageBytes);
+#pragma unroll
+            for (int i = 0; i < kChunks; ++i) {
+                const int j = wave * kChunks + i;
+                dma16(rs, buf + (uint32_t)(j * 1024), (uint32_t)(lane * 16 + j * 1024));
+            }
+        };
+        float bv = -INFINITY;
+        int bl = -1;  // offset in the segment of the thread's first maximum
+        uint64_t bexact = 0;
+        issue(0);
+        for (int st = 0; st < nst; ++st) {
+            if (st + 1 < nst) {
+                issue(st + 1);
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kChunks) : "memory");  // stage st landed
+            } else {
+                wait_vmem_all();
+            }
+            __syncthreads();  // every wavefront's part of stage st is in LDS
+            const int s0 = st * kStageElems;
+            const int nch = (len - s0 < kStageElems ? len - s0 : kStageElems) / VEC;  // valid chunks
+            const char* buf = lds + (st & 1) * kStageBytes;
+            V4 x[kPerThread];
+#pragma unroll
+            for (int u = 0; u < kPerThread; ++u) x[u] = *reinterpret_cast<const V4*>(buf + (tid + kThreads * u) * 16);
+            float mu[kPerThread];
+            bool nan = false;
+#pragma unroll
+            for (int u = 0; u < kPerThread; ++u) {
+                const L* e = reinterpret_cast<const L*>(&x[u]);
+                float c = ddt::widen<L>(e[0]);
+                bool q = false;
+#pragma unroll
+                for (int k = 1; k < VEC; k += 2) {
+                    const float a = ddt::widen<L>(e[k]);
+                    const float b2 = k + 1 < VEC ? ddt::widen<L>(e[k + 1]) : a;
+                    c = ddt::fmax3_raw(c, a, b2);
+                    q |= __builtin_isunordered(a, b2);
+                }
+                q |= __builtin_isunordered(ddt::widen<L>(e[0]), ddt::widen<L>(e[0]));
+                const bool valid = tid + kThreads * u < nch;
+                mu[u] = valid ? c : -INFINITY;
+                nan |= valid && q;
+            }
+            float m = mu[0];
+#pragma unroll
+            for (int u = 1; u < kPerThread; u += 2) m = ddt::fmax3_raw(m, mu[u], u + 1 < kPerThread ? mu[u + 1] : mu[u]);
+            if (m > bv || bl < 0) {  // (the first stage always searches, -inf rows included)
+                int fu = -1;
+#pragma unroll
+                for (int u = kPerThread - 1; u >= 0; --u)
+                    if (mu[u] == m && tid + kThreads * u < nch) fu = u;
+                if (fu >= 0) {
+                    const V4 y = *reinterpret_cast<const V4*>(buf + (tid + kThreads * fu) * 16);
+                    const L* e = reinterpret_cast<const L*>(&y);
+                    int fk = VEC - 1;
+#pragma unroll
+                    for (int k = VEC - 2; k >= 0; --k)
+                        if (ddt::widen<L>(e[k]) == m) fk = k;
+                    bv = m;
+                    bl = s0 + (tid + kThreads * fu) * VEC + fk;
+                }
+            }
+            if (nan) {
+#pragma unroll
+                for (int u = 0; u < kPerThread; ++u) {
+                    const L* e = reinterpret_cast<const L*>(&x[u]);
+                    const int o = s0 + (tid + kThreads * u) * VEC;
+                    if (tid + kThreads * u < nch) {
+#pragma unroll
+                        for (int k = 0; k < VEC; ++k)
+                            bexact = ddt::umax64(bexact, ddt::pack_key(ddt::f32_bits<L>(e[k]), c0 + o + k));
+                    }
+                }
+            }
+            __syncthreads();  // stage st consumed: its buffer takes stage st+2
+        }
+        uint64_t key = bl >= 0 ? ddt::pack_key(__float_as_uint(bv), c0 + bl) : 0;
+        key = ddt::umax64(key, bexact);
+        key = ddt::block_max(key);
+        const int parts = (int)(((r + 1) * V - 1) / E - (r * V) / E + 1);
+        if (threadIdx.x == 0) ddt::finish_chunk(key, r, parts, p.am_idx, p.am_slots);
+    }
+}
+// Rows whose layout does not allow 16-byte loads (unaligned start, row
+// stride or length) take the plain exact scan.
+template <typename L>
+__device__ void argmax_plain(const VerifyParams& p, int am_id) {
+    const int64_t V = p.am_V, E = p.am_E, total = p.am_rows * V;
+    const int64_t e0 = (int64_t)am_id * E;
+    const int64_t e1 = e0 + E < total ? e0 + E : total;
+    const L* logits = static_cast<const L*>(p.am_logits);
+    for (int64_t r = e0 / V; r * V < e1; ++r) {
+        const int64_t c0 = e0 > r * V ? e0 - r * V : 0;
+        const int64_t c1 = e1 < (r + 1) * V ? e1 - r * V : V;
+        uint64_t key = ddt::scan_chunk_exact<L, false, 1>(logits + r * p.am_ld, c0, c1);
+        key = ddt::block_max(key);
+        const int parts = (int)(((r + 1) * V - 1) / E - (r * V) / E + 1);
+        if (threadIdx.x == 0) ddt::finish_chunk(key, r, parts, p.am_idx, p.am_slots);
+    }
+}
+template <int kStageBytes>
+__device__ inline void argmax_role(const VerifyParams& p, int am_id, char* lds) {
+    if (p.am_dtype == DDT_F32) {
+        if (p.am_vec) argmax_stream<float, kStageBytes>(p, am_id, lds);
+        else argmax_plain<float>(p, am_id);
+    } else {
+        if (p.am_vec) argmax_stream<uint16_t, kStageBytes>(p, am_id, lds);
+        else argmax_plain<uint16_t>(p, am_id);
+    }
+}
 
 template <typename T, int DL, int DR>
 struct Shape {
@@ -369,9 +532,6 @@ struct Shape {
     static_assert(LDS_BYTES + ROWS_WG * 4 + 4 <= 160 * 1024, "LDS budget");
 };
 
-// Wait until this wavefront's vector-memory loads (the LDS-DMA of later
-// tiles, issued as inline asm the compiler does not count) have landed.
-__device__ inline void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // One workgroup = one work item (request b, key split, tile of 64 query
 // rows).  Wavefronts 0 and 1 are score wavefronts (row groups 0 and 1: S^T,
@@ -383,7 +543,7 @@ __device__ inline void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "
 // MFMAs of tile j together with the softmax of tile j-1, and the value
 // wavefronts multiply tile j-2 while loading tile j+1 into the ring slot of
 // tile j-3.
-template <typename T, int DL, int DR>
+template <typename T, int DL, int DR, bool kArgmax>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void verify_split(
     const VerifyParams p) {
     using S = Shape<T, DL, DR>;
@@ -391,6 +551,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     using Frag = typename Tr::Frag;
     constexpr int KPL = S::KPL;
     __shared__ __attribute__((aligned(16))) char smem[S::LDS_BYTES];
+    if (kArgmax && (int)blockIdx.x >= p.n_attn) {
+        // dispatched after every attention workgroup, so it takes a CU the
+        // attention leaves idle
+        // stages of at most 64 KB, two of them in this kernel's LDS
+        constexpr int kAmStage = S::LDS_BYTES / 2 >= 65536 ? 65536 : (S::LDS_BYTES / 2) / 4096 * 4096;
+        argmax_role<kAmStage>(p, (int)blockIdx.x - p.n_attn, smem);
+        return;
+    }
     __shared__ float s_mref[ROWS_WG];  // per-row softmax reference, for the log-sum-exp
     __shared__ int s_redo;
 
@@ -399,7 +567,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const int grp = wave % NGRP;
 
     // ---- work item: (request, key split, row tile), XCD-contiguous ----
-    const int wl = ddt::xcd_logical_block(blockIdx.x, gridDim.x);
+    const int wl = ddt::xcd_logical_block(blockIdx.x, kArgmax ? p.n_attn : (int)gridDim.x);
     int b = 0;
     {
         int lo = 0, hi = p.B - 1;
@@ -810,18 +978,12 @@ __global__ __launch_bounds__(256) void verify_combine(const VerifyParams p) {
     if (row >= p.rows) return;
     const int64_t qrow = (int64_t)b * p.rows + row;
     // splits in batches of KB with all loads of a batch issued together (the
-    // partials sit in L2 / last-level cache: latency, not bandwidth, decides);
-    // indices past the last split repeat it with weight zero
-    constexpr int KB = 8;
+    // partials sit in L2 / last-level cache: latency, not bandwidth,
+    // decides), merged with a running maximum; indices past the last split
+    // repeat it with weight zero
+    constexpr int KB = 32;
     auto slot_of = [&](int s) { return p.wg_begin[b] + min(s, ns - 1) * p.row_tiles + rt; };
     float M = -INFINITY;
-    for (int s0 = 0; s0 < ns; s0 += KB) {
-        float l[KB];
-#pragma unroll
-        for (int k = 0; k < KB; ++k) l[k] = p.ws_lse[(size_t)slot_of(s0 + k) * ROWS_WG + prow];
-#pragma unroll
-        for (int k = 0; k < KB; ++k) M = fmaxf(M, l[k]);
-    }
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     float wsum = 0.f;
     for (int s0 = 0; s0 < ns; s0 += KB) {
@@ -834,6 +996,16 @@ __global__ __launch_bounds__(256) void verify_combine(const VerifyParams p) {
             v[k] = load4<T>(static_cast<const T*>(p.ws_o) + ((size_t)slot * NW + wave) * (NCTW * 4 * 64 * 4) +
                             ((c * 4 + grp) * 64 + lane) * 4);
         }
+        float mb = M;
+#pragma unroll
+        for (int k = 0; k < KB; ++k) mb = fmaxf(mb, s0 + k < ns ? l[k] : -INFINITY);
+        if (mb != M && M != -INFINITY) {  // rescale what earlier batches summed
+            const float r = __builtin_amdgcn_exp2f(M - mb);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] *= r;
+            wsum *= r;
+        }
+        M = mb;
 #pragma unroll
         for (int k = 0; k < KB; ++k) {
             const float w = (s0 + k >= ns || l[k] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(l[k] - M);
@@ -926,8 +1098,12 @@ Plan make_plan(const ddt_attn_desc* d, const int32_t* P, VerifyParams* vp) {
 }
 
 template <typename T, int DL, int DR>
-int launch(const VerifyParams& vp, const Plan& pl, hipStream_t stream) {
-    hipLaunchKernelGGL((verify_split<T, DL, DR>), dim3(pl.total_wg), dim3(kThreads), 0, stream, vp);
+int launch(const VerifyParams& vp, const Plan& pl, int n_argmax, hipStream_t stream) {
+    if (n_argmax > 0)
+        hipLaunchKernelGGL((verify_split<T, DL, DR, true>), dim3(pl.total_wg + n_argmax), dim3(kThreads), 0, stream,
+                           vp);
+    else
+        hipLaunchKernelGGL((verify_split<T, DL, DR, false>), dim3(pl.total_wg), dim3(kThreads), 0, stream, vp);
     DDT_CHECK_LAUNCH();
     if (pl.any_split) {
         const int nblk = vp.B * pl.row_tiles * NW * (DL / 64);
@@ -935,6 +1111,53 @@ int launch(const VerifyParams& vp, const Plan& pl, hipStream_t stream) {
         DDT_CHECK_LAUNCH();
     }
     return DDT_OK;
+}
+
+// Validates the call and fills the attention part of the launch parameters.
+int setup_attn(const ddt_attn_desc* d, const void* q_lat, const void* q_pe, const void* ckv, const void* kpe,
+               const int64_t* kv_base, const int32_t* prefix_len_host, const uint64_t* mask, void* out, float* lse,
+               void* workspace, size_t workspace_bytes, VerifyParams* vp, Plan* pl) {
+    int rc = check_desc(d, prefix_len_host);
+    if (rc != DDT_OK) return rc;
+    if (!q_lat || !q_pe || !ckv || !kpe || !kv_base || !mask || !out || !lse) return DDT_EINVAL;
+    if (!ddt::aligned(q_lat, 16) || !ddt::aligned(q_pe, 16) || !ddt::aligned(ckv, 16) || !ddt::aligned(kpe, 16) ||
+        !ddt::aligned(out, 16) || !ddt::aligned(lse, 4))
+        return DDT_EINVAL;
+    *pl = make_plan(d, prefix_len_host, vp);
+    if (pl->ws_bytes > 0) {
+        if (workspace == nullptr || workspace_bytes < pl->ws_bytes || !ddt::aligned(workspace, 256))
+            return DDT_EWORKSPACE;
+        vp->ws_o = workspace;
+        vp->ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl->ws_lse_off);
+    }
+    vp->q_lat = q_lat;
+    vp->q_pe = q_pe;
+    vp->ckv = ckv;
+    vp->kpe = kpe;
+    vp->kv_base = kv_base;
+    vp->mask = mask;
+    vp->out = out;
+    vp->lse = lse;
+    vp->ld_ql = d->ld_ql;
+    vp->ld_qp = d->ld_qp;
+    vp->ld_ckv = d->ld_ckv;
+    vp->ld_kpe = d->ld_kpe;
+    vp->B = d->B;
+    vp->H = d->H;
+    vp->N = d->N;
+    vp->W = (d->N + 63) / 64;
+    vp->rows = d->H * d->N;
+    vp->row_tiles = pl->row_tiles;
+    vp->chunk = pl->chunk;
+    vp->total_wg = pl->total_wg;
+    vp->n_attn = pl->total_wg;
+    vp->scale_log2 = d->scale * kLog2e;
+    return DDT_OK;
+}
+
+int run(const ddt_attn_desc* d, const VerifyParams& vp, const Plan& pl, int n_argmax, hipStream_t stream) {
+    if (d->dtype == DDT_BF16) return launch<uint16_t, 512, 64>(vp, pl, n_argmax, stream);
+    return launch<float, 64, 16>(vp, pl, n_argmax, stream);
 }
 
 }  // namespace
@@ -951,41 +1174,61 @@ extern "C" int ddt_verify_attn(const ddt_attn_desc* d, const void* q_lat, const 
                                const void* kpe, const int64_t* kv_base, const int32_t* prefix_len_host,
                                const uint64_t* mask, void* out, float* lse, void* workspace,
                                size_t workspace_bytes, hipStream_t stream) {
-    int rc = check_desc(d, prefix_len_host);
-    if (rc != DDT_OK) return rc;
-    if (!q_lat || !q_pe || !ckv || !kpe || !kv_base || !mask || !out || !lse) return DDT_EINVAL;
-    if (!ddt::aligned(q_lat, 16) || !ddt::aligned(q_pe, 16) || !ddt::aligned(ckv, 16) || !ddt::aligned(kpe, 16) ||
-        !ddt::aligned(out, 16) || !ddt::aligned(lse, 4))
-        return DDT_EINVAL;
     VerifyParams vp{};
-    const Plan pl = make_plan(d, prefix_len_host, &vp);
-    if (pl.ws_bytes > 0) {
-        if (workspace == nullptr || workspace_bytes < pl.ws_bytes || !ddt::aligned(workspace, 256))
-            return DDT_EWORKSPACE;
-        vp.ws_o = workspace;
-        vp.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.ws_lse_off);
+    Plan pl;
+    const int rc = setup_attn(d, q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, out, lse, workspace,
+                              workspace_bytes, &vp, &pl);
+    if (rc != DDT_OK) return rc;
+    return run(d, vp, pl, 0, stream);
+}
+
+extern "C" int ddt_verify_attn_argmax(const ddt_attn_desc* d, const void* q_lat, const void* q_pe, const void* ckv,
+                                      const void* kpe, const int64_t* kv_base, const int32_t* prefix_len_host,
+                                      const uint64_t* mask, void* out, float* lse, void* workspace,
+                                      size_t workspace_bytes, const ddt_argmax_task* am, hipStream_t stream) {
+    VerifyParams vp{};
+    Plan pl;
+    int rc = setup_attn(d, q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, out, lse, workspace,
+                        workspace_bytes, &vp, &pl);
+    if (rc != DDT_OK) return rc;
+    if (am == nullptr) return DDT_EINVAL;
+    // the argmax task: checks as in ddt_argmax
+    if (am->rows < 0 || am->V < 1 || am->V > 0x7fffffff || am->ld < am->V) return DDT_EINVAL;
+    if (am->dtype != DDT_F32 && am->dtype != DDT_BF16) return DDT_EUNSUPPORTED;
+    if (am->rows == 0) return run(d, vp, pl, 0, stream);
+    if (am->logits == nullptr || am->idx == nullptr || am->rows > 0x7fffffff / 64) return DDT_EINVAL;
+    size_t need = 0;
+    ddt_argmax_workspace(am->rows, am->V, &need);
+    if (need > 0 && (am->workspace == nullptr || am->workspace_bytes < need || !ddt::aligned(am->workspace, 16)))
+        return DDT_EWORKSPACE;
+    // one argmax workgroup per CU the attention leaves idle (at least half
+    // the CUs' worth when it fills the GPU), each taking an equal share of
+    // the flattened rows x V range; rows are shared between workgroups only
+    // where the workspace can merge them
+    const int cus = num_cus();
+    int64_t wgs = pl.total_wg < cus ? cus - pl.total_wg : cus / 2;
+    if (wgs < 1) wgs = 1;
+    const int64_t es = ddt::elem_bytes(am->dtype);
+    const int64_t vec_elems = 16 / es;
+    const int64_t total = am->rows * am->V;
+    int64_t E;
+    if (need > 0) {
+        E = (int64_t)ddt::round_up((size_t)((total + wgs - 1) / wgs), (size_t)ddt::kChunkAlign);
+    } else {
+        // rows may not be split: whole rows per workgroup
+        const int64_t rpw = (am->rows + wgs - 1) / wgs;
+        E = rpw * am->V;
     }
-    vp.q_lat = q_lat;
-    vp.q_pe = q_pe;
-    vp.ckv = ckv;
-    vp.kpe = kpe;
-    vp.kv_base = kv_base;
-    vp.mask = mask;
-    vp.out = out;
-    vp.lse = lse;
-    vp.ld_ql = d->ld_ql;
-    vp.ld_qp = d->ld_qp;
-    vp.ld_ckv = d->ld_ckv;
-    vp.ld_kpe = d->ld_kpe;
-    vp.B = d->B;
-    vp.H = d->H;
-    vp.N = d->N;
-    vp.W = (d->N + 63) / 64;
-    vp.rows = d->H * d->N;
-    vp.row_tiles = pl.row_tiles;
-    vp.chunk = pl.chunk;
-    vp.total_wg = pl.total_wg;
-    vp.scale_log2 = d->scale * kLog2e;
-    if (d->dtype == DDT_BF16) return launch<uint16_t, 512, 64>(vp, pl, stream);
-    return launch<float, 64, 16>(vp, pl, stream);
+    wgs = (total + E - 1) / E;
+    vp.am_wgs = (int)wgs;
+    vp.am_dtype = am->dtype;
+    vp.am_vec = ddt::aligned(am->logits, 16) && (am->ld * es) % 16 == 0 && am->V % vec_elems == 0;
+    vp.am_rows = am->rows;
+    vp.am_V = am->V;
+    vp.am_ld = am->ld;
+    vp.am_E = E;
+    vp.am_logits = am->logits;
+    vp.am_idx = am->idx;
+    vp.am_slots = static_cast<ddt::RowSlot*>(am->workspace);
+    return run(d, vp, pl, (int)wgs, stream);
 }

@@ -36,6 +36,12 @@ class AttnDesc(ctypes.Structure):
                 ("ld_ckv", ctypes.c_int64), ("ld_kpe", ctypes.c_int64)]
 
 
+class ArgmaxTask(ctypes.Structure):
+    _fields_ = [("logits", ctypes.c_void_p), ("dtype", ctypes.c_int), ("rows", ctypes.c_int64),
+                ("V", ctypes.c_int64), ("ld", ctypes.c_int64), ("idx", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
 def lib():
     global _lib
     if _lib is None:
@@ -54,9 +60,11 @@ def lib():
         L.ddt_greedy_accept.argtypes = [P, P, P, i32, i32, P, P, P, P]
         L.ddt_compact_kv.argtypes = [P, i64, P, i64, i32, i32, i32, P, P, P, P, i32, i32, P, P]
         L.ddt_accept_compact.argtypes = [P, P, P, i32, i32, P, P, P, P, i64, P, i64, i32, i32, i32, P, P, P, P]
+        L.ddt_verify_attn_argmax.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P, P, P, P, sz,
+                                             ctypes.POINTER(ArgmaxTask), P]
         for f in ("ddt_version", "ddt_build_mask", "ddt_verify_workspace", "ddt_verify_attn",
                   "ddt_argmax_workspace", "ddt_argmax", "ddt_greedy_accept", "ddt_compact_kv",
-                  "ddt_accept_compact"):
+                  "ddt_accept_compact", "ddt_verify_attn_argmax"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -136,12 +144,7 @@ def verify_workspace_bytes(desc: AttnDesc, prefix_len_host) -> int:
     return n.value
 
 
-def verify_attn(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, *, H, scale, out=None, lse=None,
-                workspace=None, kv_chunk=0, stream=None):
-    """Tree-verify attention.  q_lat [B*N*H, d_lat], q_pe [B*N*H, d_rope] (2-D views),
-    ckv [pool, d_lat], kpe [pool, d_rope] (2-D views of the cache pool), kv_base [B]
-    int64 (device), prefix_len_host [B] (host), mask [B, N, W] from build_mask.
-    Returns (out [B*N*H, d_lat], lse [B*N*H] fp32)."""
+def _attn_args(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, H, scale, out, lse, workspace, kv_chunk):
     for t, n in ((q_lat, "q_lat"), (q_pe, "q_pe"), (ckv, "ckv"), (kpe, "kpe")):
         _dev(t, q_lat.dtype, n)
     _contig(kv_base, torch.int64, "kv_base")
@@ -164,10 +167,43 @@ def verify_attn(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, *, H, sca
     if workspace is None and need > 0:
         workspace = torch.empty((need,), dtype=torch.uint8, device=q_lat.device)
     ws_n = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return desc, pl, out, lse, workspace, ws_n
+
+
+def verify_attn(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, *, H, scale, out=None, lse=None,
+                workspace=None, kv_chunk=0, stream=None):
+    """Tree-verify attention.  q_lat [B*N*H, d_lat], q_pe [B*N*H, d_rope] (2-D views),
+    ckv [pool, d_lat], kpe [pool, d_rope] (2-D views of the cache pool), kv_base [B]
+    int64 (device), prefix_len_host [B] (host), mask [B, N, W] from build_mask.
+    Returns (out [B*N*H, d_lat], lse [B*N*H] fp32)."""
+    desc, pl, out, lse, workspace, ws_n = _attn_args(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, H,
+                                                     scale, out, lse, workspace, kv_chunk)
     _check(lib().ddt_verify_attn(ctypes.byref(desc), _p(q_lat), _p(q_pe), _p(ckv), _p(kpe), _p(kv_base),
                                  pl.ctypes.data, _p(mask), _p(out), _p(lse), _p(workspace), ws_n,
                                  _stream(stream)), "ddt_verify_attn")
     return out, lse
+
+
+def verify_attn_argmax(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, logits, *, H, scale, out=None,
+                       lse=None, workspace=None, idx=None, argmax_workspace=None, kv_chunk=0, stream=None):
+    """verify_attn and argmax(logits) in one launch -> (out, lse, idx)."""
+    desc, pl, out, lse, workspace, ws_n = _attn_args(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, H,
+                                                     scale, out, lse, workspace, kv_chunk)
+    _dev(logits, None, "logits")
+    ld = _rows(logits, "logits")
+    rows, V = logits.shape
+    if idx is None:
+        idx = torch.empty((rows,), dtype=torch.int32, device=logits.device)
+    _contig(idx, torch.int32, "idx")
+    need = argmax_workspace_bytes(rows, V)
+    if argmax_workspace is None and need > 0:
+        argmax_workspace = torch.zeros((need,), dtype=torch.uint8, device=logits.device)  # zero before first use
+    am_n = 0 if argmax_workspace is None else argmax_workspace.numel() * argmax_workspace.element_size()
+    task = ArgmaxTask(_p(logits), _dtype_code(logits), rows, V, ld, _p(idx), _p(argmax_workspace), am_n)
+    _check(lib().ddt_verify_attn_argmax(ctypes.byref(desc), _p(q_lat), _p(q_pe), _p(ckv), _p(kpe), _p(kv_base),
+                                        pl.ctypes.data, _p(mask), _p(out), _p(lse), _p(workspace), ws_n,
+                                        ctypes.byref(task), _stream(stream)), "ddt_verify_attn_argmax")
+    return out, lse, idx
 
 
 def argmax_workspace_bytes(rows: int, V: int) -> int:

@@ -107,6 +107,10 @@ def test_argmax(orc, rows, V, dtype):
         x[3, [V // 3, V - 1]] = np.nan              # first NaN wins
         x[4, :] = -1.0
         x[4, [5, 9]] = [-0.0, 0.0]                  # -0 == +0 -> index 5
+    if V > 200 and rows > 6:
+        x[5, :] = -np.inf                           # all -inf -> index 0
+        x[6, :] = 0.0
+        x[6, 150] = 1e-39                           # a positive denormal is the maximum
     if dtype == "bf16":
         x = synth.to_bf16_bits(np.nan_to_num(x, nan=0.0))
         x[2 % rows, V // 2] = synth.BF16_NAN
@@ -231,6 +235,50 @@ def _attn_check(orc, w, kv_chunks=(0,), rows=None):
         assert e_out <= tol and e_lse <= tol, (ch, e_out, e_lse)
         results.append(o)
     return results
+
+
+@pytest.mark.parametrize("cfg,over,logit_shape,ldt,kv_chunk", [
+    (2, dict(), (64, 163840), "f32", 0),                       # the K2-like head share, split keys
+    (2, dict(), (64, 163840), "bf16", 1 << 20),                # one split per request
+    (1, dict(), (2100, 4099), "f32", 0),                       # fp32 attention; argmax rows unchunked
+    (3, dict(B=3, prefix_range=(100, 3000)), (96, 50001), "bf16", 224),
+    (2, dict(), (9, 40000), "f32", 0),                         # streamed rows: NaN, -inf, signed zeros
+    (2, dict(), (9, 70016), "bf16", 0),
+])
+def test_attn_argmax_fused(orc, cfg, over, logit_shape, ldt, kv_chunk):
+    """verify_attn_argmax == verify_attn (against the oracle) and argmax
+    (against the oracle) from one launch; the argmax workspace is reused."""
+    w = synth.workload(cfg, with_logits=False, **over) if cfg == 2 else synth.workload(cfg, **over)
+    dw = DevWorkload(w)
+    rng = np.random.default_rng(sum(logit_shape))
+    x = rng.standard_normal(logit_shape).astype(np.float32)
+    x[np.arange(logit_shape[0]), rng.integers(0, logit_shape[1], logit_shape[0])] += 8.0
+    x[0, [5, logit_shape[1] - 3]] = 50.0                        # tie -> lower index
+    if logit_shape[0] == 9:
+        V = logit_shape[1]
+        x[1] = -np.inf                                          # every value -inf: index 0
+        x[2, [100, V // 2]] = [99.0, np.nan]                    # NaN above every number
+        x[3] = -1.0
+        x[3, [V // 3, V // 3 + 1, V - 7]] = [-0.0, 0.0, 0.0]    # -0 == +0: the first zero
+        x[4, V - 1] = 1e30                                      # last element of the row
+        x[5, 7] = np.inf
+        x[6, [V - 5, V - 2]] = [np.nan, np.nan]                 # NaN in a row's final stage
+    if ldt == "bf16":
+        x = synth.to_bf16_bits(x)
+    logits = to_dev(x)
+    mask, _, _ = ddt.build_mask(dw.parents)
+    ref_out, ref_lse = oracle_attn(orc, w)
+    ref_idx = orc.argmax(x)
+    ws = torch.zeros((max(ddt.argmax_workspace_bytes(*logit_shape), 16),), dtype=torch.uint8, device="cuda")
+    for rep in range(2):
+        out, lse, idx = ddt.verify_attn_argmax(dw.q_lat(), dw.q_pe(), dw.ckv(), dw.kpe(), dw.kv_base, w.prefix_len,
+                                               mask, logits, H=w.H, scale=w.scale, kv_chunk=kv_chunk,
+                                               argmax_workspace=ws)
+        assert (to_host(idx) == ref_idx).all(), rep
+        o = as_f64(to_host(out))
+        e_out, e_lse = rel_l2(o, ref_out), rel_l2(to_host(lse), ref_lse)
+        assert e_out <= ATTN_TOL[w.dtype] and e_lse <= ATTN_TOL[w.dtype], (rep, e_out, e_lse)
+    assert int(ws.sum().item()) == 0
 
 
 def test_attn_config1_tiny_fp32(orc):
