@@ -120,8 +120,10 @@ def main():
     pool, q = to_dev(w.pool), to_dev(w.q)
     parents, draft = to_dev(w.parents), to_dev(w.draft_ids)
     kv_base = to_dev(w.kv_base)
+    # committed lengths: every step reads these and writes the advanced
+    # lengths to new_prefix, so each step verifies the same tree
     prefix0 = to_dev(w.prefix_len)
-    prefix = prefix0.clone()
+    new_prefix = torch.empty_like(prefix0)
     logits = None if w.logits is None else to_dev(w.logits)
     target = None if w.target_ids is None else to_dev(w.target_ids)
     dl = w.d_lat
@@ -155,19 +157,18 @@ def main():
                         workspace=ws)
 
     def step():
-        prefix.copy_(prefix0)                      # same committed length every step
         ddt.build_mask(parents, mask, depth, terr)
         if logits is not None:
-            # attention and the (independent) target argmax in one launch:
-            # the argmax workgroups take the CUs the attention leaves idle
-            ddt.verify_attn_argmax(q_lat, q_pe, ckv, kpe, kv_base, P_host, mask, logits, H=H, scale=w.scale,
-                                   out=out, lse=lse, workspace=ws, idx=tids, argmax_workspace=am_ws)
-            t = tids.view(B, N)
+            # two launches: the attention with the (independent) target argmax
+            # on the CUs it leaves idle, then the split merge with acceptance +
+            # compaction + length update beside it
+            ddt.verify_step(q_lat, q_pe, ckv, kpe, kv_base, P_host, mask, logits, draft, parents, prefix0, H=H,
+                            scale=w.scale, new_prefix_len=new_prefix, out=out, lse=lse, workspace=ws, idx=tids,
+                            argmax_workspace=am_ws, accept_len=acc, path=path, tokens=tok)
         else:
             attn()
-            t = target
-        # acceptance + compaction (and the length update) in one launch
-        ddt.accept_compact(t, draft, parents, ckv, kpe, kv_base, prefix, acc, path, tok)
+            ddt.accept_compact(target, draft, parents, ckv, kpe, kv_base, prefix0, acc, path, tok,
+                               new_prefix_len=new_prefix)
 
     if args.traffic_probe:
         ddt.build_mask(parents, mask, depth, terr)

@@ -219,14 +219,48 @@ int ddt_compact_kv(void* ckv, int64_t ld_ckv, void* kpe, int64_t ld_kpe, int dty
  * Preceded the Header" and "Mistakes and Iterative Refinement".  The same
  * results as ddt_greedy_accept followed by ddt_compact_kv on the path it
  * found: one workgroup per request walks the tree, writes accept_len, path
- * and tokens, then moves the accepted rows and advances prefix_len.
- * Arguments, layouts and errors as for those two calls (the walk's path is
- * always a valid compaction path).
+ * and tokens, then moves the accepted rows.  The committed lengths are read
+ * from prefix_len and the advanced ones written to new_prefix_len (device
+ * arrays of B; the same array for an in-place update).  Other arguments,
+ * layouts and errors as for those two calls (the walk's path is always a
+ * valid compaction path).
  */
 int ddt_accept_compact(const int32_t* target_ids, const int32_t* draft_ids, const int32_t* parents, int B, int N,
                        int32_t* accept_len, int32_t* path, int32_t* tokens, void* ckv, int64_t ld_ckv, void* kpe,
-                       int64_t ld_kpe, int dtype, int d_lat, int d_rope, const int64_t* kv_base, int32_t* prefix_len,
-                       int32_t* src_slot, hipStream_t stream);
+                       int64_t ld_kpe, int dtype, int d_lat, int d_rope, const int64_t* kv_base,
+                       const int32_t* prefix_len, int32_t* new_prefix_len, int32_t* src_slot, hipStream_t stream);
+
+/*
+ * One verify step after the mask: tree-verify attention, target argmax,
+ * greedy acceptance and KV compaction with the length update, in two
+ * launches.  [Ambition], sections "The Thinking Process", "The Decision
+ * Architecture" and "The Knowledge Architecture"; [Keystone], sections
+ * "What the Header Declares" and "The Reasoning That Preceded the Header".
+ * Results are those of
+ * ddt_verify_attn_argmax followed by ddt_accept_compact with
+ * target_ids = am->idx and the attention's cache (ckv, kpe, kv_base, dtype,
+ * d_lat, d_rope, strides).  The first launch runs the attention with the
+ * argmax on idle CUs; the second runs the split merge with one
+ * acceptance + compaction workgroup per request beside it (the compaction
+ * writes the cache only after the attention has read it).
+ * am->rows must be B*N (one target row per tree node, request-major).
+ * acc->prefix_len (device) must hold the same lengths as prefix_len_host.
+ * Errors as for the calls it replaces.
+ */
+typedef struct {
+    const int32_t* draft_ids;   /* [B][N] device                               */
+    const int32_t* parents;     /* [B][N] device                               */
+    int32_t* accept_len;        /* [B] out                                     */
+    int32_t* path;              /* [B][N] out                                  */
+    int32_t* tokens;            /* [B][N] out                                  */
+    const int32_t* prefix_len;  /* [B] device, committed lengths               */
+    int32_t* new_prefix_len;    /* [B] out, advanced lengths (may be prefix_len) */
+    int32_t* src_slot;          /* [B][N] out, or NULL                         */
+} ddt_accept_task;
+int ddt_verify_step(const ddt_attn_desc* d, const void* q_lat, const void* q_pe, void* ckv, void* kpe,
+                    const int64_t* kv_base, const int32_t* prefix_len_host, const uint64_t* mask, void* out,
+                    float* lse, void* workspace, size_t workspace_bytes, const ddt_argmax_task* am,
+                    const ddt_accept_task* acc, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -8,7 +8,7 @@
 // P+path[j]; the path starts at 0 and increases, so path[j] >= j and the
 // block-wise LDS-staged copy of ddt::copy_path_rows (tree_tail.h) is race
 // free with no global scratch.  ddt_accept_compact runs acceptance and
-// compaction of a request in one workgroup.
+// compaction of a request in one workgroup (ddt::accept_compact_body).
 #include "common.h"
 #include "tree_tail.h"
 
@@ -48,46 +48,11 @@ __global__ __launch_bounds__(ddt::kCompactThreads) void compact_kernel(
     if (threadIdx.x == 0) prefix_len[b] = (int32_t)(P + k + 1);
 }
 
-// Acceptance and compaction of one request in one workgroup: wavefront 0
-// walks the tree (LDS), all threads then move the accepted rows.  The walk
-// only moves to higher node numbers, so its path is always a valid
-// compaction path.
+// Acceptance and compaction of one request per workgroup.
 template <typename U>
-__global__ __launch_bounds__(ddt::kCompactThreads) void accept_compact_kernel(
-    const int32_t* __restrict__ target, const int32_t* __restrict__ draft, const int32_t* __restrict__ parents,
-    int N, int32_t* __restrict__ accept_len, int32_t* __restrict__ path, int32_t* __restrict__ tokens,
-    char* __restrict__ ckv, int64_t ld_ckv, char* __restrict__ kpe, int64_t ld_kpe, int ckv_units, int kpe_units,
-    const int64_t* __restrict__ kv_base, int32_t* __restrict__ prefix_len, int32_t* __restrict__ src_slot,
-    int rows_per_block) {
+__global__ __launch_bounds__(ddt::kCompactThreads) void accept_compact_kernel(const ddt::AcceptCompactArgs a) {
     extern __shared__ uint4 stage_raw[];
-    __shared__ int32_t spar[DDT_MAX_NODES];
-    __shared__ int32_t sdraft[DDT_MAX_NODES];
-    __shared__ int32_t spath[DDT_MAX_NODES];
-    __shared__ int s_n;
-    const int b = blockIdx.x;
-    const int64_t off = (int64_t)b * N;
-    for (int i = threadIdx.x; i < N; i += blockDim.x) {
-        spar[i] = parents[off + i];
-        sdraft[i] = draft[off + i];
-    }
-    __syncthreads();
-    if (threadIdx.x < ddt::kWave) {
-        const int lane = threadIdx.x;
-        const int n = ddt::greedy_walk(target, off, spar, sdraft, N, spath, lane);
-        if (lane == 0) s_n = n;
-    }
-    __syncthreads();
-    const int n = s_n, k = n - 1;
-    if (threadIdx.x < ddt::kWave)
-        ddt::write_accept(target, off, sdraft, spath, n, N, b, threadIdx.x, accept_len, path, tokens);
-    const int64_t P = prefix_len[b];
-    const int64_t base = kv_base[b];
-    if (src_slot != nullptr) {
-        for (int j = threadIdx.x; j < N; j += blockDim.x) src_slot[off + j] = j <= k ? (int32_t)(P + spath[j]) : -1;
-    }
-    ddt::copy_path_rows<U>(ckv, ld_ckv, kpe, ld_kpe, ckv_units, kpe_units, base, P, k, rows_per_block,
-                           reinterpret_cast<U*>(stage_raw), [&](int j) { return spath[j]; });
-    if (threadIdx.x == 0) prefix_len[b] = (int32_t)(P + k + 1);
+    ddt::accept_compact_body<U>(a, blockIdx.x, reinterpret_cast<U*>(stage_raw));
 }
 
 }  // namespace
@@ -119,28 +84,27 @@ extern "C" int ddt_compact_kv(void* ckv, int64_t ld_ckv, void* kpe, int64_t ld_k
 extern "C" int ddt_accept_compact(const int32_t* target_ids, const int32_t* draft_ids, const int32_t* parents,
                                   int B, int N, int32_t* accept_len, int32_t* path, int32_t* tokens, void* ckv,
                                   int64_t ld_ckv, void* kpe, int64_t ld_kpe, int dtype, int d_lat, int d_rope,
-                                  const int64_t* kv_base, int32_t* prefix_len, int32_t* src_slot,
-                                  hipStream_t stream) {
+                                  const int64_t* kv_base, const int32_t* prefix_len, int32_t* new_prefix_len,
+                                  int32_t* src_slot, hipStream_t stream) {
     if (B < 0 || N < 1 || N > DDT_MAX_NODES || d_lat < 1 || d_rope < 0) return DDT_EINVAL;
     if (dtype != DDT_F32 && dtype != DDT_BF16) return DDT_EUNSUPPORTED;
     if (B == 0) return DDT_OK;
     if (!target_ids || !draft_ids || !parents || !accept_len || !path || !tokens) return DDT_EINVAL;
-    if (!ckv || !kv_base || !prefix_len) return DDT_EINVAL;
+    if (!ckv || !kv_base || !prefix_len || !new_prefix_len) return DDT_EINVAL;
     if (d_rope > 0 && !kpe) return DDT_EINVAL;
     if (d_rope == 0) kpe = ckv;
     ddt::CompactLayout lay;
     const int rc = ddt::compact_layout(ckv, ld_ckv, kpe, ld_kpe, dtype, d_lat, d_rope, N, &lay);
     if (rc != DDT_OK) return rc;
+    ddt::AcceptCompactArgs a{target_ids, draft_ids, parents, N, accept_len, path, tokens, (char*)ckv, (char*)kpe,
+                             lay.lc, lay.lk, lay.ckv_units, lay.kpe_units, lay.rows_per_block, kv_base,
+                             prefix_len, new_prefix_len, src_slot};
     if (lay.vec16)
         hipLaunchKernelGGL(accept_compact_kernel<uint4>, dim3(B), dim3(ddt::kCompactThreads), lay.stage_bytes,
-                           stream, target_ids, draft_ids, parents, N, accept_len, path, tokens, (char*)ckv, lay.lc,
-                           (char*)kpe, lay.lk, lay.ckv_units, lay.kpe_units, kv_base, prefix_len, src_slot,
-                           lay.rows_per_block);
+                           stream, a);
     else
         hipLaunchKernelGGL(accept_compact_kernel<uint32_t>, dim3(B), dim3(ddt::kCompactThreads), lay.stage_bytes,
-                           stream, target_ids, draft_ids, parents, N, accept_len, path, tokens, (char*)ckv, lay.lc,
-                           (char*)kpe, lay.lk, lay.ckv_units, lay.kpe_units, kv_base, prefix_len, src_slot,
-                           lay.rows_per_block);
+                           stream, a);
     DDT_CHECK_LAUNCH();
     return DDT_OK;
 }

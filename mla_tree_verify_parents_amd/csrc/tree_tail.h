@@ -101,6 +101,63 @@ __device__ inline void copy_path_rows(char* __restrict__ ckv, int64_t ld_ckv, ch
     }
 }
 
+// Arguments of acceptance + compaction for every request of a batch (row
+// strides in bytes; copy units as in CompactLayout).
+struct AcceptCompactArgs {
+    const int32_t* target;   // [B*N] target ids (argmax of the target logits)
+    const int32_t* draft;    // [B*N] draft ids
+    const int32_t* parents;  // [B*N]
+    int N;
+    int32_t* accept_len;  // [B]
+    int32_t* path;        // [B*N]
+    int32_t* tokens;      // [B*N]
+    char* ckv;
+    char* kpe;
+    int64_t ld_ckv, ld_kpe;
+    int ckv_units, kpe_units, rows_per_block;
+    const int64_t* kv_base;
+    const int32_t* prefix_len;  // [B] committed lengths
+    int32_t* new_prefix_len;    // [B] may be prefix_len itself
+    int32_t* src_slot;          // [B*N] or null
+};
+
+// Acceptance and compaction of request b by one workgroup: wavefront 0
+// walks the tree (LDS), all threads then move the accepted rows through
+// `stage` (rows_per_block rows).  The walk only moves to higher node
+// numbers, so its path is always a valid compaction path.  Every thread
+// reads the committed length before thread 0 writes the new one, so
+// new_prefix_len may alias prefix_len.
+template <typename U>
+__device__ void accept_compact_body(const AcceptCompactArgs& a, int b, U* stage) {
+    __shared__ int32_t spar[DDT_MAX_NODES];
+    __shared__ int32_t sdraft[DDT_MAX_NODES];
+    __shared__ int32_t spath[DDT_MAX_NODES];
+    __shared__ int s_n;
+    const int N = a.N;
+    const int64_t off = (int64_t)b * N;
+    for (int i = threadIdx.x; i < N; i += blockDim.x) {
+        spar[i] = a.parents[off + i];
+        sdraft[i] = a.draft[off + i];
+    }
+    __syncthreads();
+    if (threadIdx.x < kWave) {
+        const int n = greedy_walk(a.target, off, spar, sdraft, N, spath, threadIdx.x);
+        if (threadIdx.x == 0) s_n = n;
+    }
+    __syncthreads();
+    const int n = s_n, k = n - 1;
+    if (threadIdx.x < kWave)
+        write_accept(a.target, off, sdraft, spath, n, N, b, threadIdx.x, a.accept_len, a.path, a.tokens);
+    const int64_t P = a.prefix_len[b];
+    const int64_t base = a.kv_base[b];
+    if (a.src_slot != nullptr) {
+        for (int j = threadIdx.x; j < N; j += blockDim.x) a.src_slot[off + j] = j <= k ? (int32_t)(P + spath[j]) : -1;
+    }
+    copy_path_rows<U>(a.ckv, a.ld_ckv, a.kpe, a.ld_kpe, a.ckv_units, a.kpe_units, base, P, k, a.rows_per_block, stage,
+                      [&](int j) { return spath[j]; });  // (ends with a barrier: every thread has read P)
+    if (threadIdx.x == 0) a.new_prefix_len[b] = (int32_t)(P + k + 1);
+}
+
 // Copy granularity and LDS staging of a compaction, chosen on the host.
 struct CompactLayout {
     int64_t lc, lk;           // row strides in bytes

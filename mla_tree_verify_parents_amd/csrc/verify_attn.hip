@@ -45,6 +45,7 @@
 
 #include "argmax_scan.h"
 #include "common.h"
+#include "tree_tail.h"
 
 namespace {
 
@@ -348,6 +349,9 @@ struct VerifyParams {
     const void* am_logits;
     int32_t* am_idx;
     ddt::RowSlot* am_slots;
+    // acceptance + compaction riding along in the merge launch (workgroups 0 .. n_accept-1)
+    int n_accept, acc_vec16;
+    ddt::AcceptCompactArgs acc;
 };
 
 // Argmax workgroup `am_id` scans elements [am_id*E, (am_id+1)*E) of the
@@ -961,14 +965,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 // One workgroup per (request, row tile, wavefront, 32-column tile of that
 // wavefront); thread (grp, lane) owns the 4 consecutive outputs that the
 // split kernel's lane `lane` stored at group `grp`.
-template <typename T, int DL>
+template <typename T, int DL, bool kAccept>
 __global__ __launch_bounds__(256) void verify_combine(const VerifyParams p) {
+    static_assert(ddt::kCompactThreads == 256, "acceptance workgroups share the merge's block size");
+    if (kAccept && (int)blockIdx.x < p.n_accept) {
+        // acceptance + compaction of request blockIdx.x: the attention that
+        // reads the cache rows it moves has finished (previous launch)
+        __shared__ uint4 stage[ddt::kCompactStageBytes / 16];
+        if (p.acc_vec16)
+            ddt::accept_compact_body<uint4>(p.acc, blockIdx.x, stage);
+        else
+            ddt::accept_compact_body<uint32_t>(p.acc, blockIdx.x, reinterpret_cast<uint32_t*>(stage));
+        return;
+    }
+    const int bid = kAccept ? (int)blockIdx.x - p.n_accept : (int)blockIdx.x;
     constexpr int NCTW = DL / 64;
     const int per_b = p.row_tiles * NW * NCTW;
-    const int b = blockIdx.x / per_b;
+    const int b = bid / per_b;
     const int ns = p.nsplit[b];
     if (ns <= 1) return;
-    int rem = blockIdx.x - b * per_b;
+    int rem = bid - b * per_b;
     const int rt = rem / (NW * NCTW);
     rem -= rt * (NW * NCTW);
     const int wave = rem / NCTW, c = rem - (rem / NCTW) * NCTW;
@@ -1105,9 +1121,12 @@ int launch(const VerifyParams& vp, const Plan& pl, int n_argmax, hipStream_t str
     else
         hipLaunchKernelGGL((verify_split<T, DL, DR, false>), dim3(pl.total_wg), dim3(kThreads), 0, stream, vp);
     DDT_CHECK_LAUNCH();
-    if (pl.any_split) {
-        const int nblk = vp.B * pl.row_tiles * NW * (DL / 64);
-        hipLaunchKernelGGL((verify_combine<T, DL>), dim3(nblk), dim3(256), 0, stream, vp);
+    const int nblk = pl.any_split ? vp.B * pl.row_tiles * NW * (DL / 64) : 0;
+    if (vp.n_accept > 0) {
+        hipLaunchKernelGGL((verify_combine<T, DL, true>), dim3(vp.n_accept + nblk), dim3(256), 0, stream, vp);
+        DDT_CHECK_LAUNCH();
+    } else if (nblk > 0) {
+        hipLaunchKernelGGL((verify_combine<T, DL, false>), dim3(nblk), dim3(256), 0, stream, vp);
         DDT_CHECK_LAUNCH();
     }
     return DDT_OK;
@@ -1160,6 +1179,53 @@ int run(const ddt_attn_desc* d, const VerifyParams& vp, const Plan& pl, int n_ar
     return launch<float, 64, 16>(vp, pl, n_argmax, stream);
 }
 
+// Validates the argmax task (as ddt_argmax does) and fills its part of the
+// launch parameters; *wgs receives the number of argmax workgroups (0 for
+// an empty task).
+int setup_argmax(const ddt_argmax_task* am, const Plan& pl, VerifyParams* vp, int* n_wgs) {
+    *n_wgs = 0;
+    if (am == nullptr) return DDT_EINVAL;
+    if (am->rows < 0 || am->V < 1 || am->V > 0x7fffffff || am->ld < am->V) return DDT_EINVAL;
+    if (am->dtype != DDT_F32 && am->dtype != DDT_BF16) return DDT_EUNSUPPORTED;
+    if (am->rows == 0) return DDT_OK;
+    if (am->logits == nullptr || am->idx == nullptr || am->rows > 0x7fffffff / 64) return DDT_EINVAL;
+    size_t need = 0;
+    ddt_argmax_workspace(am->rows, am->V, &need);
+    if (need > 0 && (am->workspace == nullptr || am->workspace_bytes < need || !ddt::aligned(am->workspace, 16)))
+        return DDT_EWORKSPACE;
+    // one argmax workgroup per CU the attention leaves idle (at least half
+    // the CUs' worth when it fills the GPU), each taking an equal share of
+    // the flattened rows x V range; rows are shared between workgroups only
+    // where the workspace can merge them
+    const int cus = num_cus();
+    int64_t wgs = pl.total_wg < cus ? cus - pl.total_wg : cus / 2;
+    if (wgs < 1) wgs = 1;
+    const int64_t es = ddt::elem_bytes(am->dtype);
+    const int64_t vec_elems = 16 / es;
+    const int64_t total = am->rows * am->V;
+    int64_t E;
+    if (need > 0) {
+        E = (int64_t)ddt::round_up((size_t)((total + wgs - 1) / wgs), (size_t)ddt::kChunkAlign);
+    } else {
+        // rows may not be split: whole rows per workgroup
+        const int64_t rpw = (am->rows + wgs - 1) / wgs;
+        E = rpw * am->V;
+    }
+    wgs = (total + E - 1) / E;
+    vp->am_wgs = (int)wgs;
+    vp->am_dtype = am->dtype;
+    vp->am_vec = ddt::aligned(am->logits, 16) && (am->ld * es) % 16 == 0 && am->V % vec_elems == 0;
+    vp->am_rows = am->rows;
+    vp->am_V = am->V;
+    vp->am_ld = am->ld;
+    vp->am_E = E;
+    vp->am_logits = am->logits;
+    vp->am_idx = am->idx;
+    vp->am_slots = static_cast<ddt::RowSlot*>(am->workspace);
+    *n_wgs = (int)wgs;
+    return DDT_OK;
+}
+
 }  // namespace
 
 extern "C" int ddt_verify_workspace(const ddt_attn_desc* d, const int32_t* prefix_len_host, size_t* bytes) {
@@ -1191,44 +1257,37 @@ extern "C" int ddt_verify_attn_argmax(const ddt_attn_desc* d, const void* q_lat,
     int rc = setup_attn(d, q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, out, lse, workspace,
                         workspace_bytes, &vp, &pl);
     if (rc != DDT_OK) return rc;
-    if (am == nullptr) return DDT_EINVAL;
-    // the argmax task: checks as in ddt_argmax
-    if (am->rows < 0 || am->V < 1 || am->V > 0x7fffffff || am->ld < am->V) return DDT_EINVAL;
-    if (am->dtype != DDT_F32 && am->dtype != DDT_BF16) return DDT_EUNSUPPORTED;
-    if (am->rows == 0) return run(d, vp, pl, 0, stream);
-    if (am->logits == nullptr || am->idx == nullptr || am->rows > 0x7fffffff / 64) return DDT_EINVAL;
-    size_t need = 0;
-    ddt_argmax_workspace(am->rows, am->V, &need);
-    if (need > 0 && (am->workspace == nullptr || am->workspace_bytes < need || !ddt::aligned(am->workspace, 16)))
-        return DDT_EWORKSPACE;
-    // one argmax workgroup per CU the attention leaves idle (at least half
-    // the CUs' worth when it fills the GPU), each taking an equal share of
-    // the flattened rows x V range; rows are shared between workgroups only
-    // where the workspace can merge them
-    const int cus = num_cus();
-    int64_t wgs = pl.total_wg < cus ? cus - pl.total_wg : cus / 2;
-    if (wgs < 1) wgs = 1;
-    const int64_t es = ddt::elem_bytes(am->dtype);
-    const int64_t vec_elems = 16 / es;
-    const int64_t total = am->rows * am->V;
-    int64_t E;
-    if (need > 0) {
-        E = (int64_t)ddt::round_up((size_t)((total + wgs - 1) / wgs), (size_t)ddt::kChunkAlign);
-    } else {
-        // rows may not be split: whole rows per workgroup
-        const int64_t rpw = (am->rows + wgs - 1) / wgs;
-        E = rpw * am->V;
-    }
-    wgs = (total + E - 1) / E;
-    vp.am_wgs = (int)wgs;
-    vp.am_dtype = am->dtype;
-    vp.am_vec = ddt::aligned(am->logits, 16) && (am->ld * es) % 16 == 0 && am->V % vec_elems == 0;
-    vp.am_rows = am->rows;
-    vp.am_V = am->V;
-    vp.am_ld = am->ld;
-    vp.am_E = E;
-    vp.am_logits = am->logits;
-    vp.am_idx = am->idx;
-    vp.am_slots = static_cast<ddt::RowSlot*>(am->workspace);
-    return run(d, vp, pl, (int)wgs, stream);
+    int wgs = 0;
+    rc = setup_argmax(am, pl, &vp, &wgs);
+    if (rc != DDT_OK) return rc;
+    return run(d, vp, pl, wgs, stream);
+}
+
+extern "C" int ddt_verify_step(const ddt_attn_desc* d, const void* q_lat, const void* q_pe, void* ckv, void* kpe,
+                               const int64_t* kv_base, const int32_t* prefix_len_host, const uint64_t* mask,
+                               void* out, float* lse, void* workspace, size_t workspace_bytes,
+                               const ddt_argmax_task* am, const ddt_accept_task* acc, hipStream_t stream) {
+    VerifyParams vp{};
+    Plan pl;
+    int rc = setup_attn(d, q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, out, lse, workspace,
+                        workspace_bytes, &vp, &pl);
+    if (rc != DDT_OK) return rc;
+    if (am == nullptr || acc == nullptr) return DDT_EINVAL;
+    if (am->rows != (int64_t)d->B * d->N) return DDT_EINVAL;  // one target row per tree node
+    int wgs = 0;
+    rc = setup_argmax(am, pl, &vp, &wgs);
+    if (rc != DDT_OK) return rc;
+    if (!acc->draft_ids || !acc->parents || !acc->accept_len || !acc->path || !acc->tokens || !acc->prefix_len ||
+        !acc->new_prefix_len)
+        return DDT_EINVAL;
+    ddt::CompactLayout lay;
+    rc = ddt::compact_layout(ckv, d->ld_ckv, kpe, d->ld_kpe, d->dtype, d->d_lat, d->d_rope, d->N, &lay);
+    if (rc != DDT_OK) return rc;
+    vp.n_accept = d->B;
+    vp.acc_vec16 = lay.vec16 ? 1 : 0;
+    vp.acc = ddt::AcceptCompactArgs{am->idx, acc->draft_ids, acc->parents, d->N, acc->accept_len, acc->path,
+                                    acc->tokens, static_cast<char*>(ckv), static_cast<char*>(kpe), lay.lc, lay.lk,
+                                    lay.ckv_units, lay.kpe_units, lay.rows_per_block, kv_base, acc->prefix_len,
+                                    acc->new_prefix_len, acc->src_slot};
+    return run(d, vp, pl, wgs, stream);
 }

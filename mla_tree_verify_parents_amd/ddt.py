@@ -42,6 +42,12 @@ class ArgmaxTask(ctypes.Structure):
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
 
 
+class AcceptTask(ctypes.Structure):
+    _fields_ = [("draft_ids", ctypes.c_void_p), ("parents", ctypes.c_void_p), ("accept_len", ctypes.c_void_p),
+                ("path", ctypes.c_void_p), ("tokens", ctypes.c_void_p), ("prefix_len", ctypes.c_void_p),
+                ("new_prefix_len", ctypes.c_void_p), ("src_slot", ctypes.c_void_p)]
+
+
 def lib():
     global _lib
     if _lib is None:
@@ -59,12 +65,14 @@ def lib():
         L.ddt_argmax.argtypes = [P, i32, i64, i64, i64, P, P, sz, P]
         L.ddt_greedy_accept.argtypes = [P, P, P, i32, i32, P, P, P, P]
         L.ddt_compact_kv.argtypes = [P, i64, P, i64, i32, i32, i32, P, P, P, P, i32, i32, P, P]
-        L.ddt_accept_compact.argtypes = [P, P, P, i32, i32, P, P, P, P, i64, P, i64, i32, i32, i32, P, P, P, P]
+        L.ddt_accept_compact.argtypes = [P, P, P, i32, i32, P, P, P, P, i64, P, i64, i32, i32, i32, P, P, P, P, P]
         L.ddt_verify_attn_argmax.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P, P, P, P, sz,
                                              ctypes.POINTER(ArgmaxTask), P]
+        L.ddt_verify_step.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P, P, P, P, sz,
+                                      ctypes.POINTER(ArgmaxTask), ctypes.POINTER(AcceptTask), P]
         for f in ("ddt_version", "ddt_build_mask", "ddt_verify_workspace", "ddt_verify_attn",
                   "ddt_argmax_workspace", "ddt_argmax", "ddt_greedy_accept", "ddt_compact_kv",
-                  "ddt_accept_compact", "ddt_verify_attn_argmax"):
+                  "ddt_accept_compact", "ddt_verify_attn_argmax", "ddt_verify_step"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -184,11 +192,7 @@ def verify_attn(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, *, H, sca
     return out, lse
 
 
-def verify_attn_argmax(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, logits, *, H, scale, out=None,
-                       lse=None, workspace=None, idx=None, argmax_workspace=None, kv_chunk=0, stream=None):
-    """verify_attn and argmax(logits) in one launch -> (out, lse, idx)."""
-    desc, pl, out, lse, workspace, ws_n = _attn_args(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, H,
-                                                     scale, out, lse, workspace, kv_chunk)
+def _argmax_task(logits, idx, argmax_workspace):
     _dev(logits, None, "logits")
     ld = _rows(logits, "logits")
     rows, V = logits.shape
@@ -199,11 +203,63 @@ def verify_attn_argmax(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, lo
     if argmax_workspace is None and need > 0:
         argmax_workspace = torch.zeros((need,), dtype=torch.uint8, device=logits.device)  # zero before first use
     am_n = 0 if argmax_workspace is None else argmax_workspace.numel() * argmax_workspace.element_size()
-    task = ArgmaxTask(_p(logits), _dtype_code(logits), rows, V, ld, _p(idx), _p(argmax_workspace), am_n)
+    return ArgmaxTask(_p(logits), _dtype_code(logits), rows, V, ld, _p(idx), _p(argmax_workspace), am_n), idx
+
+
+def verify_attn_argmax(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, logits, *, H, scale, out=None,
+                       lse=None, workspace=None, idx=None, argmax_workspace=None, kv_chunk=0, stream=None):
+    """verify_attn and argmax(logits) in one launch -> (out, lse, idx)."""
+    desc, pl, out, lse, workspace, ws_n = _attn_args(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, H,
+                                                     scale, out, lse, workspace, kv_chunk)
+    task, idx = _argmax_task(logits, idx, argmax_workspace)
     _check(lib().ddt_verify_attn_argmax(ctypes.byref(desc), _p(q_lat), _p(q_pe), _p(ckv), _p(kpe), _p(kv_base),
                                         pl.ctypes.data, _p(mask), _p(out), _p(lse), _p(workspace), ws_n,
                                         ctypes.byref(task), _stream(stream)), "ddt_verify_attn_argmax")
     return out, lse, idx
+
+
+def _accept_outputs(parents, accept_len, path, tokens):
+    B, N = parents.shape
+    dev = parents.device
+    if accept_len is None:
+        accept_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    if path is None:
+        path = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if tokens is None:
+        tokens = torch.empty((B, N), dtype=torch.int32, device=dev)
+    for t, n in ((accept_len, "accept_len"), (path, "path"), (tokens, "tokens")):
+        _contig(t, torch.int32, n)
+    return accept_len, path, tokens
+
+
+def verify_step(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, logits, draft_ids, parents, prefix_len, *,
+                H, scale, new_prefix_len=None, out=None, lse=None, workspace=None, idx=None, argmax_workspace=None,
+                accept_len=None, path=None, tokens=None, src_slot=None, kv_chunk=0, stream=None):
+    """Attention + argmax, then acceptance + compaction, in two launches.
+
+    logits [B*N, V] (one target row per tree node); draft_ids, parents [B, N]
+    int32; prefix_len [B] int32 device (same values as prefix_len_host);
+    new_prefix_len [B] int32 device receives the advanced lengths (default:
+    prefix_len itself, updated in place).  The cache views ckv / kpe are
+    compacted in place.
+    -> (out, lse, idx, accept_len, path, tokens, new_prefix_len)."""
+    desc, pl, out, lse, workspace, ws_n = _attn_args(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, H,
+                                                     scale, out, lse, workspace, kv_chunk)
+    task, idx = _argmax_task(logits, idx, argmax_workspace)
+    for t, n in ((draft_ids, "draft_ids"), (parents, "parents"), (prefix_len, "prefix_len")):
+        _contig(t, torch.int32, n)
+    if tuple(parents.shape) != (desc.B, desc.N) or tuple(draft_ids.shape) != (desc.B, desc.N):
+        raise ValueError("draft_ids and parents must be [B, N]")
+    if new_prefix_len is None:
+        new_prefix_len = prefix_len
+    _contig(new_prefix_len, torch.int32, "new_prefix_len")
+    accept_len, path, tokens = _accept_outputs(parents, accept_len, path, tokens)
+    acc = AcceptTask(_p(draft_ids), _p(parents), _p(accept_len), _p(path), _p(tokens), _p(prefix_len),
+                     _p(new_prefix_len), _p(src_slot))
+    _check(lib().ddt_verify_step(ctypes.byref(desc), _p(q_lat), _p(q_pe), _p(ckv), _p(kpe), _p(kv_base),
+                                 pl.ctypes.data, _p(mask), _p(out), _p(lse), _p(workspace), ws_n,
+                                 ctypes.byref(task), ctypes.byref(acc), _stream(stream)), "ddt_verify_step")
+    return out, lse, idx, accept_len, path, tokens, new_prefix_len
 
 
 def argmax_workspace_bytes(rows: int, V: int) -> int:
@@ -266,26 +322,23 @@ def compact_kv(ckv, kpe, kv_base, prefix_len, path, accept_len, src_slot=None, s
 
 
 def accept_compact(target_ids, draft_ids, parents, ckv, kpe, kv_base, prefix_len, accept_len=None, path=None,
-                   tokens=None, src_slot=None, stream=None):
-    """greedy_accept + compact_kv in one launch -> (accept_len, path, tokens)."""
+                   tokens=None, src_slot=None, new_prefix_len=None, stream=None):
+    """greedy_accept + compact_kv in one launch -> (accept_len, path, tokens).
+
+    The advanced lengths go to new_prefix_len (default: prefix_len, in place)."""
     for t, n in ((target_ids, "target_ids"), (draft_ids, "draft_ids"), (parents, "parents")):
         _contig(t, torch.int32, n)
     _dev(ckv, None, "ckv")
     _dev(kpe, ckv.dtype, "kpe")
     _contig(kv_base, torch.int64, "kv_base")
     _contig(prefix_len, torch.int32, "prefix_len")
+    if new_prefix_len is None:
+        new_prefix_len = prefix_len
+    _contig(new_prefix_len, torch.int32, "new_prefix_len")
     B, N = parents.shape
-    dev = parents.device
-    if accept_len is None:
-        accept_len = torch.empty((B,), dtype=torch.int32, device=dev)
-    if path is None:
-        path = torch.empty((B, N), dtype=torch.int32, device=dev)
-    if tokens is None:
-        tokens = torch.empty((B, N), dtype=torch.int32, device=dev)
-    for t, n in ((accept_len, "accept_len"), (path, "path"), (tokens, "tokens")):
-        _contig(t, torch.int32, n)
+    accept_len, path, tokens = _accept_outputs(parents, accept_len, path, tokens)
     _check(lib().ddt_accept_compact(_p(target_ids), _p(draft_ids), _p(parents), B, N, _p(accept_len), _p(path),
                                     _p(tokens), _p(ckv), _rows(ckv, "ckv"), _p(kpe), _rows(kpe, "kpe"),
                                     _dtype_code(ckv), ckv.shape[1], kpe.shape[1], _p(kv_base), _p(prefix_len),
-                                    _p(src_slot), _stream(stream)), "ddt_accept_compact")
+                                    _p(new_prefix_len), _p(src_slot), _stream(stream)), "ddt_accept_compact")
     return accept_len, path, tokens

@@ -55,11 +55,11 @@ def test_host_side_validation(lib):
     assert lib.ddt_argmax(null, 7, 4, 10, 10, null, null, 0, null) == -2    # dtype
     assert lib.ddt_compact_kv(null, 576, null, 576, 1, 512, 64, null, null, null, null, 1, 0, null, null) == -1
     assert lib.ddt_accept_compact(null, null, null, 1, 0, null, null, null, null, 576, null, 576, 1, 512, 64,
-                                  null, null, null, null) == -1                    # N < 1
+                                  null, null, null, null, null) == -1              # N < 1
     assert lib.ddt_accept_compact(null, null, null, 1, 8, null, null, null, null, 576, null, 576, 1, 512, 64,
-                                  null, null, null, null) == -1                    # null pointers
+                                  null, null, null, null, null) == -1              # null pointers
     assert lib.ddt_accept_compact(null, null, null, 0, 8, null, null, null, null, 576, null, 576, 1, 512, 64,
-                                  null, null, null, null) == 0                     # nothing to do
+                                  null, null, null, null, null) == 0               # nothing to do
     d = ddt.AttnDesc(1, 8, 64, 512, 64, ddt.DDT_BF16, 0.04, 0, 576, 576, 576, 576)
     pl = (ctypes.c_int32 * 1)(100)
     n = ctypes.c_size_t(0)
@@ -75,3 +75,25 @@ def test_host_side_validation(lib):
     assert lib.ddt_verify_workspace(ctypes.byref(d), pl, ctypes.byref(n)) == 0
     assert lib.ddt_verify_attn(ctypes.byref(d), null, null, null, null, null, pl, null, null, null,
                                null, 0, null) == -1
+
+
+def test_verify_step_validation(lib):
+    """ddt_verify_step rejects a missing or mismatched argmax task and a
+    missing acceptance output before launching.  The device pointers are
+    placeholders that are never dereferenced: every call fails validation."""
+    fake = ctypes.c_void_p(1 << 16)
+    d = ddt.AttnDesc(1, 8, 64, 512, 64, ddt.DDT_BF16, 0.04, 0, 576, 576, 576, 576)
+    pl = (ctypes.c_int32 * 1)(100)
+    args = (ctypes.byref(d), fake, fake, fake, fake, fake, pl, fake, fake, fake, fake, 1 << 30)
+    good_am = ddt.ArgmaxTask(fake, ddt.DDT_F32, 64, 1000, 1000, fake, fake, 1 << 30)
+    good_acc = ddt.AcceptTask(fake, fake, fake, fake, fake, fake, fake, None)
+    assert lib.ddt_verify_step(*args, None, ctypes.byref(good_acc), None) == -1            # no argmax task
+    assert lib.ddt_verify_step(*args, ctypes.byref(good_am), None, None) == -1             # no acceptance task
+    rows63 = ddt.ArgmaxTask(fake, ddt.DDT_F32, 63, 1000, 1000, fake, fake, 1 << 30)
+    assert lib.ddt_verify_step(*args, ctypes.byref(rows63), ctypes.byref(good_acc), None) == -1  # rows != B*N
+    for k in range(7):                                                                    # each output needed
+        f = [fake] * 7
+        f[k] = None
+        acc = ddt.AcceptTask(*f, None)
+        assert lib.ddt_verify_step(*args, ctypes.byref(good_am), ctypes.byref(acc), None) == -1, k
+

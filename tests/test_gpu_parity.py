@@ -281,6 +281,52 @@ def test_attn_argmax_fused(orc, cfg, over, logit_shape, ldt, kv_chunk):
     assert int(ws.sum().item()) == 0
 
 
+@pytest.mark.parametrize("cfg,over,V,ldt,kv_chunk", [
+    (2, dict(), None, "f32", 0),                                  # the K2-like head share, its own logits
+    (1, dict(B=3, H=3, N=5, prefix=61), 4096, "f32", 0),          # fp32 attention
+    (3, dict(B=3, prefix_range=(100, 3000)), None, "bf16", 224),  # ragged prefixes, full vocabulary
+    (3, dict(B=2, prefix_range=(0, 40)), 1000, "f32", 0),         # no split: the merge launch only accepts
+])
+def test_verify_step(orc, cfg, over, V, ldt, kv_chunk):
+    """ddt_verify_step == attention and argmax, then greedy acceptance on the
+    argmax ids and compaction with the length update (all against the
+    oracle); the committed lengths are read from one array and the advanced
+    ones written to another."""
+    w = synth.workload(cfg, **over)
+    rng = np.random.default_rng(17 + cfg)
+    if w.logits is not None:
+        x = w.logits
+    else:
+        V = w.vocab if V is None else V
+        t = synth.planted_targets(rng, w.parents, w.draft_ids % V, V, 0.8)
+        w.draft_ids = w.draft_ids % V
+        x = synth.target_logits(rng, t.reshape(-1), V)
+        if ldt == "bf16":
+            x = synth.to_bf16_bits(x)
+    dw = DevWorkload(w)
+    B, N = w.B, w.N
+    ref_out, ref_lse = oracle_attn(orc, w)        # attention reads the cache before compaction
+    t_ref = orc.argmax(x).reshape(B, N)
+    oa, op, ot = orc.greedy_accept(t_ref, w.draft_ids, w.parents)
+    opool = w.pool.copy()
+    opl, osrc = orc.compact_kv(opool[:, :w.d_lat], opool[:, w.d_lat:], w.kv_base, w.prefix_len, op, oa)
+    mask, _, _ = ddt.build_mask(dw.parents)
+    new_pl = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    src = torch.empty((B, N), dtype=torch.int32, device="cuda")
+    out, lse, idx, acc, path, tok, npl = ddt.verify_step(
+        dw.q_lat(), dw.q_pe(), dw.ckv(), dw.kpe(), dw.kv_base, w.prefix_len, mask, to_dev(x), dw.draft,
+        dw.parents, dw.prefix_dev, H=w.H, scale=w.scale, new_prefix_len=new_pl, src_slot=src, kv_chunk=kv_chunk)
+    assert (to_host(idx).reshape(B, N) == t_ref).all()
+    e_out, e_lse = rel_l2(as_f64(to_host(out)), ref_out), rel_l2(to_host(lse), ref_lse)
+    assert e_out <= ATTN_TOL[w.dtype] and e_lse <= ATTN_TOL[w.dtype], (e_out, e_lse)
+    assert (to_host(acc) == oa).all() and (to_host(path) == op).all() and (to_host(tok) == ot).all()
+    assert (to_host(npl) == opl).all() and (to_host(dw.prefix_dev) == w.prefix_len).all()
+    assert (to_host(src) == osrc).all()
+    got = np.ascontiguousarray(to_host(dw.pool))
+    assert got.dtype == opool.dtype and (got.view(np.uint8) == opool.view(np.uint8)).all()  # bits: the pool holds NaN
+    print(f"{w.name} B={B} N={N}: accepted {oa.tolist()}")
+
+
 def test_attn_config1_tiny_fp32(orc):
     _attn_check(orc, synth.workload(1), kv_chunks=(0, 32, 64))
 
