@@ -245,7 +245,12 @@ int ddt_accept_compact(const int32_t* target_ids, const int32_t* draft_ids, cons
  * writes the cache only after the attention has read it).
  * am->rows must be B*N (one target row per tree node, request-major).
  * acc->prefix_len (device) must hold the same lengths as prefix_len_host.
- * Errors as for the calls it replaces.
+ * mask may be NULL when N <= 128: the attention then derives each row's
+ * ancestor bits from acc->parents itself (pointer doubling across a
+ * wavefront), so the step needs no ddt_build_mask launch; a request whose
+ * tree is invalid sees no tree keys, as with ddt_build_mask's all-zero
+ * mask.  (Depth and tree_err are then not produced.)  A NULL mask with
+ * N > 128 is DDT_EINVAL.  Other errors as for the calls it replaces.
  */
 typedef struct {
     const int32_t* draft_ids;   /* [B][N] device                               */

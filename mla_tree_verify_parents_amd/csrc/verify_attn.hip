@@ -325,13 +325,82 @@ __device__ inline float4 load4<float>(const float* src) {
 // tiles, issued as inline asm the compiler does not count) have landed.
 __device__ inline void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Ancestor bits (self included) of `node` in a tree of N <= 128 nodes
+// whose parents are par[0..N) (the ancestor mask of "The Architecture of
+// Pragmatic Ambition", section "The Decision Architecture", for one row),
+// as two 64-bit words, by pointer doubling across the wavefront: lane l
+// keeps nodes l and l + 64, each with the set of ancestors found so far and
+// a jump to the first ancestor not yet in it.  A round ORs in the jump
+// target's set and takes over its jump; the set then still holds exactly
+// the ancestors below the jump, and the jump at least doubles its distance,
+// so log2(depth) + 1 rounds finish.  A tree that is not valid (parents[0]
+// != -1 or parents[i] outside [0, i)) gives no bits, like ddt_build_mask's
+// all-zero mask.  Every lane of the wavefront must take part.
+__device__ inline void tree_ancestors(const int32_t* __restrict__ par, int N, int node, uint64_t& w0,
+                                      uint64_t& w1) {
+    const int lane = threadIdx.x & 63;
+    const int u1 = lane + 64;
+    int j0 = lane < N ? par[lane] : -1;
+    int j1 = u1 < N ? par[u1] : -1;
+    const bool ok = (lane >= N || (lane == 0 ? j0 == -1 : (j0 >= 0 && j0 < lane))) &&
+                    (u1 >= N || (j1 >= 0 && j1 < u1));
+    w0 = 0;
+    w1 = 0;
+    if (__ballot(!ok) != 0) return;
+    uint64_t a0 = 1ull << lane, a1 = 0;  // node lane: words 0 and 1 of its set
+    uint64_t b0 = 0, b1 = 1ull << lane;  // node lane + 64
+    if (N <= 64) {
+        while (__ballot(j0 >= 0) != 0) {
+            const int src = j0 < 0 ? 0 : j0;
+            const uint64_t ta = __shfl(a0, src, 64);
+            const int tj = __shfl(j0, src, 64);
+            if (j0 >= 0) {
+                a0 |= ta;
+                j0 = tj;
+            }
+        }
+        w0 = __shfl(a0, node, 64);
+        return;
+    }
+    // (a shuffle returns the source lane's own register, so both nodes of
+    // the source lane are fetched and the reader picks one)
+    while (__ballot(j0 >= 0 || j1 >= 0) != 0) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            int& j = k == 0 ? j0 : j1;
+            const int src = (j < 0 ? 0 : j) & 63;
+            const bool hi = j >= 64;
+            const uint64_t xa0 = __shfl(a0, src, 64), xa1 = __shfl(a1, src, 64);
+            const uint64_t xb0 = __shfl(b0, src, 64), xb1 = __shfl(b1, src, 64);
+            const int xj0 = __shfl(j0, src, 64), xj1 = __shfl(j1, src, 64);
+            if (j >= 0) {
+                const uint64_t x0 = hi ? xb0 : xa0, x1 = hi ? xb1 : xa1;
+                if (k == 0) {
+                    a0 |= x0;
+                    a1 |= x1;
+                } else {
+                    b0 |= x0;
+                    b1 |= x1;
+                }
+                j = hi ? xj1 : xj0;
+            }
+        }
+    }
+    const bool hi = node >= 64;
+    const uint64_t ya0 = __shfl(a0, node & 63, 64), ya1 = __shfl(a1, node & 63, 64);
+    const uint64_t yb0 = __shfl(b0, node & 63, 64), yb1 = __shfl(b1, node & 63, 64);
+    w0 = hi ? yb0 : ya0;
+    w1 = hi ? yb1 : ya1;
+}
+
 struct VerifyParams {
     const void* q_lat;
     const void* q_pe;
     const void* ckv;
     const void* kpe;
     const int64_t* kv_base;
-    const uint64_t* mask;
+    const uint64_t* mask;       // ancestor bits from ddt_build_mask, or null:
+    const int32_t* parents;     // then each row's bits come from the parents (N <= 128)
     void* out;
     float* lse;
     void* ws_o;     // [slot][row group][DL/32][4][64][4] in the input dtype, normalised partial outputs
@@ -439,7 +508,8 @@ __device__ void argmax_stream(const VerifyParams& p, int am_id, char* lds) {
             }
             float m = mu[0];
 #pragma unroll
-            for (int u = 1; u < kPerThread; u += 2) m = ddt::fmax3_raw(m, mu[u], u + 1 < kPerThread ? mu[u + 1] : mu[u]);
+            for (int u = 1; u < kPerThread; u += 2)
+                m = ddt::fmax3_raw(m, mu[u], u + 1 < kPerThread ? mu[u + 1] : mu[u]);
             if (m > bv || bl < 0) {  // (the first stage always searches, -inf rows included)
                 int fu = -1;
 #pragma unroll
@@ -602,7 +672,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     if (wave < NGRP) {
         // =========================== score wavefront ===========================
         const int node = row / p.H;
-        const uint64_t* __restrict__ mrow = p.mask + ((int64_t)b * p.N + node) * p.W;
+        const uint64_t* __restrict__ mrow = p.mask + ((int64_t)b * p.N + node) * p.W;  // (unused without a mask)
         // queries: B operand of the score MFMA, resident for the whole split
         Frag q[S::NKS];
 #pragma unroll
@@ -616,9 +686,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         // registers; larger trees fetch words per tile
         uint64_t mreg[2] = {0, 0};
         if (kend > P) {
+            if (p.mask != nullptr) {
 #pragma unroll
-            for (int w = 0; w < 2; ++w)
-                if (w < p.W) mreg[w] = mrow[w];
+                for (int w = 0; w < 2; ++w)
+                    if (w < p.W) mreg[w] = mrow[w];
+            } else {
+                tree_ancestors(p.parents + (int64_t)b * p.N, p.N, node, mreg[0], mreg[1]);
+            }
         }
         // Settle the query and mask loads here, once, behind an opaque
         // definition, so no wait inside the loop is tied to them.
@@ -646,6 +720,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             uint64_t mw0, mw1;
             if (wlo == 0) {
                 mw0 = mreg[0];
+                mw1 = mreg[1];
+            } else if (p.mask == nullptr) {  // at most 128 nodes: word 1 is the last
+                mw0 = mreg[1];
                 mw1 = mreg[1];
             } else {
                 mw0 = mrow[wlo < p.W ? wlo : p.W - 1];
@@ -1133,12 +1210,15 @@ int launch(const VerifyParams& vp, const Plan& pl, int n_argmax, hipStream_t str
 }
 
 // Validates the call and fills the attention part of the launch parameters.
+// A null mask takes the ancestor bits from `parents` in the kernel.
 int setup_attn(const ddt_attn_desc* d, const void* q_lat, const void* q_pe, const void* ckv, const void* kpe,
-               const int64_t* kv_base, const int32_t* prefix_len_host, const uint64_t* mask, void* out, float* lse,
-               void* workspace, size_t workspace_bytes, VerifyParams* vp, Plan* pl) {
+               const int64_t* kv_base, const int32_t* prefix_len_host, const uint64_t* mask, const int32_t* parents,
+               void* out, float* lse, void* workspace, size_t workspace_bytes, VerifyParams* vp, Plan* pl) {
     int rc = check_desc(d, prefix_len_host);
     if (rc != DDT_OK) return rc;
-    if (!q_lat || !q_pe || !ckv || !kpe || !kv_base || !mask || !out || !lse) return DDT_EINVAL;
+    if (!q_lat || !q_pe || !ckv || !kpe || !kv_base || !out || !lse) return DDT_EINVAL;
+    if (!mask && !parents) return DDT_EINVAL;
+    if (!mask && d->N > 128) return DDT_EINVAL;  // in-kernel ancestor bits cover two words
     if (!ddt::aligned(q_lat, 16) || !ddt::aligned(q_pe, 16) || !ddt::aligned(ckv, 16) || !ddt::aligned(kpe, 16) ||
         !ddt::aligned(out, 16) || !ddt::aligned(lse, 4))
         return DDT_EINVAL;
@@ -1155,6 +1235,7 @@ int setup_attn(const ddt_attn_desc* d, const void* q_lat, const void* q_pe, cons
     vp->kpe = kpe;
     vp->kv_base = kv_base;
     vp->mask = mask;
+    vp->parents = mask ? nullptr : parents;
     vp->out = out;
     vp->lse = lse;
     vp->ld_ql = d->ld_ql;
@@ -1242,8 +1323,8 @@ extern "C" int ddt_verify_attn(const ddt_attn_desc* d, const void* q_lat, const 
                                size_t workspace_bytes, hipStream_t stream) {
     VerifyParams vp{};
     Plan pl;
-    const int rc = setup_attn(d, q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, out, lse, workspace,
-                              workspace_bytes, &vp, &pl);
+    const int rc = setup_attn(d, q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, nullptr, out, lse,
+                              workspace, workspace_bytes, &vp, &pl);
     if (rc != DDT_OK) return rc;
     return run(d, vp, pl, 0, stream);
 }
@@ -1254,8 +1335,8 @@ extern "C" int ddt_verify_attn_argmax(const ddt_attn_desc* d, const void* q_lat,
                                       size_t workspace_bytes, const ddt_argmax_task* am, hipStream_t stream) {
     VerifyParams vp{};
     Plan pl;
-    int rc = setup_attn(d, q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, out, lse, workspace,
-                        workspace_bytes, &vp, &pl);
+    int rc = setup_attn(d, q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, nullptr, out, lse,
+                        workspace, workspace_bytes, &vp, &pl);
     if (rc != DDT_OK) return rc;
     int wgs = 0;
     rc = setup_argmax(am, pl, &vp, &wgs);
@@ -1267,12 +1348,12 @@ extern "C" int ddt_verify_step(const ddt_attn_desc* d, const void* q_lat, const 
                                const int64_t* kv_base, const int32_t* prefix_len_host, const uint64_t* mask,
                                void* out, float* lse, void* workspace, size_t workspace_bytes,
                                const ddt_argmax_task* am, const ddt_accept_task* acc, hipStream_t stream) {
+    if (am == nullptr || acc == nullptr) return DDT_EINVAL;
     VerifyParams vp{};
     Plan pl;
-    int rc = setup_attn(d, q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, out, lse, workspace,
-                        workspace_bytes, &vp, &pl);
+    int rc = setup_attn(d, q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, acc->parents, out, lse,
+                        workspace, workspace_bytes, &vp, &pl);
     if (rc != DDT_OK) return rc;
-    if (am == nullptr || acc == nullptr) return DDT_EINVAL;
     if (am->rows != (int64_t)d->B * d->N) return DDT_EINVAL;  // one target row per tree node
     int wgs = 0;
     rc = setup_argmax(am, pl, &vp, &wgs);

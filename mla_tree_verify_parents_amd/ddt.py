@@ -152,12 +152,16 @@ def verify_workspace_bytes(desc: AttnDesc, prefix_len_host) -> int:
     return n.value
 
 
-def _attn_args(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, H, scale, out, lse, workspace, kv_chunk):
+def _attn_args(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, H, scale, out, lse, workspace, kv_chunk,
+               BN=None):
     for t, n in ((q_lat, "q_lat"), (q_pe, "q_pe"), (ckv, "ckv"), (kpe, "kpe")):
         _dev(t, q_lat.dtype, n)
     _contig(kv_base, torch.int64, "kv_base")
-    _contig(mask, torch.int64, "mask")
-    B, N = mask.shape[0], mask.shape[1]
+    if mask is None:  # (B, N) given instead: the kernel derives the ancestor bits
+        B, N = BN
+    else:
+        _contig(mask, torch.int64, "mask")
+        B, N = mask.shape[0], mask.shape[1]
     rows = B * N * H
     if q_lat.shape[0] != rows or q_pe.shape[0] != rows:
         raise ValueError("q rows must be B*N*H")
@@ -237,6 +241,8 @@ def verify_step(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, logits, d
                 accept_len=None, path=None, tokens=None, src_slot=None, kv_chunk=0, stream=None):
     """Attention + argmax, then acceptance + compaction, in two launches.
 
+    mask: from build_mask, or None for trees of at most 128 nodes (the
+    attention then derives each row's ancestor bits from parents itself);
     logits [B*N, V] (one target row per tree node); draft_ids, parents [B, N]
     int32; prefix_len [B] int32 device (same values as prefix_len_host);
     new_prefix_len [B] int32 device receives the advanced lengths (default:
@@ -244,7 +250,7 @@ def verify_step(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, logits, d
     compacted in place.
     -> (out, lse, idx, accept_len, path, tokens, new_prefix_len)."""
     desc, pl, out, lse, workspace, ws_n = _attn_args(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, H,
-                                                     scale, out, lse, workspace, kv_chunk)
+                                                     scale, out, lse, workspace, kv_chunk, BN=tuple(parents.shape))
     task, idx = _argmax_task(logits, idx, argmax_workspace)
     for t, n in ((draft_ids, "draft_ids"), (parents, "parents"), (prefix_len, "prefix_len")):
         _contig(t, torch.int32, n)

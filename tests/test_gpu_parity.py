@@ -281,18 +281,26 @@ def test_attn_argmax_fused(orc, cfg, over, logit_shape, ldt, kv_chunk):
     assert int(ws.sum().item()) == 0
 
 
+@pytest.mark.parametrize("with_mask", [True, False], ids=["mask", "in_kernel_mask"])
 @pytest.mark.parametrize("cfg,over,V,ldt,kv_chunk", [
     (2, dict(), None, "f32", 0),                                  # the K2-like head share, its own logits
     (1, dict(B=3, H=3, N=5, prefix=61), 4096, "f32", 0),          # fp32 attention
     (3, dict(B=3, prefix_range=(100, 3000)), None, "bf16", 224),  # ragged prefixes, full vocabulary
     (3, dict(B=2, prefix_range=(0, 40)), 1000, "f32", 0),         # no split: the merge launch only accepts
+    (1, dict(B=2, H=1, N=128, prefix=70), 500, "f32", 0),         # two mask words, one row per node
+    (1, dict(B=2, H=2, N=100, prefix=9, chain=True), 500, "f32", 32),  # chains: deepest trees
 ])
-def test_verify_step(orc, cfg, over, V, ldt, kv_chunk):
+def test_verify_step(orc, cfg, over, V, ldt, kv_chunk, with_mask):
     """ddt_verify_step == attention and argmax, then greedy acceptance on the
     argmax ids and compaction with the length update (all against the
     oracle); the committed lengths are read from one array and the advanced
-    ones written to another."""
+    ones written to another.  Without a mask the attention derives the
+    ancestor bits from the parents itself."""
+    over = dict(over)
+    chain = over.pop("chain", False)
     w = synth.workload(cfg, **over)
+    if chain:
+        w.parents[:] = np.arange(-1, w.N - 1, dtype=np.int32)
     rng = np.random.default_rng(17 + cfg)
     if w.logits is not None:
         x = w.logits
@@ -310,7 +318,7 @@ def test_verify_step(orc, cfg, over, V, ldt, kv_chunk):
     oa, op, ot = orc.greedy_accept(t_ref, w.draft_ids, w.parents)
     opool = w.pool.copy()
     opl, osrc = orc.compact_kv(opool[:, :w.d_lat], opool[:, w.d_lat:], w.kv_base, w.prefix_len, op, oa)
-    mask, _, _ = ddt.build_mask(dw.parents)
+    mask = ddt.build_mask(dw.parents)[0] if with_mask else None
     new_pl = torch.full((B,), -7, dtype=torch.int32, device="cuda")
     src = torch.empty((B, N), dtype=torch.int32, device="cuda")
     out, lse, idx, acc, path, tok, npl = ddt.verify_step(
@@ -325,6 +333,29 @@ def test_verify_step(orc, cfg, over, V, ldt, kv_chunk):
     got = np.ascontiguousarray(to_host(dw.pool))
     assert got.dtype == opool.dtype and (got.view(np.uint8) == opool.view(np.uint8)).all()  # bits: the pool holds NaN
     print(f"{w.name} B={B} N={N}: accepted {oa.tolist()}")
+
+
+def test_verify_step_invalid_tree_without_mask():
+    """An invalid tree gives its rows no tree keys without a mask exactly as
+    build_mask's all-zero mask does (same kernel, same bits: bit-exact);
+    the valid request beside it is unaffected."""
+    w = synth.workload(3, B=2, N=40, prefix_range=(50, 400))
+    w.parents[1, 9] = 12                                  # parent after its child: invalid
+    V = 700
+    rng = np.random.default_rng(5)
+    w.draft_ids = w.draft_ids % V
+    x = synth.target_logits(rng, synth.planted_targets(rng, w.parents, w.draft_ids, V, 0.8).reshape(-1), V)
+    res = []
+    for with_mask in (True, False):
+        dw = DevWorkload(w)
+        mask, _, err = ddt.build_mask(dw.parents)
+        assert to_host(err).tolist() == [0, 1]
+        r = ddt.verify_step(dw.q_lat(), dw.q_pe(), dw.ckv(), dw.kpe(), dw.kv_base, w.prefix_len,
+                            mask if with_mask else None, to_dev(x), dw.draft, dw.parents, dw.prefix_dev,
+                            H=w.H, scale=w.scale, new_prefix_len=torch.empty_like(dw.prefix_dev))
+        res.append([to_host(t) for t in r] + [to_host(dw.pool)])
+    for a, b in zip(*res):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
 
 
 def test_attn_config1_tiny_fp32(orc):
