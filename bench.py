@@ -45,7 +45,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=2, help="workload configuration (2, 3 or 4)")
+    ap.add_argument("--config", type=int, default=2, help="workload configuration (2, 3, 4, or 5: the verify loop)")
+    ap.add_argument("--loop-steps", type=int, default=100, help="timed iterations of the verify loop (config 5)")
     ap.add_argument("--attn-reps", type=int, default=200, help="back-to-back attention launches timed for the roofline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget for the oracle timing")
@@ -110,6 +111,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.config == 5:
+        return run_loop(args, dev)
     w, desc = workload_for(args.config)
 
     def to_dev(a):
@@ -258,6 +261,106 @@ def main():
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, flops)
     print(json.dumps(res), flush=True)
+
+
+def run_loop(args, dev):
+    """Configuration 5: the verify loop.  Every iteration draws its inputs
+    (untimed: draft candidates, best-first trees, node latents, queries,
+    target logits), runs the hot path (one ddt_verify_step call: ancestor
+    bits, attention, argmax, acceptance, compaction, length update; two
+    launches) between HIP events, then advances the loop (the bonus token is
+    the next root; the host mirrors the grown lengths).  `value` is the
+    attention FLOPs of all timed iterations over their summed device time."""
+    import torch
+
+    from mla_tree_verify_parents_amd import ddt, e2e, synth
+
+    W, K = args.warmup, args.loop_steps
+    loop = e2e.VerifyLoop(steps=W + K)
+    stream = torch.cuda.current_stream()
+    t_ms, flops, keys, acc_sum = 0.0, 0, 0, 0
+    snap = None
+    for it in range(W + K):
+        inp = loop.make_inputs()
+        if it == W + K - 1 and not args.no_cpu_baseline:
+            snap = (synth.Workload(name="config5", B=loop.B, H=loop.H, N=loop.N, d_lat=loop.d_lat,
+                                   d_rope=loop.d_rope, dtype="bf16", scale=loop.scale,
+                                   prefix_len=inp.prefix_len.copy(), kv_base=loop.kv_base_host.copy(),
+                                   capacity=loop.capacity.copy(), pool=to_host_bits(loop.pool),
+                                   q=to_host_bits(inp.q), parents=inp.parents, draft_ids=inp.draft_ids,
+                                   logits=inp.logits.cpu().numpy(), vocab=loop.vocab))
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        res = loop.run_step(inp)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        acc = loop.advance(res)
+        if it >= W:
+            t_ms += e0.elapsed_time(e1)
+            flops += inp.visible_pairs(loop.H) * FLOP_PER_PAIR
+            keys += int(inp.prefix_len.sum()) + loop.B * loop.N
+            acc_sum += int(acc.sum())
+    ms_step = t_ms / K
+    # the attention launch alone on the last iteration's inputs, for the roofline
+    mask = ddt.build_mask(inp.parents_dev)[0]
+    dl = loop.d_lat
+    ws = loop.workspace_for(inp.prefix_len)
+
+    def attn():
+        ddt.verify_attn(inp.q[:, :dl], inp.q[:, dl:], loop.ckv(), loop.kpe(), loop.kv_base, inp.prefix_len, mask,
+                        H=loop.H, scale=loop.scale, out=loop.out, lse=loop.lse, workspace=ws)
+
+    reps = max(4, min(args.attn_reps, 50))
+    attn()
+    torch.cuda.synchronize()
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record(stream)
+    for _ in range(reps):
+        attn()
+    a1.record(stream)
+    torch.cuda.synchronize()
+    ms_attn = a0.elapsed_time(a1) / reps
+    last_flops = inp.visible_pairs(loop.H) * FLOP_PER_PAIR
+    achieved = last_flops / (ms_attn * 1e-3) / 1e12
+    last_keys = int(inp.prefix_len.sum()) + loop.B * loop.N
+    attn_bytes = last_keys * (dl + loop.d_rope) * 2 + loop.B * loop.N * loop.H * ((dl + loop.d_rope) * 2 + dl * 2 + 4)
+    res = {
+        "metric": "verify-attn TFLOP/s + cache tokens/s; % of MFMA/HBM roofline, 1xMI355X",
+        "value": round(flops / (t_ms * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) latents, queries and target logits with planted tokens; "
+                "best-first trees from N(0,9) draft logits)",
+        "config": {"workload": "config5 verify loop: B=32, H=8, 512+64 bf16, prefix U[2048,65536] growing, "
+                               "64 nodes (best-first, top-8, depth<=8), target logits 2048x163840 fp32",
+                   "requests": loop.B, "heads": loop.H, "nodes": loop.N, "iterations": K,
+                   "cache_tokens_per_iteration": keys / K, "accepted_drafts_per_request_step": acc_sum / (K * loop.B),
+                   "attn_flop_per_step": flops / K},
+        "cache_tokens_per_s": round(keys / (t_ms * 1e-3), 1),
+        "verify_attn_ms": round(ms_attn, 5),
+        "roofline": {"bound": "mfma", "kernel": "verify_split+verify_combine (ddt_verify_attn), last iteration",
+                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "algorithmic_bytes": attn_bytes,
+                     "achieved_GBps": round(attn_bytes / (ms_attn * 1e-3) / 1e9, 1)},
+    }
+    if snap is not None:
+        res["cpu_baseline"] = cpu_baseline(snap, args.cpu_seconds, last_flops)
+    print(json.dumps(res), flush=True)
+
+
+def to_host_bits(t):
+    """bf16 device tensor -> numpy uint16 bit patterns."""
+    import torch
+    return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
 
 
 def row_pairs(w):
