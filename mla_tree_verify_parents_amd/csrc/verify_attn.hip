@@ -41,7 +41,10 @@
 //    reuse its L2.
 #include <math.h>
 
+#include <algorithm>
 #include <type_traits>
+#include <utility>
+#include <vector>
 
 #include "argmax_scan.h"
 #include "common.h"
@@ -410,7 +413,14 @@ struct VerifyParams {
     float scale_log2;
     int P[DDT_MAX_BATCH];
     int nsplit[DDT_MAX_BATCH];
-    int wg_begin[DDT_MAX_BATCH + 1];
+    int wg_begin[DDT_MAX_BATCH + 1];  // partial-output slot of (b, split 0, row tile 0)
+    // dispatch order: groups (b, split) of row tiles, cut into units of up
+    // to unit_rows row tiles dealt to the XCDs round robin; whole-chunk
+    // splits first (request-major), then each request's shorter last split,
+    // longest first
+    int full_gbegin[DDT_MAX_BATCH + 1];  // first whole-chunk group of request b
+    int part_b[DDT_MAX_BATCH];           // request of the k-th last-split group
+    int n_full_groups, n_units, unit_rows, units_per_group;
     // target argmax riding along in the same launch (workgroups n_attn ..)
     int n_attn;                 // attention workgroups (the rest are argmax workgroups)
     int am_wgs, am_dtype, am_vec;
@@ -617,6 +627,35 @@ struct Shape {
 // MFMAs of tile j together with the softmax of tile j-1, and the value
 // wavefronts multiply tile j-2 while loading tile j+1 into the ring slot of
 // tile j-3.
+// Work item of attention block `blk`: request b, key split, row tile rt;
+// false for the few blocks that pad the XCD deal.  The hardware deals
+// blocks to the 8 XCDs round robin, so block x + 8j runs on XCD x; unit u
+// (up to unit_rows row tiles of one key split, which then share that XCD's
+// L2) goes to XCD u % 8 at position u / 8, and units are numbered in the
+// order they should start.
+__device__ inline bool work_item(const VerifyParams& p, int blk, int& b, int& split, int& rt) {
+    const int x = blk % ddt::kXcds, j = blk / ddt::kXcds;
+    const int pos = j / p.unit_rows, r_in = j - pos * p.unit_rows;
+    const int u = pos * ddt::kXcds + x;
+    if (u >= p.n_units) return false;
+    const int grp = u / p.units_per_group, sg = u - grp * p.units_per_group;
+    rt = sg * p.unit_rows + r_in;
+    if (rt >= p.row_tiles) return false;
+    if (grp < p.n_full_groups) {
+        int lo = 0, hi = p.B - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (p.full_gbegin[mid] <= grp) lo = mid; else hi = mid - 1;
+        }
+        b = lo;
+        split = grp - p.full_gbegin[b];
+    } else {
+        b = p.part_b[grp - p.n_full_groups];
+        split = (p.P[b] + p.N) / p.chunk;  // the shorter last split
+    }
+    return true;
+}
+
 template <typename T, int DL, int DR, bool kArgmax>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void verify_split(
     const VerifyParams p) {
@@ -640,20 +679,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int grp = wave % NGRP;
 
-    // ---- work item: (request, key split, row tile), XCD-contiguous ----
-    const int wl = ddt::xcd_logical_block(blockIdx.x, kArgmax ? p.n_attn : (int)gridDim.x);
-    int b = 0;
-    {
-        int lo = 0, hi = p.B - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (p.wg_begin[mid] <= wl) lo = mid; else hi = mid - 1;
-        }
-        b = lo;
-    }
-    const int local = wl - p.wg_begin[b];
-    const int split = local / p.row_tiles;
-    const int rt = local - split * p.row_tiles;
+    // ---- work item: (request, key split, row tile) ----
+    int b = 0, split = 0, rt = 0;
+    if (!work_item(p, (int)blockIdx.x, b, split, rt)) return;  // (uniform: the whole workgroup)
+    const int wl = p.wg_begin[b] + split * p.row_tiles + rt;   // partial-output slot
     const int P = p.P[b];
     const int kbeg = split * p.chunk;
     const int kend = min(kbeg + p.chunk, P + p.N);
@@ -1130,6 +1159,7 @@ int num_cus() {
 
 struct Plan {
     int row_tiles = 0, chunk = 0, total_wg = 0;
+    int n_blocks = 0;  // attention blocks launched (work items plus padding of the XCD deal)
     bool any_split = false;
     size_t ws_bytes = 0, ws_lse_off = 0;
 };
@@ -1153,21 +1183,101 @@ int check_desc(const ddt_attn_desc* d, const int32_t* prefix_len_host) {
     return DDT_OK;
 }
 
+// Estimated finish time, in tile phases, of the attention launch when the
+// keys are split into chunks of `chunk`: workgroups of a whole chunk start
+// first and fill the CUs in rounds; the shorter last splits then go, longest
+// first, to the earliest free CUs (loads are kept as (value, count) buckets,
+// so the estimate costs about groups^2 steps, not one per workgroup); a
+// merge launch is added when any request is split.
+constexpr int64_t kItemOverhead = 10;   // prologue, pipeline fill and epilogue of a workgroup, in tiles
+constexpr int64_t kMergeCost = 8;       // the split merge launch, in tiles
+
+int64_t plan_cost(const ddt_attn_desc* d, const int32_t* P, int row_tiles, int64_t chunk, int cus) {
+    int64_t full = 0;
+    bool split = false;
+    std::vector<int64_t> tails;
+    for (int b = 0; b < d->B; ++b) {
+        const int64_t T = (int64_t)P[b] + d->N;
+        full += T / chunk;
+        if (T > chunk) split = true;
+        if (T % chunk) tails.push_back(T % chunk);
+    }
+    std::sort(tails.begin(), tails.end(), [](int64_t a, int64_t c) { return a > c; });
+    const int64_t cf = (chunk + KT - 1) / KT + kItemOverhead;
+    const int64_t items = full * row_tiles;
+    const int64_t rounds = items / cus, rem = items % cus;
+    // CU loads as ascending (value, count) buckets
+    std::vector<std::pair<int64_t, int64_t>> load, next;
+    if (cus - rem > 0) load.push_back({rounds * cf, cus - rem});
+    if (rem > 0) load.push_back({(rounds + 1) * cf, rem});
+    for (const int64_t t : tails) {
+        const int64_t c = (t + KT - 1) / KT + kItemOverhead;
+        int64_t need = row_tiles;
+        while (need > 0) {  // the `need` least-loaded CUs each take one workgroup of the group
+            next.clear();
+            std::vector<std::pair<int64_t, int64_t>> moved;
+            size_t i = 0;
+            for (; i < load.size() && need > 0; ++i) {
+                const int64_t take = load[i].second < need ? load[i].second : need;
+                moved.push_back({load[i].first + c, take});
+                need -= take;
+                if (take < load[i].second) next.push_back({load[i].first, load[i].second - take});
+            }
+            for (; i < load.size(); ++i) next.push_back(load[i]);
+            next.insert(next.end(), moved.begin(), moved.end());
+            std::sort(next.begin(), next.end());
+            load.clear();
+            for (const auto& e : next) {
+                if (!load.empty() && load.back().first == e.first)
+                    load.back().second += e.second;
+                else
+                    load.push_back(e);
+            }
+        }
+    }
+    const int64_t finish = load.empty() ? 0 : load.back().first;
+    return finish + (split ? kMergeCost : 0);
+}
+
+// The key chunk with the lowest estimated finish time among chunks that cut
+// the longest request into 1..64 equal parts, that give the CUs 1..32
+// rounds of equal work, and the smallest chunk (ties go to the larger
+// chunk: fewer partial outputs).
+int64_t choose_chunk(const ddt_attn_desc* d, const int32_t* P, int row_tiles, int cus) {
+    int64_t tmax = 0, work = 0;
+    for (int b = 0; b < d->B; ++b) {
+        const int64_t T = (int64_t)P[b] + d->N;
+        tmax = T > tmax ? T : tmax;
+        work += T * row_tiles;
+    }
+    const int64_t top = (int64_t)ddt::round_up((size_t)tmax, KT);
+    int64_t best = top, best_cost = plan_cost(d, P, row_tiles, top, cus);
+    auto consider = [&](int64_t c) {
+        c = (int64_t)ddt::round_up((size_t)c, KT);
+        if (c < kMinChunk) c = kMinChunk;
+        if (c > top) c = top;
+        const int64_t cost = plan_cost(d, P, row_tiles, c, cus);
+        if (cost < best_cost || (cost == best_cost && c > best)) best = c, best_cost = cost;
+    };
+    consider(kMinChunk);
+    for (int m = 2; m <= 64; ++m) consider((tmax + m - 1) / m);
+    for (int k = 1; k <= 32; ++k) consider((work + (int64_t)k * cus - 1) / ((int64_t)k * cus));
+    return best;
+}
+
+constexpr int kUnitRows = 8;  // row tiles of one key split dealt to one XCD together
+
 Plan make_plan(const ddt_attn_desc* d, const int32_t* P, VerifyParams* vp) {
     Plan pl;
     const int rows = d->H * d->N;
     pl.row_tiles = (rows + ROWS_WG - 1) / ROWS_WG;
-    if (d->kv_chunk > 0) {
+    const int cus = num_cus();
+    if (d->kv_chunk > 0)
         pl.chunk = (int)ddt::round_up((size_t)d->kv_chunk, KT);
-    } else {
-        int64_t work = 0;
-        for (int b = 0; b < d->B; ++b) work += (int64_t)pl.row_tiles * (P[b] + d->N);
-        const int64_t ideal = (work + num_cus() - 1) / num_cus();
-        int64_t ch = (int64_t)ddt::round_up((size_t)ideal, KT);
-        if (ch < kMinChunk) ch = kMinChunk;
-        pl.chunk = (int)ch;
-    }
+    else
+        pl.chunk = (int)choose_chunk(d, P, pl.row_tiles, cus);
     int64_t total = 0;
+    int n_full = 0;
     for (int b = 0; b < d->B; ++b) {
         const int64_t T = (int64_t)P[b] + d->N;
         const int ns = (int)((T + pl.chunk - 1) / pl.chunk);
@@ -1176,12 +1286,40 @@ Plan make_plan(const ddt_attn_desc* d, const int32_t* P, VerifyParams* vp) {
             vp->P[b] = P[b];
             vp->nsplit[b] = ns;
             vp->wg_begin[b] = (int)total;
+            vp->full_gbegin[b] = n_full;
         }
+        n_full += (int)(T / pl.chunk);
         total += (int64_t)ns * pl.row_tiles;
     }
     if (total > 0x7fffffff) total = 0x7fffffff;
     pl.total_wg = (int)total;
-    if (vp) vp->wg_begin[d->B] = pl.total_wg;
+    // last splits shorter than a chunk, longest first
+    int order[DDT_MAX_BATCH];
+    int n_part = 0;
+    for (int b = 0; b < d->B; ++b)
+        if (((int64_t)P[b] + d->N) % pl.chunk) order[n_part++] = b;
+    std::stable_sort(order, order + n_part, [&](int a, int c) {
+        return ((int64_t)P[a] + d->N) % pl.chunk > ((int64_t)P[c] + d->N) % pl.chunk;
+    });
+    // One round of workgroups (at most one per CU): deal single row tiles so
+    // every XCD gets the same number of workgroups (the CUs left idle then
+    // sit evenly on all XCDs, for the argmax riding along); several rounds:
+    // deal units of kUnitRows row tiles that share a key split through L2.
+    int unit_rows = pl.row_tiles < kUnitRows ? pl.row_tiles : kUnitRows;
+    if (pl.total_wg <= cus) unit_rows = 1;
+    const int upg = (pl.row_tiles + unit_rows - 1) / unit_rows;
+    const int64_t n_units = (int64_t)(n_full + n_part) * upg;
+    const int64_t blocks = (n_units + ddt::kXcds - 1) / ddt::kXcds * ddt::kXcds * unit_rows;
+    pl.n_blocks = blocks > 0x7fffffff ? 0x7fffffff : (int)blocks;
+    if (vp) {
+        vp->wg_begin[d->B] = pl.total_wg;
+        vp->full_gbegin[d->B] = n_full;
+        for (int k = 0; k < n_part; ++k) vp->part_b[k] = order[k];
+        vp->n_full_groups = n_full;
+        vp->n_units = (int)n_units;
+        vp->unit_rows = unit_rows;
+        vp->units_per_group = upg;
+    }
     if (pl.any_split) {
         const size_t o = (size_t)pl.total_wg * ROWS_WG * d->d_lat * (size_t)ddt::elem_bytes(d->dtype);
         pl.ws_lse_off = ddt::round_up(o, 256);
@@ -1193,10 +1331,10 @@ Plan make_plan(const ddt_attn_desc* d, const int32_t* P, VerifyParams* vp) {
 template <typename T, int DL, int DR>
 int launch(const VerifyParams& vp, const Plan& pl, int n_argmax, hipStream_t stream) {
     if (n_argmax > 0)
-        hipLaunchKernelGGL((verify_split<T, DL, DR, true>), dim3(pl.total_wg + n_argmax), dim3(kThreads), 0, stream,
+        hipLaunchKernelGGL((verify_split<T, DL, DR, true>), dim3(pl.n_blocks + n_argmax), dim3(kThreads), 0, stream,
                            vp);
     else
-        hipLaunchKernelGGL((verify_split<T, DL, DR, false>), dim3(pl.total_wg), dim3(kThreads), 0, stream, vp);
+        hipLaunchKernelGGL((verify_split<T, DL, DR, false>), dim3(pl.n_blocks), dim3(kThreads), 0, stream, vp);
     DDT_CHECK_LAUNCH();
     const int nblk = pl.any_split ? vp.B * pl.row_tiles * NW * (DL / 64) : 0;
     if (vp.n_accept > 0) {
@@ -1250,7 +1388,7 @@ int setup_attn(const ddt_attn_desc* d, const void* q_lat, const void* q_pe, cons
     vp->row_tiles = pl->row_tiles;
     vp->chunk = pl->chunk;
     vp->total_wg = pl->total_wg;
-    vp->n_attn = pl->total_wg;
+    vp->n_attn = pl->n_blocks;
     vp->scale_log2 = d->scale * kLog2e;
     return DDT_OK;
 }
@@ -1274,12 +1412,13 @@ int setup_argmax(const ddt_argmax_task* am, const Plan& pl, VerifyParams* vp, in
     ddt_argmax_workspace(am->rows, am->V, &need);
     if (need > 0 && (am->workspace == nullptr || am->workspace_bytes < need || !ddt::aligned(am->workspace, 16)))
         return DDT_EWORKSPACE;
-    // one argmax workgroup per CU the attention leaves idle (at least half
-    // the CUs' worth when it fills the GPU), each taking an equal share of
-    // the flattened rows x V range; rows are shared between workgroups only
-    // where the workspace can merge them
+    // one argmax workgroup per CU the attention leaves idle, each taking an
+    // equal share of the flattened rows x V range; when the attention takes
+    // every CU (several rounds), two workgroups per CU that start as the
+    // attention's last workgroups end; rows are shared between workgroups
+    // only where the workspace can merge them
     const int cus = num_cus();
-    int64_t wgs = pl.total_wg < cus ? cus - pl.total_wg : cus / 2;
+    int64_t wgs = pl.total_wg < cus ? cus - pl.total_wg : 2 * (int64_t)cus;
     if (wgs < 1) wgs = 1;
     const int64_t es = ddt::elem_bytes(am->dtype);
     const int64_t vec_elems = 16 / es;
