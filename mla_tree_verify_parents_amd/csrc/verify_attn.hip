@@ -43,8 +43,6 @@
 
 #include <algorithm>
 #include <type_traits>
-#include <utility>
-#include <vector>
 
 #include "argmax_scan.h"
 #include "common.h"
@@ -1186,82 +1184,108 @@ int check_desc(const ddt_attn_desc* d, const int32_t* prefix_len_host) {
 // Estimated finish time, in tile phases, of the attention launch when the
 // keys are split into chunks of `chunk`: workgroups of a whole chunk start
 // first and fill the CUs in rounds; the shorter last splits then go, longest
-// first, to the earliest free CUs (loads are kept as (value, count) buckets,
-// so the estimate costs about groups^2 steps, not one per workgroup); a
-// merge launch is added when any request is split.
+// first, to the earliest free CUs (loads are kept as (value, count) buckets
+// in a heap, so the estimate costs a few heap steps per request, not one per
+// workgroup); a merge launch is added when any request is split.
 constexpr int64_t kItemOverhead = 10;   // prologue, pipeline fill and epilogue of a workgroup, in tiles
 constexpr int64_t kMergeCost = 8;       // the split merge launch, in tiles
 
-int64_t plan_cost(const ddt_attn_desc* d, const int32_t* P, int row_tiles, int64_t chunk, int cus) {
+// `T` holds the requests' key counts in descending order.
+int64_t plan_cost(const int64_t* T, int B, int row_tiles, int64_t chunk, int cus) {
     int64_t full = 0;
     bool split = false;
-    std::vector<int64_t> tails;
-    for (int b = 0; b < d->B; ++b) {
-        const int64_t T = (int64_t)P[b] + d->N;
-        full += T / chunk;
-        if (T > chunk) split = true;
-        if (T % chunk) tails.push_back(T % chunk);
+    int64_t tails[DDT_MAX_BATCH];
+    int nt = 0;
+    for (int b = 0; b < B; ++b) {
+        full += T[b] / chunk;
+        if (T[b] > chunk) split = true;
+        if (T[b] % chunk) tails[nt++] = T[b] % chunk;
     }
-    std::sort(tails.begin(), tails.end(), [](int64_t a, int64_t c) { return a > c; });
+    std::sort(tails, tails + nt, [](int64_t x, int64_t y) { return x > y; });
     const int64_t cf = (chunk + KT - 1) / KT + kItemOverhead;
     const int64_t items = full * row_tiles;
     const int64_t rounds = items / cus, rem = items % cus;
-    // CU loads as ascending (value, count) buckets
-    std::vector<std::pair<int64_t, int64_t>> load, next;
-    if (cus - rem > 0) load.push_back({rounds * cf, cus - rem});
-    if (rem > 0) load.push_back({(rounds + 1) * cf, rem});
-    for (const int64_t t : tails) {
-        const int64_t c = (t + KT - 1) / KT + kItemOverhead;
+    // CU loads as (value, count) buckets in a min-heap; a group's workgroups
+    // go to the least-loaded CUs
+    struct Bucket {
+        int64_t v, n;
+    };
+    constexpr int kMaxBuckets = 4 * DDT_MAX_BATCH + 4;
+    Bucket heap[kMaxBuckets];    // (uninitialised: only the first nb are live)
+    Bucket loaded[kMaxBuckets];  // buckets a group has just loaded
+    int nb = 0;
+    const auto later = [](const Bucket& x, const Bucket& y) { return x.v > y.v; };
+    auto push = [&](int64_t v, int64_t n) {
+        heap[nb++] = Bucket{v, n};
+        std::push_heap(heap, heap + nb, later);
+    };
+    if (cus - rem > 0) push(rounds * cf, cus - rem);
+    if (rem > 0) push((rounds + 1) * cf, rem);
+    int64_t finish = rem > 0 ? (rounds + 1) * cf : rounds * cf;
+    for (int k = 0; k < nt; ++k) {
+        const int64_t c = (tails[k] + KT - 1) / KT + kItemOverhead;
         int64_t need = row_tiles;
-        while (need > 0) {  // the `need` least-loaded CUs each take one workgroup of the group
-            next.clear();
-            std::vector<std::pair<int64_t, int64_t>> moved;
-            size_t i = 0;
-            for (; i < load.size() && need > 0; ++i) {
-                const int64_t take = load[i].second < need ? load[i].second : need;
-                moved.push_back({load[i].first + c, take});
-                need -= take;
-                if (take < load[i].second) next.push_back({load[i].first, load[i].second - take});
-            }
-            for (; i < load.size(); ++i) next.push_back(load[i]);
-            next.insert(next.end(), moved.begin(), moved.end());
-            std::sort(next.begin(), next.end());
-            load.clear();
-            for (const auto& e : next) {
-                if (!load.empty() && load.back().first == e.first)
-                    load.back().second += e.second;
-                else
-                    load.push_back(e);
+        int nl = 0;
+        while (need > 0) {
+            std::pop_heap(heap, heap + nb, later);
+            const Bucket low = heap[--nb];
+            const int64_t take = low.n < need ? low.n : need;
+            need -= take;
+            if (take < low.n) push(low.v, low.n - take);
+            const int64_t v = low.v + c;
+            if (nl > 0 && loaded[nl - 1].v == v)
+                loaded[nl - 1].n += take;
+            else if (nl < kMaxBuckets / 2)
+                loaded[nl++] = Bucket{v, take};
+            else
+                loaded[nl - 1] = Bucket{v, loaded[nl - 1].n + take};  // (fold: loads only grow)
+            finish = v > finish ? v : finish;
+            if (nb == 0 && need > 0) {  // more workgroups than CUs: the rest queue behind these
+                for (int j = 0; j < nl; ++j) push(loaded[j].v, loaded[j].n);
+                nl = 0;
             }
         }
+        for (int j = 0; j < nl; ++j) {
+            if (nb < kMaxBuckets)
+                push(loaded[j].v, loaded[j].n);
+            else  // keep the heap bounded: fold into the lowest bucket (an estimate)
+                heap[0].n += loaded[j].n;
+        }
     }
-    const int64_t finish = load.empty() ? 0 : load.back().first;
     return finish + (split ? kMergeCost : 0);
 }
 
 // The key chunk with the lowest estimated finish time among chunks that cut
-// the longest request into 1..64 equal parts, that give the CUs 1..32
-// rounds of equal work, and the smallest chunk (ties go to the larger
-// chunk: fewer partial outputs).
+// the longest request into 1 to 32 equal parts, that give the CUs 1 to 16
+// rounds of equal work (a spread of each), and the smallest chunk (ties go
+// to the larger chunk: fewer partial outputs).
 int64_t choose_chunk(const ddt_attn_desc* d, const int32_t* P, int row_tiles, int cus) {
+    int64_t T[DDT_MAX_BATCH];
     int64_t tmax = 0, work = 0;
     for (int b = 0; b < d->B; ++b) {
-        const int64_t T = (int64_t)P[b] + d->N;
-        tmax = T > tmax ? T : tmax;
-        work += T * row_tiles;
+        T[b] = (int64_t)P[b] + d->N;
+        tmax = T[b] > tmax ? T[b] : tmax;
+        work += T[b] * row_tiles;
     }
     const int64_t top = (int64_t)ddt::round_up((size_t)tmax, KT);
-    int64_t best = top, best_cost = plan_cost(d, P, row_tiles, top, cus);
+    int64_t best = top, best_cost = plan_cost(T, d->B, row_tiles, top, cus);
+    int64_t tried[64];
+    int nt = 0;
     auto consider = [&](int64_t c) {
         c = (int64_t)ddt::round_up((size_t)c, KT);
         if (c < kMinChunk) c = kMinChunk;
         if (c > top) c = top;
-        const int64_t cost = plan_cost(d, P, row_tiles, c, cus);
+        for (int i = 0; i < nt; ++i)
+            if (tried[i] == c) return;
+        if (nt < 64) tried[nt++] = c;
+        const int64_t cost = plan_cost(T, d->B, row_tiles, c, cus);
         if (cost < best_cost || (cost == best_cost && c > best)) best = c, best_cost = cost;
     };
     consider(kMinChunk);
-    for (int m = 2; m <= 64; ++m) consider((tmax + m - 1) / m);
-    for (int k = 1; k <= 32; ++k) consider((work + (int64_t)k * cus - 1) / ((int64_t)k * cus));
+    static const int kParts[] = {2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 14, 16, 20, 24, 28, 32};
+    for (const int m : kParts) consider((tmax + m - 1) / m);
+    static const int kRounds[] = {1, 2, 3, 4, 5, 6, 8, 10, 12, 16};
+    for (const int k : kRounds) consider((work + (int64_t)k * cus - 1) / ((int64_t)k * cus));
     return best;
 }
 

@@ -175,9 +175,10 @@ def _attn_args(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, H, scale, 
         lse = torch.empty((rows,), dtype=torch.float32, device=q_lat.device)
     _contig(out, q_lat.dtype, "out")
     _contig(lse, torch.float32, "lse")
-    need = verify_workspace_bytes(desc, pl)
-    if workspace is None and need > 0:
-        workspace = torch.empty((need,), dtype=torch.uint8, device=q_lat.device)
+    if workspace is None:  # (a caller's workspace is checked by the library)
+        need = verify_workspace_bytes(desc, pl)
+        if need > 0:
+            workspace = torch.empty((need,), dtype=torch.uint8, device=q_lat.device)
     ws_n = 0 if workspace is None else workspace.numel() * workspace.element_size()
     return desc, pl, out, lse, workspace, ws_n
 
