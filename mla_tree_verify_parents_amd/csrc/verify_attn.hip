@@ -273,6 +273,20 @@ __device__ inline void dma16(u32x4 rsrc, uint32_t lds, uint32_t voff) {
         : "m0");
 }
 
+// Touch 4 bytes per lane at rsrc + voff, delivered into LDS at `lds`
+// (64 lanes x 4 bytes of scratch): pulls the lines into L2 with no register
+// destination for the compiler to track.  Offsets outside the descriptor's
+// range read nothing.
+__device__ inline void l2_touch(u32x4 rsrc, uint32_t lds, uint32_t voff) {
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dword %0, %1, 0 offen lds"
+        :
+        : "v"(voff), "s"(rsrc), "s"(lds)
+        : "m0");
+}
+
 // An opaque (empty) redefinition of a register value.
 template <typename V>
 __device__ inline void pin_reg(V& v) {
@@ -671,6 +685,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         return;
     }
     __shared__ float s_mref[ROWS_WG];  // per-row softmax reference, for the log-sum-exp
+    __shared__ __attribute__((aligned(256))) char s_touch[256];  // landing area of the L2 touches
     __shared__ int s_redo;
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
@@ -903,6 +918,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         voff[i] = (uint32_t)(r * (ra ? ldA : ldB) + chunk * 16);
         pin_reg(voff[i]);
     }
+    // L2 touches of a tile: every 128-byte line of its rows (LA lines of
+    // c_kv, then LB of k_pe, per row), 64 lines per instruction, three
+    // instructions per value wavefront; wavefront grp's instruction k covers
+    // lines grp*64 + 128k ..; lines past the tile read nothing
+    constexpr int LA = (DL * (int)sizeof(T) + 127) / 128, LB = (DR * (int)sizeof(T) + 127) / 128;
+    constexpr int kTouch = 3;
+    static_assert(KT * (LA + LB) <= kTouch * 64 * S::NDW, "three touches per value wavefront cover a tile");
+    static_assert((KT * LA) % 64 == 0, "an instruction's lines lie in one region");
+    uint32_t toff[kTouch];
+#pragma unroll
+    for (int k = 0; k < kTouch; ++k) {
+        const int i = grp * 64 + lane + 128 * k, j = i - KT * LA;
+        toff[k] = i < KT * LA ? (uint32_t)((i / LA) * ldA + (i % LA) * 128)
+                              : (j < KT * LB ? (uint32_t)((j / LB) * ldB + (j % LB) * 128) : 0xFFFFFFF0u);
+        pin_reg(toff[k]);
+    }
     // per-tile descriptors of the two regions (rows [t0, min(t0 + KT, kend)))
     struct TileDma {
         u32x4 ra, rb;    // raw buffer descriptors of the tile's rows in c_kv / k_pe
@@ -957,24 +988,37 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             lsum[rb] = floatx16{};
         }
         mfma_settle();  // the zeroing writes above precede the first product
+        // every ring slot is free: the first NSTAGE tiles load at once, and
+        // the first phases wait only for their own tile (loads complete in
+        // issue order)
+        static_assert(NSTAGE == 4 && 3 * S::DPW <= 63, "prologue waits fit the vmcnt field");
         issue_tile(0);
-        wait_vmem_all();
+        issue_tile(1);
+        issue_tile(2);
+        issue_tile(3);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * S::DPW) : "memory");
         __syncthreads();  // tile 0 resident
-        issue_tile(1);    // phase 0: scores of tile 0
-        wait_vmem_all();
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * S::DPW) : "memory");  // phase 0: scores of tile 0
         __syncthreads();  // tile 1 resident
-        issue_tile(2);    // phase 1: scores of tile 1, softmax of tile 0
-        wait_vmem_all();
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(S::DPW) : "memory");  // phase 1: scores of tile 1, softmax of tile 0
         __syncthreads();  // tile 2 resident; probabilities of tile 0 published
         for (int it = 2; it <= ntiles + 1; ++it) {
             // phase it: O^T (this wavefront's columns x 64 rows) += V^T . P^T
             // for tile it-2: key step outer, column tile inner, row group
             // innermost (the two products of a fragment are independent);
             // value fragments run AV fragments ahead; the loads of tile it+1
-            // (into the slot of tile it-3) ride one per MFMA
+            // (into the slot of tile it-3) ride one per MFMA, then the L2
+            // touches of tile it+3, so its load two phases later finds it in
+            // L2 (one phase of lead is shorter than HBM latency under this
+            // load: measured 0.4 us of load wait per 1.2 us phase at 131072
+            // keys without the touches).  (In phase 2 the load reloads tile
+            // 3, already loaded by the prologue, with the same bytes: it
+            // keeps the loop free of branches.)
             const int tv = it - 2;
             const char* slot = smem + (tv % NSTAGE) * S::STAGE_BYTES;
             const TileDma d = tile_dma(it + 1);
+            const TileDma dt = tile_dma(it + 3);  // touched into L2 two phases before its load
+            const uint32_t touch_lds = lds_addr(s_touch);
             Frag pb[NGRP][S::NPS];
 #pragma unroll
             for (int rb = 0; rb < NGRP; ++rb) {
@@ -984,6 +1028,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                     pb[rb][j] = *reinterpret_cast<const Frag*>(pr + (j * 64 + lane) * (int)sizeof(Frag));
             }
             constexpr int NQ = NCH * S::NPS;  // fragments per tile
+            static_assert(S::DPW + kTouch <= NQ * NGRP, "loads and touches ride on distinct MFMAs");
             constexpr int AV = kValueAhead;
             Frag vf[AV + 1];
 #pragma unroll
@@ -998,12 +1043,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                     const int m = q * NGRP + rb;
                     Tr::mfma_acc(vf[q % (AV + 1)], pb[rb][q / NCH], o[rb][q % NCH]);
                     if (m < S::DPW) issue(d, m);
+                    if (m >= S::DPW && m < S::DPW + kTouch) {
+                        const int k = m - S::DPW;
+                        l2_touch(grp * 64 + 128 * k < KT * LA ? dt.ra : dt.rb, touch_lds, toff[k]);
+                    }
                     // row sums ride at the end of each key step
                     if (q % NCH == NCH - 1) lsum[rb] = Tr::mfma(ones, pb[rb][q / NCH], lsum[rb]);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
-            wait_vmem_all();
+            // tile it+1 landed (loads complete in issue order); this phase's
+            // kTouch touches may stay in flight
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kTouch) : "memory");
             __syncthreads();  // tile it+1 resident; tile it-2 and probabilities it-2 consumed
         }
         if (pass == 1 || s_redo == 0) break;
