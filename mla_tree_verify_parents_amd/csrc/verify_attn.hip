@@ -1008,16 +1008,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             // innermost (the two products of a fragment are independent);
             // value fragments run AV fragments ahead; the loads of tile it+1
             // (into the slot of tile it-3) ride one per MFMA, then the L2
-            // touches of tile it+3, so its load two phases later finds it in
+            // touches of tile it+2, so its load in the next phase finds it in
             // L2 (one phase of lead is shorter than HBM latency under this
             // load: measured 0.4 us of load wait per 1.2 us phase at 131072
-            // keys without the touches).  (In phase 2 the load reloads tile
+            // keys without the touches; touching two or three phases ahead
+            // measured 2 % slower).  (In phase 2 the load reloads tile
             // 3, already loaded by the prologue, with the same bytes: it
             // keeps the loop free of branches.)
             const int tv = it - 2;
             const char* slot = smem + (tv % NSTAGE) * S::STAGE_BYTES;
             const TileDma d = tile_dma(it + 1);
-            const TileDma dt = tile_dma(it + 3);  // touched into L2 two phases before its load
+            const TileDma dt = tile_dma(it + 2);  // touched into L2 one phase before its load
             const uint32_t touch_lds = lds_addr(s_touch);
             Frag pb[NGRP][S::NPS];
 #pragma unroll
