@@ -27,7 +27,7 @@ inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Remap a linear block id so that each XCD receives one contiguous range of
 // logical work items (blocks b, b+8, b+16, ... all land on XCD b % 8).
-__device__ inline int xcd_logical_block(int bid, int nblocks) {
+__host__ __device__ inline int xcd_logical_block(int bid, int nblocks) {
     const int xcd = bid % kXcds;
     const int j = bid / kXcds;
     const int q = nblocks / kXcds, r = nblocks % kXcds;

@@ -434,7 +434,7 @@ struct VerifyParams {
     int part_b[DDT_MAX_BATCH];           // request of the k-th last-split group
     int n_full_groups, n_units, unit_rows, units_per_group;
     int whole_blocks;  // blocks of the units dealt whole (a multiple of 8 units); the rest row by row
-    int touch;         // touch each tile into L2 a phase before its load (key stream larger than the LLC)
+    int single_round;  // at most one workgroup per CU: XCD x takes a contiguous range of work items
     // target argmax riding along in the same launch (workgroups n_attn ..)
     int n_attn;                 // attention workgroups (the rest are argmax workgroups)
     int am_wgs, am_dtype, am_vec;
@@ -650,6 +650,24 @@ struct Shape {
 // by row tile instead, so every XCD gets the same number of workgroups
 // (give or take one).
 __host__ __device__ inline bool work_item(const VerifyParams& p, int blk, int& b, int& split, int& rt) {
+    if (p.single_round) {
+        // one round: XCD x runs work items [x*n/8, (x+1)*n/8) in (request,
+        // split, row tile) order: neighbouring key splits and the row tiles
+        // of a split share the XCD (measured 0.9 us faster than the deal
+        // below at the K2-like head share)
+        const int wl = ddt::xcd_logical_block(blk, p.total_wg);
+        if (blk >= p.total_wg) return false;
+        int lo = 0, hi = p.B - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (p.wg_begin[mid] <= wl) lo = mid; else hi = mid - 1;
+        }
+        b = lo;
+        const int local = wl - p.wg_begin[b];
+        split = local / p.row_tiles;
+        rt = local - split * p.row_tiles;
+        return true;
+    }
     int u, r_in;
     if (blk < p.whole_blocks) {
         const int x = blk % ddt::kXcds, j = blk / ddt::kXcds;
@@ -681,7 +699,7 @@ __host__ __device__ inline bool work_item(const VerifyParams& p, int blk, int& b
     return true;
 }
 
-template <typename T, int DL, int DR, bool kArgmax>
+template <typename T, int DL, int DR, bool kArgmax, bool kTouch>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void verify_split(
     const VerifyParams p) {
     using S = Shape<T, DL, DR>;
@@ -936,12 +954,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     // instructions per value wavefront; wavefront grp's instruction k covers
     // lines grp*64 + 128k ..; lines past the tile read nothing
     constexpr int LA = (DL * (int)sizeof(T) + 127) / 128, LB = (DR * (int)sizeof(T) + 127) / 128;
-    constexpr int kTouch = 3;
-    static_assert(KT * (LA + LB) <= kTouch * 64 * S::NDW, "three touches per value wavefront cover a tile");
+    constexpr int kTouches = 3;
+    static_assert(KT * (LA + LB) <= kTouches * 64 * S::NDW, "three touches per value wavefront cover a tile");
     static_assert((KT * LA) % 64 == 0, "an instruction's lines lie in one region");
-    uint32_t toff[kTouch];
+    uint32_t toff[kTouches];
 #pragma unroll
-    for (int k = 0; k < kTouch; ++k) {
+    for (int k = 0; k < kTouches; ++k) {
         const int i = grp * 64 + lane + 128 * k, j = i - KT * LA;
         toff[k] = i < KT * LA ? (uint32_t)((i / LA) * ldA + (i % LA) * 128)
                               : (j < KT * LB ? (uint32_t)((j / LB) * ldB + (j % LB) * 128) : 0xFFFFFFF0u);
@@ -1001,19 +1019,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             lsum[rb] = floatx16{};
         }
         mfma_settle();  // the zeroing writes above precede the first product
-        // every ring slot is free: the first NSTAGE tiles load at once, and
-        // the first phases wait only for their own tile (loads complete in
-        // issue order)
-        static_assert(NSTAGE == 4 && 3 * S::DPW <= 63, "prologue waits fit the vmcnt field");
+        // (loading the first four tiles at once measured slower at the
+        // K2-like head share: the burst delays tile 0)
         issue_tile(0);
-        issue_tile(1);
-        issue_tile(2);
-        issue_tile(3);
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * S::DPW) : "memory");
+        wait_vmem_all();
         __syncthreads();  // tile 0 resident
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * S::DPW) : "memory");  // phase 0: scores of tile 0
+        issue_tile(1);    // phase 0: scores of tile 0
+        wait_vmem_all();
         __syncthreads();  // tile 1 resident
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(S::DPW) : "memory");  // phase 1: scores of tile 1, softmax of tile 0
+        issue_tile(2);    // phase 1: scores of tile 1, softmax of tile 0
+        wait_vmem_all();
         __syncthreads();  // tile 2 resident; probabilities of tile 0 published
         for (int it = 2; it <= ntiles + 1; ++it) {
             // phase it: O^T (this wavefront's columns x 64 rows) += V^T . P^T
@@ -1025,15 +1040,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             // L2 (one phase of lead is shorter than HBM latency under this
             // load: measured 0.4 us of load wait per 1.2 us phase at 131072
             // keys without the touches; touching two or three phases ahead
-            // measured 2 % slower).  (In phase 2 the load reloads tile
-            // 3, already loaded by the prologue, with the same bytes: it
-            // keeps the loop free of branches.)
+            // measured 2 % slower).  Without kTouch (key streams that stay in
+            // the last-level cache) the touches are not issued at all.
             const int tv = it - 2;
             const char* slot = smem + (tv % NSTAGE) * S::STAGE_BYTES;
             const TileDma d = tile_dma(it + 1);
-            // touched into L2 one phase before its load (an empty range, which
-            // reads nothing, when touches are off)
-            const TileDma dt = tile_dma(p.touch ? it + 2 : ntiles);
+            const TileDma dt = tile_dma(it + 2);  // touched into L2 one phase before its load
             const uint32_t touch_lds = lds_addr(s_touch);
             Frag pb[NGRP][S::NPS];
 #pragma unroll
@@ -1044,7 +1056,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                     pb[rb][j] = *reinterpret_cast<const Frag*>(pr + (j * 64 + lane) * (int)sizeof(Frag));
             }
             constexpr int NQ = NCH * S::NPS;  // fragments per tile
-            static_assert(S::DPW + kTouch <= NQ * NGRP, "loads and touches ride on distinct MFMAs");
+            static_assert(S::DPW + kTouches <= NQ * NGRP, "loads and touches ride on distinct MFMAs");
             constexpr int AV = kValueAhead;
             Frag vf[AV + 1];
 #pragma unroll
@@ -1059,7 +1071,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                     const int m = q * NGRP + rb;
                     Tr::mfma_acc(vf[q % (AV + 1)], pb[rb][q / NCH], o[rb][q % NCH]);
                     if (m < S::DPW) issue(d, m);
-                    if (m >= S::DPW && m < S::DPW + kTouch) {
+                    if (kTouch && m >= S::DPW && m < S::DPW + kTouches) {
                         const int k = m - S::DPW;
                         l2_touch(grp * 64 + 128 * k < KT * LA ? dt.ra : dt.rb, touch_lds, toff[k]);
                     }
@@ -1069,8 +1081,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 }
             }
             // tile it+1 landed (loads complete in issue order); this phase's
-            // kTouch touches may stay in flight
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kTouch) : "memory");
+            // touches may stay in flight
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kTouch ? kTouches : 0) : "memory");
             __syncthreads();  // tile it+1 resident; tile it-2 and probabilities it-2 consumed
         }
         if (pass == 1 || s_redo == 0) break;
@@ -1225,6 +1237,7 @@ int num_cus() {
 struct Plan {
     int row_tiles = 0, chunk = 0, total_wg = 0;
     int n_blocks = 0;  // attention blocks launched (work items plus padding of the XCD deal)
+    bool touch = false;  // the instance that touches tiles into L2
     bool any_split = false;
     size_t ws_bytes = 0, ws_lse_off = 0;
 };
@@ -1403,7 +1416,14 @@ Plan make_plan(const ddt_attn_desc* d, const int32_t* P, VerifyParams* vp) {
     const int64_t whole = n_units / ddt::kXcds * ddt::kXcds * unit_rows;
     const int64_t rest = (n_units % ddt::kXcds) * unit_rows;
     const int64_t blocks = whole + (rest + ddt::kXcds - 1) / ddt::kXcds * ddt::kXcds;
-    pl.n_blocks = blocks > 0x7fffffff ? 0x7fffffff : (int)blocks;
+    pl.n_blocks = pl.total_wg <= cus ? pl.total_wg : (blocks > 0x7fffffff ? 0x7fffffff : (int)blocks);
+    // L2 touches pay off once the launch's key stream outgrows the
+    // last-level cache (measured: +12 to +16 % at 318 MB to 1.45 GB,
+    // neutral at 151 MB, a loss at 5 MB where the keys stay cached)
+    int64_t key_bytes = 0;
+    for (int b = 0; b < d->B; ++b)
+        key_bytes += ((int64_t)P[b] + d->N) * (d->d_lat + d->d_rope) * ddt::elem_bytes(d->dtype);
+    pl.touch = key_bytes > kTouchMinBytes;
     if (vp) {
         vp->wg_begin[d->B] = pl.total_wg;
         vp->full_gbegin[d->B] = n_full;
@@ -1411,13 +1431,7 @@ Plan make_plan(const ddt_attn_desc* d, const int32_t* P, VerifyParams* vp) {
         vp->n_full_groups = n_full;
         vp->n_units = (int)n_units;
         vp->whole_blocks = (int)whole;
-        // L2 touches pay off once the launch's key stream outgrows the
-        // last-level cache (measured: +12 to +16 % at 318 MB to 1.45 GB,
-        // neutral at 151 MB, a loss at 5 MB where the keys stay cached)
-        int64_t key_bytes = 0;
-        for (int b = 0; b < d->B; ++b)
-            key_bytes += ((int64_t)P[b] + d->N) * (d->d_lat + d->d_rope) * ddt::elem_bytes(d->dtype);
-        vp->touch = key_bytes > kTouchMinBytes ? 1 : 0;
+        vp->single_round = pl.total_wg <= cus ? 1 : 0;
         vp->unit_rows = unit_rows;
         vp->units_per_group = upg;
     }
@@ -1431,11 +1445,18 @@ Plan make_plan(const ddt_attn_desc* d, const int32_t* P, VerifyParams* vp) {
 
 template <typename T, int DL, int DR>
 int launch(const VerifyParams& vp, const Plan& pl, int n_argmax, hipStream_t stream) {
-    if (n_argmax > 0)
-        hipLaunchKernelGGL((verify_split<T, DL, DR, true>), dim3(pl.n_blocks + n_argmax), dim3(kThreads), 0, stream,
-                           vp);
-    else
-        hipLaunchKernelGGL((verify_split<T, DL, DR, false>), dim3(pl.n_blocks), dim3(kThreads), 0, stream, vp);
+    const dim3 grid(pl.n_blocks + n_argmax);
+    if (n_argmax > 0) {
+        if (pl.touch)
+            hipLaunchKernelGGL((verify_split<T, DL, DR, true, true>), grid, dim3(kThreads), 0, stream, vp);
+        else
+            hipLaunchKernelGGL((verify_split<T, DL, DR, true, false>), grid, dim3(kThreads), 0, stream, vp);
+    } else {
+        if (pl.touch)
+            hipLaunchKernelGGL((verify_split<T, DL, DR, false, true>), grid, dim3(kThreads), 0, stream, vp);
+        else
+            hipLaunchKernelGGL((verify_split<T, DL, DR, false, false>), grid, dim3(kThreads), 0, stream, vp);
+    }
     DDT_CHECK_LAUNCH();
     const int nblk = pl.any_split ? vp.B * pl.row_tiles * NW * (DL / 64) : 0;
     if (vp.n_accept > 0) {
