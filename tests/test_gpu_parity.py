@@ -399,6 +399,29 @@ def test_attn_config3_full_sampled(orc):
     _attn_check(orc, w, rows=rows)
 
 
+def test_attn_config4_full_sampled(orc):
+    """The long-context configuration (4 x 131072 keys, 64 heads, 128 nodes):
+    several rounds of workgroups dealt in units of row tiles across the
+    XCDs, tiles touched into L2 before their loads; 48 sampled rows."""
+    w = synth.workload(4)
+    rng = np.random.default_rng(4)
+    rows = np.sort(rng.choice(w.rows, 48, replace=False))
+    _attn_check(orc, w, rows=rows)
+
+
+@pytest.mark.parametrize("cfg,over", [
+    (3, dict(B=2, H=64, N=128, prefix_range=(20000, 45000))),  # whole-chunk splits in rounds, then shorter last splits
+    (4, dict(B=3, H=16, N=96, prefix=9000)),                   # row tiles not a multiple of the unit
+])
+def test_attn_multi_round_sampled(orc, cfg, over):
+    """Launches of several rounds: whole-chunk work items dealt to the XCDs
+    in units of row tiles, the shorter last splits after them."""
+    w = synth.workload(cfg, **over)
+    rng = np.random.default_rng(w.B * 7 + w.N)
+    rows = np.sort(rng.choice(w.rows, 64, replace=False))
+    _attn_check(orc, w, rows=rows)
+
+
 @pytest.mark.parametrize("factor", [100.0, 1e4])
 def test_attn_large_score_range(orc, factor):
     """Some cache rows far into each request scaled up so their scores exceed
