@@ -293,6 +293,110 @@ int orc_compact_kv(void* ckv, int64_t ld_ckv, void* kpe, int64_t ld_kpe, int dty
     return 0;
 }
 
+/*
+ * Per-depth draft candidates ([P1] "The Knowledge Architecture": the tree
+ * builder takes the drafter's per-depth top-k candidates).  For each row r
+ * of fp32 draft logits (row stride ld): ids[r][0..K) are the K largest
+ * entries in order of value (descending), equal values by index
+ * (ascending); logp[r][k] = x[ids[r][k]] - lse, the log-softmax over the
+ * whole row, lse = m + ln(sum_v exp(x_v - m)) with m the row maximum, in
+ * fp64.  Selection k is the largest entry that comes after selection k-1 in
+ * that order, found by a left-to-right scan.  Finite logits, 1 <= K <= V.
+ */
+int orc_draft_topk(const float* logits, int64_t rows, int64_t V, int64_t ld, int K, int32_t* ids,
+                   double* logp) {
+    if (!logits || !ids || !logp || rows < 0 || V < 1 || ld < V || K < 1 || K > V) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        const float* x = logits + r * ld;
+        double m = x[0];
+        for (int64_t v = 1; v < V; ++v)
+            if (x[v] > m) m = x[v];
+        double s = 0.0;
+        for (int64_t v = 0; v < V; ++v) s += exp((double)x[v] - m);
+        const double lse = m + log(s);
+        int64_t prev = -1;
+        for (int k = 0; k < K; ++k) {
+            int64_t best = -1;
+            for (int64_t v = 0; v < V; ++v) {
+                /* only entries after the previous selection in (value desc, index asc) order */
+                if (prev >= 0 && !(x[v] < x[prev] || (x[v] == x[prev] && v > prev))) continue;
+                if (best < 0 || x[v] > x[best]) best = v;
+            }
+            ids[r * K + k] = (int32_t)best;
+            logp[r * K + k] = (double)x[best] - lse;
+            prev = best;
+        }
+    }
+    return 0;
+}
+
+/*
+ * Best-first draft tree ([P1] "The Knowledge Architecture": a best-first
+ * tree from the drafter's per-depth top-k; [P2] "The Context: Building an
+ * Engine from First Principles": the GPU builder replaced a per-request
+ * heap on the CPU).  Candidates: the token of rank r at depth d (ids[d-1][r],
+ * log-probability lp[d-1][r]) under a node at depth d-1.  A node's score is
+ * its parent's plus its own lp, an fp32 addition (the root scores 0).  The
+ * frontier starts with (depth 1, rank 0) under the root; repeatedly the
+ * frontier candidate with the highest score (then the lower depth, then the
+ * earlier insertion) becomes the next node, and its first child (depth
+ * d+1, rank 0; if d < D) and next sibling (depth d, rank r+1; if r+1 < K)
+ * enter the frontier, in that order.  budget+1 nodes result, numbered in
+ * that order: parents[i] < i, tokens[0] = root, depth[0] = 0.  Returns -2
+ * when the candidates run out first.
+ */
+int orc_best_first_tree(const int32_t* ids, const float* lp, int D, int K, int budget, int32_t root,
+                        int32_t* parents, int32_t* tokens, int32_t* depth) {
+    if (!ids || !lp || !parents || !tokens || !depth || D < 0 || K < 0 || budget < 0) return -1;
+    int cap = 2 * budget + 2;
+    float* fs = (float*)malloc(sizeof(float) * cap);
+    int* fd = (int*)malloc(sizeof(int) * cap);
+    int* fr = (int*)malloc(sizeof(int) * cap);
+    int* fp = (int*)malloc(sizeof(int) * cap);
+    long* fq = (long*)malloc(sizeof(long) * cap);
+    float* ns = (float*)malloc(sizeof(float) * (budget + 1));
+    if (!fs || !fd || !fr || !fp || !fq || !ns) {
+        free(fs); free(fd); free(fr); free(fp); free(fq); free(ns);
+        return 2;
+    }
+    int nf = 0;
+    long seq = 0;
+    parents[0] = -1;
+    tokens[0] = root;
+    depth[0] = 0;
+    ns[0] = 0.0f;
+    if (budget > 0 && D > 0 && K > 0) {
+        fs[nf] = ns[0] + lp[0]; fd[nf] = 1; fr[nf] = 0; fp[nf] = 0; fq[nf] = seq++; ++nf;
+    }
+    int n = 1, rc = 0;
+    while (n < budget + 1) {
+        if (nf == 0) { rc = -2; break; }
+        int best = 0;
+        for (int i = 1; i < nf; ++i) {
+            if (fs[i] > fs[best] || (fs[i] == fs[best] && (fd[i] < fd[best] || (fd[i] == fd[best] && fq[i] < fq[best]))))
+                best = i;
+        }
+        const float sc = fs[best];
+        const int d = fd[best], r = fr[best], par = fp[best];
+        --nf;  /* remove: the last candidate takes its place */
+        fs[best] = fs[nf]; fd[best] = fd[nf]; fr[best] = fr[nf]; fp[best] = fp[nf]; fq[best] = fq[nf];
+        parents[n] = par;
+        tokens[n] = ids[(d - 1) * K + r];
+        depth[n] = d;
+        ns[n] = sc;
+        if (d < D) {
+            fs[nf] = ns[n] + lp[d * K]; fd[nf] = d + 1; fr[nf] = 0; fp[nf] = n; fq[nf] = seq++; ++nf;
+        }
+        if (r + 1 < K) {
+            fs[nf] = ns[par] + lp[(d - 1) * K + r + 1]; fd[nf] = d; fr[nf] = r + 1; fp[nf] = par; fq[nf] = seq++; ++nf;
+        }
+        ++n;
+    }
+    free(fs); free(fd); free(fr); free(fp); free(fq); free(ns);
+    return rc;
+}
+
 /* Number of OpenMP threads the oracle runs with (for reporting). */
 int orc_num_threads(void) {
 #ifdef _OPENMP

@@ -52,8 +52,10 @@ def lib():
         L.orc_greedy_accept.argtypes = [P, P, P, i32, i32, P, P, P]
         L.orc_compact_kv.argtypes = [P, i64, P, i64, i32, i32, i32, P, P, P, P, i32, i32, P]
         L.orc_num_threads.argtypes = []
+        L.orc_draft_topk.argtypes = [P, i64, i64, i64, i32, P, P]
+        L.orc_best_first_tree.argtypes = [P, P, i32, i32, i32, i32, P, P, P]
         for f in (L.orc_build_mask, L.orc_verify_attn, L.orc_argmax, L.orc_greedy_accept,
-                  L.orc_compact_kv, L.orc_num_threads):
+                  L.orc_compact_kv, L.orc_num_threads, L.orc_draft_topk, L.orc_best_first_tree):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -177,3 +179,29 @@ def compact_kv(ckv, kpe, kv_base, prefix_len, path, accept_len):
     if rc != 0:
         raise RuntimeError(f"orc_compact_kv failed: {rc}")
     return pl, src
+
+
+def draft_topk(logits: np.ndarray, K: int):
+    """fp32 draft logits [rows, V] (row view) -> (ids [rows, K] int32, logp [rows, K] float64)."""
+    assert logits.dtype == np.float32
+    rows, V = logits.shape
+    ids = np.zeros((rows, K), np.int32)
+    logp = np.zeros((rows, K), np.float64)
+    rc = lib().orc_draft_topk(_ptr(logits), rows, V, _ld(logits), K, _ptr(ids), _ptr(logp))
+    if rc != 0:
+        raise RuntimeError(f"orc_draft_topk failed: {rc}")
+    return ids, logp
+
+
+def best_first_tree(ids: np.ndarray, lp: np.ndarray, budget: int, root: int):
+    """ids [D, K] int32, lp [D, K] float32 -> (parents, tokens, depth) [budget+1] int32."""
+    ids = _c(ids, np.int32)
+    lp = _c(lp, np.float32)
+    D, K = ids.shape
+    par = np.zeros(budget + 1, np.int32)
+    tok = np.zeros(budget + 1, np.int32)
+    dep = np.zeros(budget + 1, np.int32)
+    rc = lib().orc_best_first_tree(_ptr(ids), _ptr(lp), D, K, budget, int(root), _ptr(par), _ptr(tok), _ptr(dep))
+    if rc != 0:
+        raise RuntimeError(f"orc_best_first_tree failed: {rc}")
+    return par, tok, dep
