@@ -156,6 +156,46 @@ int ddt_argmax(const void* logits, int dtype, int64_t rows, int64_t V, int64_t l
                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Per-depth draft candidates.  [Ambition], section "The Knowledge
+ * Architecture": the tree builder takes the drafter's per-depth top-k.
+ * For each row r of fp32 draft logits (row at logits + r*ld, V entries):
+ *   ids[r][0..K)  = the K largest entries, by value (descending), equal
+ *                   values by index (ascending)                   int32
+ *   logp[r][k]    = logits[r][ids[r][k]] - lse(row), the log-softmax over
+ *                   the whole row, computed in fp32 (|error| < 1e-4 at
+ *                   V = 163840 against fp64)                     fp32
+ * Finite logits; 1 <= K <= 16, K <= V <= 2^20, ld >= V.
+ * Workspace: ddt_draft_topk_workspace bytes (16-byte aligned), scratch
+ * between the two launches (no zeroing needed).
+ */
+int ddt_draft_topk_workspace(int64_t rows, int64_t V, int K, size_t* bytes);
+int ddt_draft_topk(const float* logits, int64_t rows, int64_t V, int64_t ld, int K, int32_t* ids, float* logp,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Best-first draft tree.  [Ambition], section "The Knowledge Architecture"
+ * (a best-first tree from the drafter's per-depth top-k); [Keystone],
+ * section "The Context: Building an Engine from First Principles" (a GPU
+ * builder in place of a per-request heap on the CPU).  Per request b,
+ * candidates: the token of rank r at depth d is ids[b][d-1][r] with
+ * log-probability logp[b][d-1][r] (ddt_draft_topk's layout with rows
+ * b*D + d-1).  A node's score is its parent's plus its own log-probability
+ * (an fp32 addition; the root, root_tokens[b], scores 0).  The frontier
+ * starts with (depth 1, rank 0) under the root; repeatedly the frontier
+ * candidate with the highest score (then the lower depth, then the earlier
+ * insertion) becomes the next node, and its first child (depth d+1, rank 0;
+ * if d < D) and next sibling (depth d, rank r+1; if r+1 < K) enter the
+ * frontier, in that order.  Outputs [B][budget+1] int32, nodes numbered in
+ * that order: parents (root -1, parents[i] < i), tokens (root first),
+ * depth.  1 <= D <= 255, 1 <= K, D*K <= 4096, 0 <= budget < DDT_MAX_NODES,
+ * and the candidates must suffice (sum of K^d over d = 1..D >= budget):
+ * otherwise DDT_EINVAL.  One wavefront per request.
+ */
+int ddt_best_first_tree(const int32_t* ids, const float* logp, int B, int D, int K, int budget,
+                        const int32_t* root_tokens, int32_t* parents, int32_t* tokens, int32_t* depth,
+                        hipStream_t stream);
+
+/*
  * Tree-verify attention and target argmax in one launch: the results of
  * ddt_verify_attn and of ddt_argmax (same arguments, same outputs, same
  * workspace contracts).  The two are independent; the argmax runs as extra

@@ -1,0 +1,328 @@
+// The step before the verify path: the drafter's per-depth top-k candidates
+// and the best-first draft tree built from them ("The Architecture of
+// Pragmatic Ambition", section "The Knowledge Architecture": the tree
+// builder takes per-depth top-k candidates from a drafter and builds a
+// best-first tree; "The Architectural Keystone: Writing the Model Header
+// ...", section "The Context: Building an Engine from First Principles":
+// the GPU builder replaced a per-request heap on the CPU).
+//
+// ddt_draft_topk: a row of draft logits is cut into chunks of 4096 entries,
+// 16 contiguous entries per thread.  A chunk workgroup keeps each thread's
+// 16 entries in registers and takes the chunk's top K in K rounds of a
+// workgroup maximum over 64-bit keys (order-preserving value bits, then
+// the inverted index: the largest key is the largest value at the lowest
+// index); the round's owner thread marks its entry taken.  It also reduces
+// the chunk's (maximum, sum of exp(x - maximum)).  A second launch, one
+// workgroup per row, runs the same K-round selection over the chunks'
+// candidates and merges the (maximum, sum) pairs into the row's
+// log-sum-exp.  HBM-bound: 4 bytes per logit.
+//
+// ddt_best_first_tree: one wavefront per request.  The frontier lives in
+// LDS; each pop is a wavefront maximum over packed keys (score, then lower
+// depth, then earlier insertion), then one lane writes the node and inserts
+// the first child and the next sibling.  Scores are fp32 sums along the
+// path, as the tree's definition fixes them.
+#include "argmax_scan.h"
+#include "common.h"
+
+namespace {
+
+constexpr int kTopkThreads = 256;
+constexpr int kPerThread = 16;                               // entries (or candidates) per thread
+constexpr int kTopkChunk = kTopkThreads * kPerThread;        // 4096 entries per chunk workgroup
+constexpr int kMaxTopK = 16;
+constexpr int64_t kMaxDraftVocab = (int64_t)kTopkChunk * kTopkThreads * kPerThread / kMaxTopK;  // 2^20
+
+__device__ inline uint64_t umax(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// Workgroup maximum of one 64-bit key per thread, returned to every thread.
+__device__ inline uint64_t block_max_all(uint64_t v, uint64_t* red) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = umax(v, __shfl_xor(v, o, ddt::kWave));
+    const int wave = threadIdx.x / ddt::kWave;
+    __syncthreads();  // the previous round's readers are done with red[]
+    if ((threadIdx.x & 63) == 0) red[wave] = v;
+    __syncthreads();
+    uint64_t m = red[0];
+#pragma unroll
+    for (int w = 1; w < kTopkThreads / ddt::kWave; ++w) m = umax(m, red[w]);
+    return m;
+}
+
+// The K largest keys among every thread's kPerThread keys (0 = empty), in
+// descending order, into out[0..K) (thread 0 writes).  Keys are distinct.
+__device__ inline void select_top(uint64_t (&key)[kPerThread], int K, uint64_t* out, uint64_t* red) {
+    uint32_t taken = 0;
+    auto best = [&]() {
+        uint64_t b = 0;
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i) b = ((taken >> i) & 1u) ? b : umax(b, key[i]);
+        return b;
+    };
+    uint64_t cand = best();
+    for (int k = 0; k < K; ++k) {
+        const uint64_t m = block_max_all(cand, red);
+        if (threadIdx.x == 0) out[k] = m;
+        if (m != 0 && cand == m) {  // this thread owns the winner: take it
+#pragma unroll
+            for (int i = 0; i < kPerThread; ++i)
+                if (key[i] == m) taken |= 1u << i;
+            cand = best();
+        }
+    }
+}
+
+// Chunk c of row r: top-K keys and (max, sum exp(x - max)) into the workspace.
+__global__ __launch_bounds__(kTopkThreads) void topk_chunks(const float* __restrict__ logits, int64_t V, int64_t ld,
+                                                           int nchunk, int K, bool vec, uint64_t* __restrict__ ws_keys,
+                                                           float2* __restrict__ ws_ms) {
+    __shared__ uint64_t red[kTopkThreads / ddt::kWave];
+    __shared__ float2 red_ms[kTopkThreads / ddt::kWave];
+    const int64_t r = blockIdx.x / nchunk;
+    const int c = (int)(blockIdx.x - r * nchunk);
+    const float* row = logits + r * ld;
+    const int64_t e0 = (int64_t)c * kTopkChunk + (int64_t)threadIdx.x * kPerThread;
+    float x[kPerThread];
+    if (vec && e0 + kPerThread <= V) {
+        typedef float F4 __attribute__((ext_vector_type(4)));
+        const F4* p = reinterpret_cast<const F4*>(row + e0);
+#pragma unroll
+        for (int q = 0; q < kPerThread / 4; ++q) {
+            const F4 v = __builtin_nontemporal_load(p + q);
+            x[4 * q] = v.x, x[4 * q + 1] = v.y, x[4 * q + 2] = v.z, x[4 * q + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i) x[i] = e0 + i < V ? row[e0 + i] : -INFINITY;
+    }
+    uint64_t key[kPerThread];
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+        const bool ok = e0 + i < V;
+        key[i] = ok ? ddt::pack_key(__float_as_uint(x[i]), e0 + i) : 0;
+        m = ok ? fmaxf(m, x[i]) : m;
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) s += e0 + i < V ? __expf(x[i] - m) : 0.f;
+    // chunk (max, sum): wavefront then workgroup
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float mo = __shfl_xor(m, o, ddt::kWave), so = __shfl_xor(s, o, ddt::kWave);
+        const float mn = fmaxf(m, mo);
+        s = (m == -INFINITY ? 0.f : s * __expf(m - mn)) + (mo == -INFINITY ? 0.f : so * __expf(mo - mn));
+        m = mn;
+    }
+    const int wave = threadIdx.x / ddt::kWave;
+    if ((threadIdx.x & 63) == 0) red_ms[wave] = make_float2(m, s);
+    __shared__ uint64_t out[kMaxTopK];
+    select_top(key, K, out, red);  // (its barriers also publish red_ms)
+    if (threadIdx.x == 0) {
+        float M = red_ms[0].x, S = red_ms[0].y;
+        for (int w = 1; w < kTopkThreads / ddt::kWave; ++w) {
+            const float mw = red_ms[w].x, sw = red_ms[w].y;
+            const float mn = fmaxf(M, mw);
+            S = (M == -INFINITY ? 0.f : S * __expf(M - mn)) + (mw == -INFINITY ? 0.f : sw * __expf(mw - mn));
+            M = mn;
+        }
+        ws_ms[blockIdx.x] = make_float2(M, S);
+        for (int k = 0; k < K; ++k) ws_keys[(int64_t)blockIdx.x * K + k] = out[k];
+    }
+}
+
+// Row r: top K among its chunks' candidates, then the log-softmax values.
+__global__ __launch_bounds__(kTopkThreads) void topk_merge(const float* __restrict__ logits, int64_t ld, int nchunk,
+                                                          int K, const uint64_t* __restrict__ ws_keys,
+                                                          const float2* __restrict__ ws_ms, int32_t* __restrict__ ids,
+                                                          float* __restrict__ logp) {
+    __shared__ uint64_t red[kTopkThreads / ddt::kWave];
+    __shared__ uint64_t out[kMaxTopK];
+    __shared__ float s_lse;
+    const int64_t r = blockIdx.x;
+    const int n = nchunk * K;  // candidates of the row (at most kTopkThreads * kPerThread)
+    const uint64_t* cand = ws_keys + r * n;
+    uint64_t key[kPerThread];
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+        const int j = threadIdx.x * kPerThread + i;
+        key[i] = j < n ? cand[j] : 0;
+    }
+    if (threadIdx.x < ddt::kWave) {
+        // the row's log-sum-exp from the chunks' (max, sum) pairs
+        float m = -INFINITY, s = 0.f;
+        for (int c = threadIdx.x; c < nchunk; c += ddt::kWave) {
+            const float2 p = ws_ms[r * nchunk + c];
+            const float mn = fmaxf(m, p.x);
+            s = (m == -INFINITY ? 0.f : s * __expf(m - mn)) + (p.x == -INFINITY ? 0.f : p.y * __expf(p.x - mn));
+            m = mn;
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            const float mo = __shfl_xor(m, o, ddt::kWave), so = __shfl_xor(s, o, ddt::kWave);
+            const float mn = fmaxf(m, mo);
+            s = (m == -INFINITY ? 0.f : s * __expf(m - mn)) + (mo == -INFINITY ? 0.f : so * __expf(mo - mn));
+            m = mn;
+        }
+        if (threadIdx.x == 0) s_lse = m + __logf(s);
+    }
+    select_top(key, K, out, red);
+    if (threadIdx.x < K) {
+        const uint64_t k = out[threadIdx.x];
+        const int32_t id = (int32_t)(0xffffffffu - (uint32_t)k);
+        ids[r * K + threadIdx.x] = id;
+        logp[r * K + threadIdx.x] = logits[r * ld + id] - s_lse;
+    }
+}
+
+// ---------------------------------------------------------------- tree ----
+
+constexpr int kTreeMaxDK = 4096;  // D * K candidates per request, staged in LDS
+
+// Frontier key: score (order-preserving bits), then lower depth, then
+// earlier insertion: the largest key goes next.
+__device__ inline uint64_t frontier_key(float score, int d, int seq) {
+    return ((uint64_t)ddt::order_key(__float_as_uint(score)) << 32) | ((uint64_t)(255 - d) << 24) |
+           (uint64_t)(0xffffff - seq);
+}
+
+__global__ __launch_bounds__(64) void best_first_kernel(const int32_t* __restrict__ ids, const float* __restrict__ lp,
+                                                       int D, int K, int budget, const int32_t* __restrict__ roots,
+                                                       int32_t* __restrict__ parents, int32_t* __restrict__ tokens,
+                                                       int32_t* __restrict__ depth) {
+    __shared__ float s_lp[kTreeMaxDK];
+    __shared__ int32_t s_id[kTreeMaxDK];
+    __shared__ float f_score[DDT_MAX_NODES];
+    __shared__ int32_t f_dr[DDT_MAX_NODES];   // depth << 16 | rank
+    __shared__ int32_t f_par[DDT_MAX_NODES];
+    __shared__ int32_t f_seq[DDT_MAX_NODES];
+    __shared__ float n_score[DDT_MAX_NODES];
+    const int b = blockIdx.x, lane = threadIdx.x;
+    const int DK = D * K;
+    for (int i = lane; i < DK; i += 64) {
+        s_lp[i] = lp[(int64_t)b * DK + i];
+        s_id[i] = ids[(int64_t)b * DK + i];
+    }
+    const int64_t o = (int64_t)b * (budget + 1);
+    int nf = 0, seq = 0;
+    if (lane == 0) {
+        parents[o] = -1;
+        tokens[o] = roots[b];
+        depth[o] = 0;
+        n_score[0] = 0.f;
+    }
+    __syncthreads();
+    if (budget > 0) {
+        if (lane == 0) {
+            f_score[0] = 0.f + s_lp[0];
+            f_dr[0] = 1 << 16;
+            f_par[0] = 0;
+            f_seq[0] = 0;
+        }
+        nf = 1;
+        seq = 1;
+    }
+    for (int n = 1; n <= budget; ++n) {
+        __syncthreads();  // (one wavefront: orders the LDS writes of the previous pop)
+        // the best frontier entry: each lane scans a stride, then a wavefront maximum
+        uint64_t best = 0;
+        int at = -1;
+        for (int i = lane; i < nf; i += 64) {
+            const int dr = f_dr[i];
+            const uint64_t k = frontier_key(f_score[i], dr >> 16, f_seq[i]);
+            if (k > best) best = k, at = i;
+        }
+        uint64_t m = best;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) m = umax(m, __shfl_xor(m, off, 64));
+        const uint64_t win = __ballot(best == m && at >= 0);
+        if (win == 0) break;  // (cannot happen: the host checked that the candidates suffice)
+        const int i = __shfl(at, __builtin_ctzll(win), 64);
+        // the popped entry, read by every lane before lane 0 rewrites the frontier
+        const float sc = f_score[i];
+        const int dr = f_dr[i], d = dr >> 16, r = dr & 0xffff, par = f_par[i];
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the reads above have completed
+        if (lane == 0) {
+            const int last = nf - 1;  // the last entry takes the popped one's place
+            f_score[i] = f_score[last];
+            f_dr[i] = f_dr[last];
+            f_par[i] = f_par[last];
+            f_seq[i] = f_seq[last];
+            int nn = last;
+            parents[o + n] = par;
+            tokens[o + n] = s_id[(d - 1) * K + r];
+            depth[o + n] = d;
+            n_score[n] = sc;
+            if (d < D) {  // first child
+                f_score[nn] = sc + s_lp[d * K];
+                f_dr[nn] = (d + 1) << 16;
+                f_par[nn] = n;
+                f_seq[nn] = seq;
+                ++nn;
+            }
+            if (r + 1 < K) {  // next sibling
+                f_score[nn] = n_score[par] + s_lp[(d - 1) * K + r + 1];
+                f_dr[nn] = (d << 16) | (r + 1);
+                f_par[nn] = par;
+                f_seq[nn] = seq + 1;
+                ++nn;
+            }
+        }
+        // every lane keeps the same count: one popped, up to two inserted
+        nf = nf - 1 + (d < D ? 1 : 0) + (r + 1 < K ? 1 : 0);
+        seq += 2;
+    }
+}
+
+}  // namespace
+
+extern "C" int ddt_draft_topk_workspace(int64_t rows, int64_t V, int K, size_t* bytes) {
+    if (bytes == nullptr || rows < 0 || V < 1 || V > kMaxDraftVocab || K < 1 || K > kMaxTopK || K > V)
+        return DDT_EINVAL;
+    const int64_t nchunk = (V + kTopkChunk - 1) / kTopkChunk;
+    *bytes = (size_t)rows * nchunk * (K * sizeof(uint64_t) + sizeof(float2));
+    return DDT_OK;
+}
+
+extern "C" int ddt_draft_topk(const float* logits, int64_t rows, int64_t V, int64_t ld, int K, int32_t* ids,
+                              float* logp, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    size_t need = 0;
+    const int rc = ddt_draft_topk_workspace(rows, V, K, &need);
+    if (rc != DDT_OK || ld < V) return DDT_EINVAL;
+    if (rows == 0) return DDT_OK;
+    if (!logits || !ids || !logp) return DDT_EINVAL;
+    const int64_t nchunk = (V + kTopkChunk - 1) / kTopkChunk;
+    if (rows * nchunk > 0x7fffffff) return DDT_EINVAL;
+    if (workspace == nullptr || workspace_bytes < need || !ddt::aligned(workspace, 16)) return DDT_EWORKSPACE;
+    uint64_t* keys = static_cast<uint64_t*>(workspace);
+    float2* ms = reinterpret_cast<float2*>(keys + rows * nchunk * K);
+    const bool vec = ddt::aligned(logits, 16) && (ld * 4) % 16 == 0;
+    hipLaunchKernelGGL(topk_chunks, dim3((unsigned)(rows * nchunk)), dim3(kTopkThreads), 0, stream, logits, V, ld,
+                       (int)nchunk, K, vec, keys, ms);
+    DDT_CHECK_LAUNCH();
+    hipLaunchKernelGGL(topk_merge, dim3((unsigned)rows), dim3(kTopkThreads), 0, stream, logits, ld, (int)nchunk, K,
+                       keys, ms, ids, logp);
+    DDT_CHECK_LAUNCH();
+    return DDT_OK;
+}
+
+extern "C" int ddt_best_first_tree(const int32_t* ids, const float* logp, int B, int D, int K, int budget,
+                                   const int32_t* root_tokens, int32_t* parents, int32_t* tokens, int32_t* depth,
+                                   hipStream_t stream) {
+    if (B < 0 || D < 1 || K < 1 || budget < 0 || budget + 1 > DDT_MAX_NODES || D > 255 || K > 0xffff ||
+        (int64_t)D * K > kTreeMaxDK)
+        return DDT_EINVAL;
+    // enough candidates: sum over d = 1..D of K^d >= budget
+    int64_t avail = 0, level = 1;
+    for (int d = 1; d <= D && avail < budget; ++d) {
+        level = level * K > budget ? budget + 1 : level * K;
+        avail += level;
+    }
+    if (avail < budget) return DDT_EINVAL;
+    if (B == 0) return DDT_OK;
+    if (!ids || !logp || !root_tokens || !parents || !tokens || !depth) return DDT_EINVAL;
+    hipLaunchKernelGGL(best_first_kernel, dim3(B), dim3(64), 0, stream, ids, logp, D, K, budget, root_tokens,
+                       parents, tokens, depth);
+    DDT_CHECK_LAUNCH();
+    return DDT_OK;
+}

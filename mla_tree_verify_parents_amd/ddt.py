@@ -70,9 +70,13 @@ def lib():
                                              ctypes.POINTER(ArgmaxTask), P]
         L.ddt_verify_step.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P, P, P, P, sz,
                                       ctypes.POINTER(ArgmaxTask), ctypes.POINTER(AcceptTask), P]
+        L.ddt_draft_topk_workspace.argtypes = [i64, i64, i32, ctypes.POINTER(sz)]
+        L.ddt_draft_topk.argtypes = [P, i64, i64, i64, i32, P, P, P, sz, P]
+        L.ddt_best_first_tree.argtypes = [P, P, i32, i32, i32, i32, P, P, P, P, P]
         for f in ("ddt_version", "ddt_build_mask", "ddt_verify_workspace", "ddt_verify_attn",
                   "ddt_argmax_workspace", "ddt_argmax", "ddt_greedy_accept", "ddt_compact_kv",
-                  "ddt_accept_compact", "ddt_verify_attn_argmax", "ddt_verify_step"):
+                  "ddt_accept_compact", "ddt_verify_attn_argmax", "ddt_verify_step",
+                  "ddt_draft_topk_workspace", "ddt_draft_topk", "ddt_best_first_tree"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -349,3 +353,50 @@ def accept_compact(target_ids, draft_ids, parents, ckv, kpe, kv_base, prefix_len
                                     _dtype_code(ckv), ckv.shape[1], kpe.shape[1], _p(kv_base), _p(prefix_len),
                                     _p(new_prefix_len), _p(src_slot), _stream(stream)), "ddt_accept_compact")
     return accept_len, path, tokens
+
+
+def draft_topk_workspace_bytes(rows: int, V: int, K: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().ddt_draft_topk_workspace(rows, V, K, ctypes.byref(n)), "ddt_draft_topk_workspace")
+    return n.value
+
+
+def draft_topk(logits, K, ids=None, logp=None, workspace=None, stream=None):
+    """fp32 draft logits [rows, V] (row view) -> (ids [rows, K] int32, logp [rows, K] fp32)."""
+    _dev(logits, torch.float32, "logits")
+    ld = _rows(logits, "logits")
+    rows, V = logits.shape
+    dev = logits.device
+    if ids is None:
+        ids = torch.empty((rows, K), dtype=torch.int32, device=dev)
+    if logp is None:
+        logp = torch.empty((rows, K), dtype=torch.float32, device=dev)
+    _contig(ids, torch.int32, "ids")
+    _contig(logp, torch.float32, "logp")
+    if workspace is None:
+        workspace = torch.empty((max(16, draft_topk_workspace_bytes(rows, V, K)),), dtype=torch.uint8, device=dev)
+    ws_n = workspace.numel() * workspace.element_size()
+    _check(lib().ddt_draft_topk(_p(logits), rows, V, ld, K, _p(ids), _p(logp), _p(workspace), ws_n,
+                                _stream(stream)), "ddt_draft_topk")
+    return ids, logp
+
+
+def best_first_tree(ids, logp, root_tokens, budget, parents=None, tokens=None, depth=None, stream=None):
+    """ids [B, D, K] int32, logp [B, D, K] fp32, root_tokens [B] int32 ->
+    (parents, tokens, depth) [B, budget+1] int32."""
+    _contig(ids, torch.int32, "ids")
+    _contig(logp, torch.float32, "logp")
+    _contig(root_tokens, torch.int32, "root_tokens")
+    B, D, K = ids.shape
+    if tuple(logp.shape) != (B, D, K) or tuple(root_tokens.shape) != (B,):
+        raise ValueError("logp must be [B, D, K] and root_tokens [B]")
+    dev = ids.device
+    outs = []
+    for t, n in ((parents, "parents"), (tokens, "tokens"), (depth, "depth")):
+        if t is None:
+            t = torch.empty((B, budget + 1), dtype=torch.int32, device=dev)
+        _contig(t, torch.int32, n)
+        outs.append(t)
+    _check(lib().ddt_best_first_tree(_p(ids), _p(logp), B, D, K, budget, _p(root_tokens), _p(outs[0]), _p(outs[1]),
+                                     _p(outs[2]), _stream(stream)), "ddt_best_first_tree")
+    return tuple(outs)

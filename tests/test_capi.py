@@ -97,3 +97,21 @@ def test_verify_step_validation(lib):
         acc = ddt.AcceptTask(*f, None)
         assert lib.ddt_verify_step(*args, ctypes.byref(good_am), ctypes.byref(acc), None) == -1, k
 
+
+
+def test_draft_validation(lib):
+    n = ctypes.c_size_t(0)
+    assert lib.ddt_draft_topk_workspace(256, 163840, 8, ctypes.byref(n)) == 0 and n.value > 0
+    assert lib.ddt_draft_topk_workspace(4, 100, 0, ctypes.byref(n)) == -1          # K < 1
+    assert lib.ddt_draft_topk_workspace(4, 100, 17, ctypes.byref(n)) == -1         # K > 16
+    assert lib.ddt_draft_topk_workspace(4, 5, 8, ctypes.byref(n)) == -1            # K > V
+    assert lib.ddt_draft_topk_workspace(4, (1 << 20) + 1, 8, ctypes.byref(n)) == -1  # V > 2^20
+    assert lib.ddt_draft_topk(None, 4, 100, 99, 4, None, None, None, 0, None) == -1  # ld < V
+    assert lib.ddt_draft_topk(None, 0, 100, 100, 4, None, None, None, 0, None) == 0  # nothing to do
+    # tree: the candidates must suffice, sizes in range
+    assert lib.ddt_best_first_tree(None, None, 1, 2, 2, 7, None, None, None, None, None) == -1  # 6 candidates
+    assert lib.ddt_best_first_tree(None, None, 0, 2, 2, 6, None, None, None, None, None) == 0   # B = 0
+    assert lib.ddt_best_first_tree(None, None, 1, 0, 2, 1, None, None, None, None, None) == -1  # D < 1
+    assert lib.ddt_best_first_tree(None, None, 1, 8, 8, 1024, None, None, None, None, None) == -1  # budget + 1 > 1024
+    assert lib.ddt_best_first_tree(None, None, 1, 64, 65, 10, None, None, None, None, None) == -1  # D*K > 4096
+    assert lib.ddt_best_first_tree(None, None, 1, 8, 8, 63, None, None, None, None, None) == -1   # null pointers
