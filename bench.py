@@ -328,6 +328,7 @@ def run_loop(args, dev):
     achieved = last_flops / (ms_attn * 1e-3) / 1e12
     last_keys = int(inp.prefix_len.sum()) + loop.B * loop.N
     attn_bytes = last_keys * (dl + loop.d_rope) * 2 + loop.B * loop.N * loop.H * ((dl + loop.d_rope) * 2 + dl * 2 + 4)
+    draft = time_draft_step(loop, stream, reps)
     res = {
         "metric": "verify-attn TFLOP/s + cache tokens/s; % of MFMA/HBM roofline, 1xMI355X",
         "value": round(flops / (t_ms * 1e-3) / 1e12, 3),
@@ -354,10 +355,53 @@ def run_loop(args, dev):
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
                      "algorithmic_bytes": attn_bytes,
                      "achieved_GBps": round(attn_bytes / (ms_attn * 1e-3) / 1e9, 1)},
+        "draft_step": draft,
     }
     if snap is not None:
         res["cpu_baseline"] = cpu_baseline(snap[0], args.cpu_seconds, snap[1])
     print(json.dumps(res), flush=True)
+
+
+def time_draft_step(loop, stream, reps):
+    """The step before the verify path, on the device, at the loop's shape:
+    per-depth top-k of N(0, 3^2) draft logits (B*D rows x vocabulary) and
+    the best-first trees (not part of `value`: the loop draws its trees on
+    the host).  The top-k is an HBM scan, reported against 8 TB/s."""
+    import torch
+
+    from mla_tree_verify_parents_amd import ddt
+
+    B, D, K, V = loop.B, loop.D, loop.K, loop.vocab
+    g = torch.Generator(device=loop.device)
+    g.manual_seed(loop.seed)
+    x = torch.randn((B * D, V), generator=g, device=loop.device, dtype=torch.float32) * loop.sigma
+    ids = torch.empty((B * D, K), dtype=torch.int32, device=loop.device)
+    lp = torch.empty((B * D, K), dtype=torch.float32, device=loop.device)
+    ws = torch.empty((max(16, ddt.draft_topk_workspace_bytes(B * D, V, K)),), dtype=torch.uint8, device=loop.device)
+    roots = torch.from_numpy(loop.roots.copy()).to(loop.device)
+    outs = [torch.empty((B, loop.N), dtype=torch.int32, device=loop.device) for _ in range(3)]
+
+    def topk():
+        ddt.draft_topk(x, K, ids, lp, ws)
+
+    def tree():
+        ddt.best_first_tree(ids.view(B, D, K), lp.view(B, D, K), roots, loop.N - 1, *outs)
+
+    def timed(f):
+        f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ms_topk, ms_tree = timed(topk), timed(tree)
+    gbps = B * D * V * 4 / (ms_topk * 1e-3) / 1e9
+    return {"rows": B * D, "vocab": V, "k": K, "topk_ms": round(ms_topk, 5), "tree_ms": round(ms_tree, 5),
+            "topk_GBps": round(gbps, 1), "topk_hbm_frac": round(gbps / PEAK_HBM_GBPS, 4)}
 
 
 def to_host_bits(t):
