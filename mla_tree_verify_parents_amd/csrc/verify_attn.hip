@@ -322,6 +322,25 @@ template <>
 __device__ inline void store4<float>(float* dst, const float* v) {
     *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
 }
+// The same with a non-temporal hint: split partials are streamed to memory
+// for the merge launch rather than kept in this XCD's L2 (measured 1.1 us
+// off the attention launch at the K2-like head share).
+template <typename T>
+__device__ inline void store4_nt(T* dst, const float* v);
+template <>
+__device__ inline void store4_nt<uint16_t>(uint16_t* dst, const float* v) {
+    typedef uint32_t U2 __attribute__((ext_vector_type(2)));
+    U2 w;
+    w.x = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
+    w.y = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
+    __builtin_nontemporal_store(w, reinterpret_cast<U2*>(dst));
+}
+template <>
+__device__ inline void store4_nt<float>(float* dst, const float* v) {
+    typedef float F4 __attribute__((ext_vector_type(4)));
+    const F4 w = {v[0], v[1], v[2], v[3]};
+    __builtin_nontemporal_store(w, reinterpret_cast<F4*>(dst));
+}
 // four consecutive elements widened to fp32
 template <typename T>
 __device__ inline float4 load4(const T* src);
@@ -1135,7 +1154,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                     float v[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) v[e] = o[rb][c][v4 * 4 + e];
-                    store4<T>(ws + ((c * 4 + v4) * 64 + lane) * 4, v);
+                    store4_nt<T>(ws + ((c * 4 + v4) * 64 + lane) * 4, v);
                 }
             }
         }
