@@ -49,6 +49,7 @@ def parse():
     ap.add_argument("--loop-steps", type=int, default=100, help="timed iterations of the verify loop (config 5)")
     ap.add_argument("--attn-reps", type=int, default=200, help="back-to-back attention launches timed for the roofline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the on-device MFMA / HBM peak probes")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget for the oracle timing")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run 5 attention launches and a 256 MiB calibration copy, then exit")
@@ -258,6 +259,7 @@ def main():
                      "algorithmic_bytes": attn_bytes,
                      "achieved_GBps": round(attn_bytes / (ms_attn * 1e-3) / 1e9, 1)},
     }
+    add_peaks(res, args, dev)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, flops)
     print(json.dumps(res), flush=True)
@@ -357,9 +359,74 @@ def run_loop(args, dev):
                      "achieved_GBps": round(attn_bytes / (ms_attn * 1e-3) / 1e9, 1)},
         "draft_step": draft,
     }
+    add_peaks(res, args, dev)
     if snap is not None:
         res["cpu_baseline"] = cpu_baseline(snap[0], args.cpu_seconds, snap[1])
     print(json.dumps(res), flush=True)
+
+
+def measure_peaks(dev):
+    """What the device sustains, measured by the library's probe kernels on
+    this run: a bf16 MFMA loop on random N(0,1) operands and on zeros (the
+    board power limit sets the clock, and the clock depends on the
+    operands), a streaming HBM read and a streaming copy."""
+    import torch
+
+    from mla_tree_verify_parents_amd import ddt
+
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    stream = torch.cuda.current_stream()
+
+    def timed(f, reps, warm):
+        for _ in range(warm):
+            f()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    out = {"cus": cus}
+    # two wavefronts per SIMD: the loop then issues at about 97 % of the MFMA
+    # rate (four or more per SIMD measured 20 % lower)
+    blocks, iters = 2 * cus, 4096
+    flop = blocks * 4 * iters * ddt.PROBE_MFMA_FLOP_PER_WAVE_ITER
+    g = torch.Generator(device=dev)
+    g.manual_seed(1009)
+    for name, ops in (("random", torch.randn(ddt.PROBE_MFMA_OPERANDS, generator=g, device=dev)),
+                      ("zero", torch.zeros(ddt.PROBE_MFMA_OPERANDS, device=dev))):
+        ops = ops.to(torch.bfloat16)
+        sink = torch.empty(blocks * ddt.PROBE_THREADS, dtype=torch.float32, device=dev)
+        clk = torch.empty((blocks, 2), dtype=torch.int64, device=dev)
+        ms = timed(lambda: ddt.probe_mfma_bf16(ops, blocks, iters, sink=sink, clk=clk), 20, 10)
+        c = clk.sum(dim=0).tolist()
+        out[f"mfma_bf16_{name}_TFLOPs"] = round(flop / (ms * 1e-3) / 1e12, 1)
+        out[f"mfma_bf16_{name}_core_GHz"] = round(0.1 * c[0] / max(c[1], 1), 3)
+    nbytes = 2 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    sink = torch.empty(8 * cus * ddt.PROBE_THREADS, dtype=torch.int32, device=dev)
+    ms = timed(lambda: ddt.probe_read(src, 8 * cus, sink=sink), 20, 3)
+    out["hbm_read_GBps"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    half = src[: nbytes // 2]
+    dst = src[nbytes // 2:]
+    ms = timed(lambda: ddt.probe_copy(half, dst, 8 * cus), 20, 3)
+    out["hbm_copy_GBps"] = round(2 * half.numel() / (ms * 1e-3) / 1e9, 1)
+    out["note"] = ("achieved rates of the probe kernels on this device and run (MFMA loop: 4 independent "
+                   "32x32x16 bf16 chains per wavefront, 2 wavefronts per SIMD; HBM: 2 GiB read, 1 GiB copy)")
+    del src, sink
+    return out
+
+
+def add_peaks(res, args, dev):
+    if args.no_peaks:
+        return
+    pk = measure_peaks(dev)
+    res["measured_peaks"] = pk
+    res["roofline"]["frac_of_measured_mfma_random"] = round(res["roofline"]["achieved"] /
+                                                            pk["mfma_bf16_random_TFLOPs"], 4)
 
 
 def time_draft_step(loop, stream, reps):

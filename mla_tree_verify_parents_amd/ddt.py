@@ -73,10 +73,14 @@ def lib():
         L.ddt_draft_topk_workspace.argtypes = [i64, i64, i32, ctypes.POINTER(sz)]
         L.ddt_draft_topk.argtypes = [P, i64, i64, i64, i32, P, P, P, sz, P]
         L.ddt_best_first_tree.argtypes = [P, P, i32, i32, i32, i32, P, P, P, P, P]
+        L.ddt_probe_mfma_bf16.argtypes = [P, P, P, i32, i32, P]
+        L.ddt_probe_read.argtypes = [P, sz, P, i32, P]
+        L.ddt_probe_copy.argtypes = [P, P, sz, i32, P]
         for f in ("ddt_version", "ddt_build_mask", "ddt_verify_workspace", "ddt_verify_attn",
                   "ddt_argmax_workspace", "ddt_argmax", "ddt_greedy_accept", "ddt_compact_kv",
                   "ddt_accept_compact", "ddt_verify_attn_argmax", "ddt_verify_step",
-                  "ddt_draft_topk_workspace", "ddt_draft_topk", "ddt_best_first_tree"):
+                  "ddt_draft_topk_workspace", "ddt_draft_topk", "ddt_best_first_tree",
+                  "ddt_probe_mfma_bf16", "ddt_probe_read", "ddt_probe_copy"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -400,3 +404,59 @@ def best_first_tree(ids, logp, root_tokens, budget, parents=None, tokens=None, d
     _check(lib().ddt_best_first_tree(_p(ids), _p(logp), B, D, K, budget, _p(root_tokens), _p(outs[0]), _p(outs[1]),
                                      _p(outs[2]), _stream(stream)), "ddt_best_first_tree")
     return tuple(outs)
+
+
+# ---------------------------------------------------------------- probes ----
+# include/ddt_probe.h: the device's achievable MFMA rate and HBM bandwidth,
+# measured by the library's own kernels beside the datasheet peaks.
+PROBE_THREADS = 256
+PROBE_MFMA_OPERANDS = 4096
+PROBE_MFMA_FLOP_PER_WAVE_ITER = 524288
+
+
+def probe_mfma_bf16(ops, blocks, iters, sink=None, clk=None, stream=None):
+    """bf16 MFMA loop over the operand fragments in `ops` (4096 bf16);
+    performs blocks * 4 * iters * PROBE_MFMA_FLOP_PER_WAVE_ITER flop.
+    Returns (sink, clk): clk[b] = (core-clock ticks, 100 MHz ticks) of
+    workgroup b's loop."""
+    _contig(ops, torch.bfloat16, "ops")
+    if ops.numel() != PROBE_MFMA_OPERANDS:
+        raise ValueError(f"ops must hold {PROBE_MFMA_OPERANDS} values")
+    if sink is None:
+        sink = torch.empty((blocks * PROBE_THREADS,), dtype=torch.float32, device=ops.device)
+    if clk is None:
+        clk = torch.empty((blocks, 2), dtype=torch.int64, device=ops.device)
+    _contig(sink, torch.float32, "sink")
+    _contig(clk, torch.int64, "clk")
+    if sink.numel() < blocks * PROBE_THREADS or clk.numel() < 2 * blocks:
+        raise ValueError("sink or clk too small")
+    _check(lib().ddt_probe_mfma_bf16(_p(ops), _p(sink), _p(clk), blocks, iters, _stream(stream)),
+           "ddt_probe_mfma_bf16")
+    return sink, clk
+
+
+def probe_read(src, blocks, sink=None, stream=None):
+    """Streaming read of every byte of `src` (contiguous, 16-byte multiple)."""
+    _dev(src, None, "src")
+    if not src.is_contiguous():
+        raise ValueError("src must be contiguous")
+    if sink is None:
+        sink = torch.empty((blocks * PROBE_THREADS,), dtype=torch.int32, device=src.device)
+    _contig(sink, torch.int32, "sink")
+    if sink.numel() < blocks * PROBE_THREADS:
+        raise ValueError("sink too small")
+    nbytes = src.numel() * src.element_size()
+    _check(lib().ddt_probe_read(_p(src), nbytes, _p(sink), blocks, _stream(stream)), "ddt_probe_read")
+    return sink
+
+
+def probe_copy(src, dst, blocks, stream=None):
+    """Streaming copy of `src` into `dst` (contiguous, same byte size)."""
+    for t, n in ((src, "src"), (dst, "dst")):
+        _dev(t, None, n)
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst differ in size")
+    _check(lib().ddt_probe_copy(_p(src), _p(dst), nbytes, blocks, _stream(stream)), "ddt_probe_copy")

@@ -1,7 +1,8 @@
 """CPU checks of the C ABI: the built library loads and exports every
-function include/ddt.h declares, and host-side argument validation rejects
+function include/*.h declares, and host-side argument validation rejects
 bad calls before anything reaches the GPU (no kernel is launched here)."""
 import ctypes
+import glob
 import os
 import re
 
@@ -9,13 +10,15 @@ import pytest
 
 from mla_tree_verify_parents_amd import build, ddt
 
-HEADER = os.path.join(build.ROOT, "include", "ddt.h")
+HEADERS = sorted(glob.glob(os.path.join(build.ROOT, "include", "*.h")))
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ddt_[a-z_0-9]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names.update(re.findall(r"\b(ddt_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -30,6 +33,11 @@ def test_header_declares_the_path():
     for f in ("ddt_build_mask", "ddt_verify_attn", "ddt_verify_workspace", "ddt_argmax",
               "ddt_argmax_workspace", "ddt_greedy_accept", "ddt_compact_kv"):
         assert f in names
+
+
+def test_headers_found():
+    assert {os.path.basename(h) for h in HEADERS} >= {"ddt.h", "ddt_probe.h"}
+    assert "ddt_probe_mfma_bf16" in declared_functions()
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -115,3 +123,15 @@ def test_draft_validation(lib):
     assert lib.ddt_best_first_tree(None, None, 1, 8, 8, 1024, None, None, None, None, None) == -1  # budget + 1 > 1024
     assert lib.ddt_best_first_tree(None, None, 1, 64, 65, 10, None, None, None, None, None) == -1  # D*K > 4096
     assert lib.ddt_best_first_tree(None, None, 1, 8, 8, 63, None, None, None, None, None) == -1   # null pointers
+
+
+def test_probe_validation(lib):
+    null = None
+    one = ctypes.c_void_p(16)  # never dereferenced: every call below fails validation first
+    assert lib.ddt_probe_mfma_bf16(null, one, null, 1, 1, null) == -1     # null operands
+    assert lib.ddt_probe_mfma_bf16(one, one, null, 0, 1, null) == -1      # no workgroups
+    assert lib.ddt_probe_mfma_bf16(one, one, null, 1, 0, null) == -1      # no iterations
+    assert lib.ddt_probe_read(one, 24, one, 1, null) == -1                # not a multiple of 16
+    assert lib.ddt_probe_read(one, 0, one, 1, null) == -1
+    assert lib.ddt_probe_copy(one, ctypes.c_void_p(32), 64, 1, null) == -1  # overlapping ranges
+    assert lib.ddt_probe_copy(one, null, 64, 1, null) == -1
