@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--attn-reps", type=int, default=200, help="back-to-back attention launches timed for the roofline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true", help="skip the on-device MFMA / HBM peak probes")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache attention timing (configs 2 and 3)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget for the oracle timing")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run 5 attention launches and a 256 MiB calibration copy, then exit")
@@ -229,6 +231,10 @@ def main():
     torch.cuda.synchronize()
     ms_attn = a0.elapsed_time(a1) / args.attn_reps
 
+    cold = None
+    if args.config in (2, 3) and not args.no_cold:
+        cold = time_cold_attn(pool, dl, q_lat, q_pe, kv_base, P_host, mask, H, w.scale, out, lse, ws, side, stream)
+
     pairs = w.visible_pairs()
     flops = pairs * FLOP_PER_PAIR
     keys = int(w.keys().sum())
@@ -259,6 +265,15 @@ def main():
                      "algorithmic_bytes": attn_bytes,
                      "achieved_GBps": round(attn_bytes / (ms_attn * 1e-3) / 1e9, 1)},
     }
+    if cold is not None:
+        ms_cold, n_copies = cold
+        res["cold_cache"] = {"verify_attn_ms": round(ms_cold, 5), "cache_copies": n_copies,
+                             "copy_bytes": pool.numel() * pool.element_size(),
+                             "achieved_TFLOPs": round(flops / (ms_cold * 1e-3) / 1e12, 2),
+                             "frac": round(flops / (ms_cold * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                             "note": "back-to-back launches rotating over distinct copies of the cache "
+                                     f"(at least {COLD_BYTES >> 20} MiB in all), so the last-level cache "
+                                     "cannot serve the keys"}
     add_peaks(res, args, dev)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, flops)
@@ -363,6 +378,47 @@ def run_loop(args, dev):
     if snap is not None:
         res["cpu_baseline"] = cpu_baseline(snap[0], args.cpu_seconds, snap[1])
     print(json.dumps(res), flush=True)
+
+
+COLD_BYTES = 2 * (256 << 20)  # twice the last-level cache
+
+
+def time_cold_attn(pool, dl, q_lat, q_pe, kv_base, P_host, mask, H, scale, out, lse, ws, side, stream):
+    """Attention time with the keys out of every cache: one graph of
+    launches that each read a different copy of the cache pool, the copies
+    together at least COLD_BYTES.  Returns (ms per launch, copies)."""
+    import torch
+
+    from mla_tree_verify_parents_amd import ddt
+
+    nbytes = pool.numel() * pool.element_size()
+    n = max(2, -(-COLD_BYTES // nbytes) + 1)
+    copies = [pool.clone() for _ in range(n)]
+
+    def run_all():
+        for c in copies:
+            ddt.verify_attn(q_lat, q_pe, c[:, :dl], c[:, dl:], kv_base, P_host, mask, H=H, scale=scale, out=out,
+                            lse=lse, workspace=ws)
+
+    with torch.cuda.stream(side):
+        run_all()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run_all()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 3
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (reps * n)
+    del g, copies
+    torch.cuda.empty_cache()
+    return ms, n
 
 
 def measure_peaks(dev):
