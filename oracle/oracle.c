@@ -26,9 +26,11 @@
 
 #define ORC_F32 0
 #define ORC_BF16 1
+#define ORC_F64 2 /* only the per-head projection takes fp64 inputs (to chain oracle results) */
 
 /* Exact widening of one stored element to double. */
 static double orc_load(const void* base, int dtype, int64_t idx) {
+    if (dtype == ORC_F64) return ((const double*)base)[idx];
     if (dtype == ORC_F32) return (double)((const float*)base)[idx];
     uint32_t bits = ((uint32_t)((const uint16_t*)base)[idx]) << 16;
     float f;
@@ -395,6 +397,36 @@ int orc_best_first_tree(const int32_t* ids, const float* lp, int D, int K, int b
     }
     free(fs); free(fd); free(fr); free(fp); free(fq); free(ns);
     return rc;
+}
+
+/*
+ * Per-head projection around the absorbed attention ([P1] "The Thinking
+ * Process: A Window into Engineering Deliberation": W_UK is absorbed into
+ * the query, q_lat[h] = q_nope[h] @ W_UK[h]; the latent output returns to
+ * the head's value space through W_UV[h].  [P1] "The Output Knowledge: What
+ * This Message Creates": every projection is y = x @ W with W stored
+ * [in, out]).  Rows r = t*H + h, t in [0, M) (token-major, head-minor, the
+ * attention's query row order):
+ *   y[r][n] = sum_{k=0}^{K-1} x[r][k] * W[h][k][n]
+ * x row r starts at x + r*ld_x; W is [H][K][n_out] row-major; y is dense
+ * [M*H][n_out].  x and W may be fp32, bf16 or fp64 (dtype codes 0, 1, 2).
+ */
+int orc_head_proj(int64_t M, int H, int K, int n_out, const void* x, int x_dtype, int64_t ld_x,
+                  const void* w, int w_dtype, double* y) {
+    if (M < 0 || H < 1 || K < 1 || n_out < 1 || ld_x < K || !x || !w || !y) return -1;
+    if (x_dtype < 0 || x_dtype > 2 || w_dtype < 0 || w_dtype > 2) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < M * H; ++r) {
+        int h = (int)(r % H);
+        for (int n = 0; n < n_out; ++n) {
+            double acc = 0.0;
+            for (int k = 0; k < K; ++k)
+                acc += orc_load(x, x_dtype, r * ld_x + k) *
+                       orc_load(w, w_dtype, ((int64_t)h * K + k) * n_out + n);
+            y[r * n_out + n] = acc;
+        }
+    }
+    return 0;
 }
 
 /* Number of OpenMP threads the oracle runs with (for reporting). */

@@ -21,7 +21,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(_HERE, "oracle.c")
 LIB = os.path.join(_HERE, "liboracle.so")
 
-F32, BF16 = 0, 1
+F32, BF16, F64 = 0, 1, 2
 
 _lib = None
 
@@ -54,8 +54,10 @@ def lib():
         L.orc_num_threads.argtypes = []
         L.orc_draft_topk.argtypes = [P, i64, i64, i64, i32, P, P]
         L.orc_best_first_tree.argtypes = [P, P, i32, i32, i32, i32, P, P, P]
+        L.orc_head_proj.argtypes = [i64, i32, i32, i32, P, i32, i64, P, i32, P]
         for f in (L.orc_build_mask, L.orc_verify_attn, L.orc_argmax, L.orc_greedy_accept,
-                  L.orc_compact_kv, L.orc_num_threads, L.orc_draft_topk, L.orc_best_first_tree):
+                  L.orc_compact_kv, L.orc_num_threads, L.orc_draft_topk, L.orc_best_first_tree,
+                  L.orc_head_proj):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -134,6 +136,24 @@ def verify_attn(q_lat, q_pe, ckv, kpe, kv_base, prefix_len, parents, *, H: int,
     if rc != 0:
         raise RuntimeError(f"orc_verify_attn failed: {rc}")
     return (out, lse, wsum) if with_wsum else (out, lse)
+
+
+def head_proj(x: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """Per-head projection y[t*H + h] = x[t*H + h] @ w[h].
+
+    x [M*H, K] (2-D, row views allowed), w [H, K, n_out]; each float32,
+    uint16 (bf16 bits) or float64.  Returns y [M*H, n_out] float64."""
+    def code(a):
+        return F64 if a.dtype == np.float64 else _dtype_code(a)
+    w = np.ascontiguousarray(w)
+    H, K, n_out = w.shape
+    assert x.ndim == 2 and x.shape[1] == K and x.shape[0] % H == 0
+    M = x.shape[0] // H
+    y = np.zeros((M * H, n_out), np.float64)
+    rc = lib().orc_head_proj(M, H, K, n_out, _ptr(x), code(x), _ld(x), _ptr(w), code(w), _ptr(y))
+    if rc != 0:
+        raise RuntimeError(f"orc_head_proj failed: {rc}")
+    return y
 
 
 def argmax(logits: np.ndarray) -> np.ndarray:
