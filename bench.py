@@ -274,6 +274,9 @@ def main():
                              "note": "back-to-back launches rotating over distinct copies of the cache "
                                      f"(at least {COLD_BYTES >> 20} MiB in all), so the last-level cache "
                                      "cannot serve the keys"}
+    res["projections"] = [time_projections(B * N, H, dev)]
+    if B * N < 2048:
+        res["projections"].append(time_projections(2048, H, dev))   # the verify loop's 32 x 64 nodes
     add_peaks(res, args, dev)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, flops)
@@ -525,6 +528,56 @@ def time_draft_step(loop, stream, reps):
     gbps = B * D * V * 4 / (ms_topk * 1e-3) / 1e9
     return {"rows": B * D, "vocab": V, "k": K, "topk_ms": round(ms_topk, 5), "tree_ms": round(ms_tree, 5),
             "topk_GBps": round(gbps, 1), "topk_hbm_frac": round(gbps / PEAK_HBM_GBPS, 4)}
+
+
+def time_projections(tokens, H, dev, reps=200, d_nope=128, d_lat=512, d_rope=64, d_v=128):
+    """The per-head projections around the attention (ddt_head_proj) at
+    `tokens` tree nodes x H heads: q_nope @ w_kc[h] -> the first d_lat
+    columns of the q_lat|q_pe rows, and out_lat @ w_vc[h] -> o.  Each is
+    timed as `reps` back-to-back launches in one graph.  Algorithmic bytes
+    per launch: every input and output row once plus the weights once; at
+    about 100 flop/B they are HBM-bound, reported against 8 TB/s (and
+    their flops against the bf16 MFMA peak)."""
+    import torch
+
+    from mla_tree_verify_parents_amd import ddt
+
+    g = torch.Generator(device=dev)
+    g.manual_seed(4242)
+    rows = tokens * H
+    q_nope = torch.randn((rows, d_nope), generator=g, device=dev).to(torch.bfloat16)
+    q = torch.randn((rows, d_lat + d_rope), generator=g, device=dev).to(torch.bfloat16)
+    out_lat = torch.randn((rows, d_lat), generator=g, device=dev).to(torch.bfloat16)
+    o = torch.empty((rows, d_v), dtype=torch.bfloat16, device=dev)
+    w_kc = ddt.proj_pack_weight((torch.randn((H, d_nope, d_lat), generator=g, device=dev) / d_nope ** 0.5)
+                                .to(torch.bfloat16))
+    w_vc = ddt.proj_pack_weight((torch.randn((H, d_lat, d_v), generator=g, device=dev) / d_lat ** 0.5)
+                                .to(torch.bfloat16))
+    stream = torch.cuda.current_stream()
+    res = {"tokens": tokens, "heads": H}
+    for name, f, K, n in (("absorb_q", lambda: ddt.head_proj(q_nope, w_kc, H, y=q[:, :d_lat]), d_nope, d_lat),
+                          ("absorb_out", lambda: ddt.head_proj(out_lat, w_vc, H, y=o), d_lat, d_v)):
+        f()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(reps):
+                f()
+        graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        nbytes = rows * (K + n) * 2 + H * K * n * 2
+        flop = 2 * rows * K * n
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        res[name] = {"K": K, "n_out": n, "us": round(ms * 1e3, 3), "GBps": round(gbps, 1),
+                     "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
+                     "TFLOPs": round(flop / (ms * 1e-3) / 1e12, 2), "bytes": nbytes}
+    return res
 
 
 def to_host_bits(t):

@@ -307,6 +307,41 @@ int ddt_verify_step(const ddt_attn_desc* d, const void* q_lat, const void* q_pe,
                     float* lse, void* workspace, size_t workspace_bytes, const ddt_argmax_task* am,
                     const ddt_accept_task* acc, hipStream_t stream);
 
+/*
+ * Per-head projections around the absorbed attention.  [Ambition], section
+ * "The Thinking Process: A Window into Engineering Deliberation": W_UK is
+ * absorbed into the query, q_lat[h] = q_nope[h] @ W_UK[h] (and the latent
+ * output is brought back to the head's value space by W_UV[h]); section
+ * "The Output Knowledge: What This Message Creates": projections are
+ * y = x @ W with W stored [in, out], and the absorbed weights w_kc, w_vc
+ * are given directly.
+ *
+ * ddt_proj_pack_weight: w = [H][K][n_out] (row-major, [in, out] per head)
+ * -> packed, the same number of bytes (H*K*n_out*2) in the library's
+ * operand order (opaque; only ddt_head_proj reads it).  Weights are static:
+ * pack once, reuse for every call.  packed must not alias w and must be
+ * 16-byte aligned.
+ *
+ * ddt_head_proj: for every row r = t*H + h, t in [0, M) (token-major,
+ * head-minor: the attention's query row order, with t = b*N + i):
+ *   y[r][n] = sum_k x[r][k] * W[h][k][n],  n in [0, n_out)
+ * x row r starts at x + r*ld_x, y row r at y + r*ld_y (elements); only
+ * columns [0, n_out) of y are written, so q_lat can be written straight
+ * into the first d_lat columns of the concatenated q_lat|q_pe rows
+ * (ld_y = d_lat + d_rope).  Uses: q_lat = ddt_head_proj(q_nope, w_kc)
+ * with K = d_nope, n_out = d_lat; o = ddt_head_proj(out_lat, w_vc) with
+ * K = d_lat, n_out = d_v.  bf16 in and out (fp32 accumulation, output
+ * rounded to nearest even).
+ * Supported: dtype DDT_BF16 (else DDT_EUNSUPPORTED); K in {64, 128, 256,
+ * 512}; n_out a multiple of 32 in [32, 4096]; ld_x >= K, ld_y >= n_out,
+ * both multiples of 8; x, y, w_packed 16-byte aligned; M >= 0 (M = 0 is a
+ * no-op, and x, y may then be null); x and y must not overlap.  Otherwise
+ * DDT_EINVAL.
+ */
+int ddt_proj_pack_weight(const void* w, int H, int K, int n_out, int dtype, void* packed, hipStream_t stream);
+int ddt_head_proj(const void* x, int64_t ld_x, const void* w_packed, int M, int H, int K, int n_out, int dtype,
+                  void* y, int64_t ld_y, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

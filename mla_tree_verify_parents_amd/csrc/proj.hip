@@ -1,0 +1,202 @@
+// Per-head projections around the absorbed attention, gfx950.
+//
+// What is computed ("The Architecture of Pragmatic Ambition", section "The
+// Thinking Process: A Window into Engineering Deliberation": W_UK is
+// absorbed into the query, q_lat[h] = q_nope[h] @ W_UK[h]; section "The
+// Output Knowledge: What This Message Creates": every projection is
+// y = x @ W with W stored [in, out], and the absorbed parameters w_kc, w_vc
+// are given directly).  For every row r = t*H + h (token-major, head-minor:
+// the query row order of the attention):
+//   y[r][n] = sum_k x[r][k] * W[h][k][n]
+// The two uses: q_lat = q_nope @ w_kc[h] (K = d_nope, n_out = d_lat) before
+// the attention, and o = out_lat @ w_vc[h] (K = d_lat, n_out = d_v) after it.
+//
+// How (MI355X-first): at K2 shapes a (token, head) row moves 1280 bytes for
+// 131 kflop, about 100 flop/B, under the ridge of the chip: the kernel is an
+// HBM stream whose products must run on the matrix cores to stay one.
+//  * The weights are static, so they are packed once (ddt_proj_pack_weight)
+//    into the B-operand order of MFMA 32x32x16 bf16: fragment (h, column
+//    tile of 32, k-step of 16) is 64 lanes x 16 bytes, lane l holding
+//    W[h][16 ks + 8 (l/32) + e][32 nb + l%32], e = 0..7.  Each B load of a
+//    wavefront is then 1 KB contiguous.
+//  * A workgroup owns 64 rows of one head (tokens t0..t0+63) and 128 output
+//    columns.  The 64 x K input tile goes to LDS once (16-byte loads, rows
+//    padded by 16 bytes so the fragment reads of 32 consecutive rows hit
+//    distinct bank groups); each of the 4 wavefronts multiplies it by its
+//    own 32 columns with two accumulators (rows 0-31 and 32-63).
+//  * The fp32 results are rounded to bf16 (round to nearest even) into an
+//    LDS tile and written back as 16-byte stores along the output rows.
+//  * Workgroups of one (head, column block) are consecutive on one XCD
+//    (xcd_logical_block), so its L2 serves their shared weight fragments.
+#include "common.h"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kRows = 64;    // rows (tokens of one head) per workgroup
+constexpr int kCols = 128;   // output columns per workgroup (32 per wavefront)
+constexpr int kThreads = 256;
+constexpr int kMaxK = 512;
+
+__device__ inline uint16_t bf16_bits(float f) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f)); }
+
+// One thread per packed fragment lane: 16 bytes out, 8 strided reads in.
+__global__ __launch_bounds__(256) void proj_pack_kernel(const uint16_t* __restrict__ w, int H, int K, int n_out,
+                                                        u32x4* __restrict__ wp) {
+    const int64_t total = (int64_t)H * (n_out / 32) * (K / 16) * 64;
+    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (g >= total) return;
+    const int lane = (int)(g & 63);
+    int64_t f = g >> 6;
+    const int ks = (int)(f % (K / 16));
+    f /= K / 16;
+    const int nb = (int)(f % (n_out / 32));
+    const int h = (int)(f / (n_out / 32));
+    const int n = 32 * nb + (lane & 31);
+    const int k0 = 16 * ks + 8 * (lane >> 5);
+    const uint16_t* src = w + ((int64_t)h * K + k0) * n_out + n;
+    uint16_t v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = src[(int64_t)e * n_out];
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = (uint32_t)v[2 * e] | ((uint32_t)v[2 * e + 1] << 16);
+    wp[g] = o;
+}
+
+template <int K>
+__global__ __launch_bounds__(kThreads) void proj_kernel(const uint16_t* __restrict__ x, int64_t ld_x,
+                                                        const bf16x8* __restrict__ wp, int M, int H, int n_out,
+                                                        uint16_t* __restrict__ y, int64_t ld_y, int n_tt, int n_cb) {
+    static_assert(K % 16 == 0 && K <= kMaxK, "reduction depth: whole k-steps of 16, at most 512");
+    constexpr int KS = K / 16;                 // MFMA k-steps
+    constexpr int XCH = K / 8;                 // 16-byte chunks per input row
+    constexpr int XROW = K * 2 + 16;           // padded LDS row of the input tile (bytes)
+    constexpr int YROW = kCols * 2 + 16;       // padded LDS row of the output tile (bytes)
+    constexpr int LDS = (kRows * XROW > kRows * YROW) ? kRows * XROW : kRows * YROW;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[LDS];
+
+    const int nblocks = H * n_cb * n_tt;
+    const int wg = ddt::xcd_logical_block(blockIdx.x, nblocks);
+    const int tt = wg % n_tt;
+    const int cb = (wg / n_tt) % n_cb;
+    const int h = wg / (n_tt * n_cb);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int t0 = tt * kRows;
+
+    // input tile: rows t0..t0+63 of head h, zero past M
+    for (int c = tid; c < kRows * XCH; c += kThreads) {
+        const int row = c / XCH, ch = c % XCH;
+        const int t = t0 + row;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (t < M) v = *reinterpret_cast<const u32x4*>(x + ((int64_t)t * H + h) * ld_x + ch * 8);
+        *reinterpret_cast<u32x4*>(smem + row * XROW + ch * 16) = v;
+    }
+    __syncthreads();
+
+    const int nb = cb * (kCols / 32) + wave;  // this wavefront's 32-column tile
+    floatx16 acc0 = {}, acc1 = {};
+    if (nb * 32 < n_out) {
+        const bf16x8* wf = wp + ((int64_t)(h * (n_out / 32) + nb) * KS) * 64 + lane;
+        const unsigned char* a0p = smem + (lane & 31) * XROW + (lane >> 5) * 16;
+        const unsigned char* a1p = a0p + 32 * XROW;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 b = wf[ks * 64];
+            const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(a0p + ks * 32);
+            const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(a1p + ks * 32);
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b, acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b, acc1, 0, 0, 0);
+        }
+    }
+    __syncthreads();  // the input tile is dead; its LDS becomes the output tile
+
+    // C[i][j] of a 32x32 product sits in lane j + 32*((i/4)%2), register
+    // 4*(i/8) + i%4; here i = row (token) and j = column
+    {
+        unsigned char* col = smem + (wave * 32 + (lane & 31)) * 2;
+        const int g = lane >> 5;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int i = 8 * (r >> 2) + 4 * g + (r & 3);
+            *reinterpret_cast<uint16_t*>(col + i * YROW) = bf16_bits(acc0[r]);
+            *reinterpret_cast<uint16_t*>(col + (32 + i) * YROW) = bf16_bits(acc1[r]);
+        }
+    }
+    __syncthreads();
+
+    const int cols = min(kCols, n_out - cb * kCols);  // a multiple of 32
+    const int och = cols / 8;
+    for (int c = tid; c < kRows * (kCols / 8); c += kThreads) {
+        const int row = c / (kCols / 8), ch = c % (kCols / 8);
+        const int t = t0 + row;
+        if (t >= M || ch >= och) continue;
+        *reinterpret_cast<u32x4*>(y + ((int64_t)t * H + h) * ld_y + cb * kCols + ch * 8) =
+            *reinterpret_cast<const u32x4*>(smem + row * YROW + ch * 16);
+    }
+}
+
+template <int K>
+int launch_proj(const uint16_t* x, int64_t ld_x, const bf16x8* wp, int M, int H, int n_out, uint16_t* y,
+                int64_t ld_y, hipStream_t s) {
+    const int n_tt = (M + kRows - 1) / kRows, n_cb = (n_out + kCols - 1) / kCols;
+    const int64_t nblocks = (int64_t)H * n_cb * n_tt;
+    if (nblocks > 0x7fffffff) return DDT_EINVAL;
+    hipLaunchKernelGGL(proj_kernel<K>, dim3((unsigned)nblocks), dim3(kThreads), 0, s, x, ld_x, wp, M, H, n_out, y,
+                       ld_y, n_tt, n_cb);
+    DDT_CHECK_LAUNCH();
+    return DDT_OK;
+}
+
+bool proj_shape_ok(int H, int K, int n_out) {
+    return H >= 1 && (K == 64 || K == 128 || K == 256 || K == 512) && n_out >= 32 && n_out % 32 == 0 &&
+           n_out <= 4096;
+}
+
+}  // namespace
+
+extern "C" int ddt_proj_pack_weight(const void* w, int H, int K, int n_out, int dtype, void* packed,
+                                    hipStream_t stream) {
+    if (!w || !packed) return DDT_EINVAL;
+    if (!proj_shape_ok(H, K, n_out)) return DDT_EINVAL;
+    if (dtype != DDT_BF16) return DDT_EUNSUPPORTED;
+    if (!ddt::aligned(packed, 16) || !ddt::aligned(w, 2)) return DDT_EINVAL;
+    if (w == packed) return DDT_EINVAL;
+    const int64_t total = (int64_t)H * (n_out / 32) * (K / 16) * 64;
+    const int64_t blocks = (total + 255) / 256;
+    if (blocks > 0x7fffffff) return DDT_EINVAL;
+    hipLaunchKernelGGL(proj_pack_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(w), H, K, n_out, static_cast<u32x4*>(packed));
+    DDT_CHECK_LAUNCH();
+    return DDT_OK;
+}
+
+extern "C" int ddt_head_proj(const void* x, int64_t ld_x, const void* w_packed, int M, int H, int K, int n_out,
+                             int dtype, void* y, int64_t ld_y, hipStream_t stream) {
+    if (!w_packed || M < 0) return DDT_EINVAL;
+    if (!proj_shape_ok(H, K, n_out)) return DDT_EINVAL;
+    if (dtype != DDT_BF16) return DDT_EUNSUPPORTED;
+    if (ld_x < K || ld_y < n_out || ld_x % 8 != 0 || ld_y % 8 != 0) return DDT_EINVAL;
+    if (M == 0) return DDT_OK;  // x and y are not touched (and may be null)
+    if (!x || !y) return DDT_EINVAL;
+    if (!ddt::aligned(x, 16) || !ddt::aligned(y, 16) || !ddt::aligned(w_packed, 16)) return DDT_EINVAL;
+    {   // x and y must not overlap (rows are read into LDS while others are written)
+        const int64_t rows = (int64_t)M * H;
+        const uintptr_t x0 = (uintptr_t)x, x1 = x0 + (uintptr_t)(((rows - 1) * ld_x + K) * 2);
+        const uintptr_t y0 = (uintptr_t)y, y1 = y0 + (uintptr_t)(((rows - 1) * ld_y + n_out) * 2);
+        if (x0 < y1 && y0 < x1) return DDT_EINVAL;
+    }
+    const auto* xs = static_cast<const uint16_t*>(x);
+    const auto* wp = static_cast<const bf16x8*>(w_packed);
+    auto* ys = static_cast<uint16_t*>(y);
+    switch (K) {
+        case 64: return launch_proj<64>(xs, ld_x, wp, M, H, n_out, ys, ld_y, stream);
+        case 128: return launch_proj<128>(xs, ld_x, wp, M, H, n_out, ys, ld_y, stream);
+        case 256: return launch_proj<256>(xs, ld_x, wp, M, H, n_out, ys, ld_y, stream);
+        default: return launch_proj<512>(xs, ld_x, wp, M, H, n_out, ys, ld_y, stream);
+    }
+}

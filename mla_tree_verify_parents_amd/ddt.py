@@ -18,6 +18,7 @@ import torch
 from .build import LIB
 
 DDT_F32, DDT_BF16 = 0, 1
+DDT_OK, DDT_EINVAL, DDT_EUNSUPPORTED, DDT_EWORKSPACE, DDT_EHIP = 0, -1, -2, -3, -4
 MAX_NODES = 1024
 MAX_BATCH = 128
 
@@ -73,6 +74,8 @@ def lib():
         L.ddt_draft_topk_workspace.argtypes = [i64, i64, i32, ctypes.POINTER(sz)]
         L.ddt_draft_topk.argtypes = [P, i64, i64, i64, i32, P, P, P, sz, P]
         L.ddt_best_first_tree.argtypes = [P, P, i32, i32, i32, i32, P, P, P, P, P]
+        L.ddt_proj_pack_weight.argtypes = [P, i32, i32, i32, i32, P, P]
+        L.ddt_head_proj.argtypes = [P, i64, P, i32, i32, i32, i32, i32, P, i64, P]
         L.ddt_probe_mfma_bf16.argtypes = [P, P, P, i32, i32, P]
         L.ddt_probe_read.argtypes = [P, sz, P, i32, P]
         L.ddt_probe_copy.argtypes = [P, P, sz, i32, P]
@@ -80,6 +83,7 @@ def lib():
                   "ddt_argmax_workspace", "ddt_argmax", "ddt_greedy_accept", "ddt_compact_kv",
                   "ddt_accept_compact", "ddt_verify_attn_argmax", "ddt_verify_step",
                   "ddt_draft_topk_workspace", "ddt_draft_topk", "ddt_best_first_tree",
+                  "ddt_proj_pack_weight", "ddt_head_proj",
                   "ddt_probe_mfma_bf16", "ddt_probe_read", "ddt_probe_copy"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -404,6 +408,46 @@ def best_first_tree(ids, logp, root_tokens, budget, parents=None, tokens=None, d
     _check(lib().ddt_best_first_tree(_p(ids), _p(logp), B, D, K, budget, _p(root_tokens), _p(outs[0]), _p(outs[1]),
                                      _p(outs[2]), _stream(stream)), "ddt_best_first_tree")
     return tuple(outs)
+
+
+def proj_pack_weight(w, packed=None, stream=None):
+    """Per-head projection weights [H, K, n_out] bf16 ([in, out] per head)
+    -> the packed operand order ddt_head_proj reads (same shape and bytes)."""
+    _contig(w, torch.bfloat16, "w")
+    if w.dim() != 3:
+        raise ValueError("w must be [H, K, n_out]")
+    H, K, n_out = w.shape
+    if packed is None:
+        packed = torch.empty_like(w)
+    _contig(packed, torch.bfloat16, "packed")
+    if packed.numel() != w.numel():
+        raise ValueError("packed must hold H*K*n_out elements")
+    _check(lib().ddt_proj_pack_weight(_p(w), H, K, n_out, DDT_BF16, _p(packed), _stream(stream)),
+           "ddt_proj_pack_weight")
+    return packed
+
+
+def head_proj(x, w_packed, H, y=None, stream=None):
+    """y[t*H + h] = x[t*H + h] @ W[h] for bf16 row views x [M*H, K] (rows
+    token-major, head-minor); w_packed from proj_pack_weight ([H, K, n_out]).
+    y: None (a new [M*H, n_out] tensor) or a row view [M*H, >= n_out] whose
+    first n_out columns are written."""
+    _dev(x, torch.bfloat16, "x")
+    ld_x = _rows(x, "x")
+    _contig(w_packed, torch.bfloat16, "w_packed")
+    Hw, K, n_out = w_packed.shape
+    if Hw != H or x.shape[1] != K or x.shape[0] % H != 0:
+        raise ValueError("x must be [M*H, K] with w_packed [H, K, n_out]")
+    M = x.shape[0] // H
+    if y is None:
+        y = torch.empty((M * H, n_out), dtype=torch.bfloat16, device=x.device)
+    _dev(y, torch.bfloat16, "y")
+    ld_y = _rows(y, "y")
+    if y.shape[0] != M * H or y.shape[1] < n_out:
+        raise ValueError("y must have M*H rows of at least n_out columns")
+    _check(lib().ddt_head_proj(_p(x), ld_x, _p(w_packed), M, H, K, n_out, DDT_BF16, _p(y), ld_y, _stream(stream)),
+           "ddt_head_proj")
+    return y
 
 
 # ---------------------------------------------------------------- probes ----

@@ -125,6 +125,29 @@ def test_draft_validation(lib):
     assert lib.ddt_best_first_tree(None, None, 1, 8, 8, 63, None, None, None, None, None) == -1   # null pointers
 
 
+def test_proj_validation(lib):
+    a, b, c = ctypes.c_void_p(1 << 20), ctypes.c_void_p(2 << 20), ctypes.c_void_p(3 << 20)  # never dereferenced
+    null = None
+    # pack: shapes, dtype, aliasing
+    assert lib.ddt_proj_pack_weight(a, 8, 96, 512, 1, b, null) == -1        # K not built in
+    assert lib.ddt_proj_pack_weight(a, 8, 128, 500, 1, b, null) == -1       # n_out % 32
+    assert lib.ddt_proj_pack_weight(a, 0, 128, 512, 1, b, null) == -1       # H < 1
+    assert lib.ddt_proj_pack_weight(a, 8, 128, 512, 0, b, null) == -2       # fp32 not built in
+    assert lib.ddt_proj_pack_weight(a, 8, 128, 512, 1, a, null) == -1       # in place
+    assert lib.ddt_proj_pack_weight(null, 8, 128, 512, 1, b, null) == -1
+    # projection: strides, alignment, overlap; M = 0 is a no-op
+    assert lib.ddt_head_proj(a, 128, b, 0, 8, 128, 512, 1, c, 576, null) == 0
+    assert lib.ddt_head_proj(a, 127, b, 0, 8, 128, 512, 1, c, 576, null) == -1   # ld_x < K
+    assert lib.ddt_head_proj(a, 130, b, 0, 8, 128, 512, 1, c, 576, null) == -1   # ld_x % 8
+    assert lib.ddt_head_proj(a, 128, b, 0, 8, 128, 512, 1, c, 500, null) == -1   # ld_y < n_out
+    assert lib.ddt_head_proj(ctypes.c_void_p((1 << 20) + 8), 128, b, 4, 8, 128, 512, 1, c, 576, null) == -1
+    assert lib.ddt_head_proj(a, 128, b, 4, 8, 128, 512, 1, ctypes.c_void_p((1 << 20) + 4096), 576, null) == -1
+    assert lib.ddt_head_proj(a, 128, b, 4, 8, 128, 512, 0, c, 576, null) == -2   # fp32 not built in
+    assert lib.ddt_head_proj(a, 128, b, -1, 8, 128, 512, 1, c, 576, null) == -1
+    assert lib.ddt_head_proj(null, 128, b, 0, 8, 128, 512, 1, null, 576, null) == 0   # M = 0: untouched
+    assert lib.ddt_head_proj(null, 128, b, 1, 8, 128, 512, 1, c, 576, null) == -1
+
+
 def test_probe_validation(lib):
     null = None
     one = ctypes.c_void_p(16)  # never dereferenced: every call below fails validation first
