@@ -274,6 +274,7 @@ def main():
                              "note": "back-to-back launches rotating over distinct copies of the cache "
                                      f"(at least {COLD_BYTES >> 20} MiB in all), so the last-level cache "
                                      "cannot serve the keys"}
+    res["prefill"] = time_prefill(dev)
     res["projections"] = [time_projections(B * N, H, dev)]
     if B * N < 2048:
         res["projections"].append(time_projections(2048, H, dev))   # the verify loop's 32 x 64 nodes
@@ -578,6 +579,51 @@ def time_projections(tokens, H, dev, reps=200, d_nope=128, d_lat=512, d_rope=64,
                      "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
                      "TFLOPs": round(flop / (ms * 1e-3) / 1e12, 2), "bytes": nbytes}
     return res
+
+
+def time_prefill(dev, T=8192, P0=0, H=8, chunk=1024, reps=5):
+    """Causal prefill of a T-token prompt through the verify attention
+    (chain-tree masks, chunks of `chunk` tokens, one verify call each; the
+    chunk loop captured in one graph).  Visible pairs: H * sum_t (P0+t+1)."""
+    import torch
+
+    from mla_tree_verify_parents_amd import synth
+    from mla_tree_verify_parents_amd.prefill import ChunkedPrefill
+
+    rng = np.random.default_rng(8192)
+    dl, dr = 512, 64
+    pool, base, _ = synth.make_pool(rng, np.array([P0], np.int32), T, dl + dr, "bf16")
+    q = synth.normal(rng, (T * H, dl + dr), "bf16")
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    pd, qd = to(pool), to(q)
+    kvb = torch.from_numpy(base).to(dev)
+    pf = ChunkedPrefill(H, 1.0 / np.sqrt(dl + dr), chunk=chunk, device=dev)
+    out = torch.empty((T * H, dl), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((T * H,), dtype=torch.float32, device=dev)
+
+    def run():
+        pf.run(qd[:, :dl], qd[:, dl:], pd[:, :dl], pd[:, dl:], kvb, P0, out=out, lse=lse)
+
+    run()                      # builds the chain masks and the workspace
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    graph.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    pairs = H * (T * P0 + T * (T + 1) // 2)
+    tflops = pairs * FLOP_PER_PAIR / (ms * 1e-3) / 1e12
+    return {"tokens": T, "prefix": P0, "heads": H, "chunk": chunk, "chunks": len(pf.chunks(T, P0)),
+            "ms": round(ms, 4), "visible_pairs": pairs, "TFLOPs": round(tflops, 1),
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "tokens_per_s": round(T / (ms * 1e-3), 1)}
 
 
 def to_host_bits(t):

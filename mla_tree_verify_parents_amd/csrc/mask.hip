@@ -2,10 +2,21 @@
 // section "The Decision Architecture": tree verification differs from
 // prefill only in the mask; a node sees its own ancestors inside the tree).
 //
-// One workgroup per request.  The parent array is staged in LDS and checked;
-// every (node, word) pair is then one work item that walks the parent links
-// from the node towards the root.  Node numbers strictly decrease along the
-// walk, so a walk for word w stops as soon as it drops below 64*w.
+// One workgroup per request, O(N log 64 + N*W) work for any tree shape (a
+// 1024-node chain -- a causal prefill chunk -- costs as little as a bushy
+// tree).  The parent array is staged in LDS and checked, then:
+//  1. Nodes are cut into blocks of 64 (the mask words).  One wavefront per
+//     block finds, for each node i of the block, inblock[i] = the bits of
+//     its ancestors-or-self inside the block and up[i] = its first ancestor
+//     below the block (or -1), by pointer doubling across the wavefront:
+//     lane l holds node 64w + l with the ancestor bits of the path segment
+//     from i up to (excluding) its jump target J; a round ORs in the
+//     segment of J and takes over J's jump, while J stays in the block.
+//     Parents precede their children, so at most 63 in-block ancestors
+//     exist and 6 rounds finish every lane.
+//  2. Node i's word w is inblock[a] for the first ancestor-or-self a of i
+//     inside block w, reached by following up[] (each jump leaves a block),
+//     or 0 if the ancestry skips block w.  Depth = popcount of the row - 1.
 #include "common.h"
 
 namespace {
@@ -17,6 +28,8 @@ __global__ __launch_bounds__(kMaskThreads) void mask_kernel(const int32_t* __res
                                                             int32_t* __restrict__ depth,
                                                             int32_t* __restrict__ tree_err) {
     __shared__ int32_t spar[DDT_MAX_NODES];
+    __shared__ uint64_t inblock[DDT_MAX_NODES];
+    __shared__ int32_t up[DDT_MAX_NODES];
     __shared__ int s_bad;
     const int b = blockIdx.x;
     const int32_t* par = parents + (int64_t)b * N;
@@ -34,25 +47,52 @@ __global__ __launch_bounds__(kMaskThreads) void mask_kernel(const int32_t* __res
     if (tree_err != nullptr && threadIdx.x == 0) tree_err[b] = ok ? 0 : 1;
 
     uint64_t* mrow = mask + (int64_t)b * N * W;
-    for (int idx = threadIdx.x; idx < N * W; idx += blockDim.x) {
-        const int i = idx / W, w = idx - (idx / W) * W;
-        const int lo = w * 64;
-        uint64_t bits = 0;
-        if (ok) {
-            for (int j = i; j >= lo; j = spar[j])
-                if (j < lo + 64) bits |= 1ull << (j - lo);
-        }
-        mrow[idx] = bits;
+    if (!ok) {  // invalid tree: all-zero mask, depth -1
+        for (int idx = threadIdx.x; idx < N * W; idx += blockDim.x) mrow[idx] = 0;
+        if (depth != nullptr)
+            for (int i = threadIdx.x; i < N; i += blockDim.x) depth[(int64_t)b * N + i] = -1;
+        return;
     }
-    if (depth != nullptr) {
-        for (int i = threadIdx.x; i < N; i += blockDim.x) {
-            int d = -1;
-            if (ok) {
-                d = 0;
-                for (int j = i; spar[j] >= 0; j = spar[j]) ++d;
+
+    // 1. per-block ancestor bits and the first ancestor below the block
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int w = wave; w < W; w += kMaskThreads / 64) {
+        const int lo = 64 * w, i = lo + lane;
+        const bool valid = i < N;
+        uint64_t S = valid ? (1ull << lane) : 0ull;
+        int J = valid ? spar[i] : -1;
+#pragma unroll
+        for (int round = 0; round < 6; ++round) {
+            const bool inb = J >= lo;
+            const int src = inb ? J - lo : lane;
+            const uint64_t Ss = __shfl(S, src, 64);
+            const int Js = __shfl(J, src, 64);
+            if (inb) {
+                S |= Ss;
+                J = Js;
             }
-            depth[(int64_t)b * N + i] = d;
         }
+        if (valid) {
+            inblock[i] = S;
+            up[i] = J;
+        }
+    }
+    __syncthreads();
+
+    // 2. one node per thread: walk the block-level jumps, highest word first
+    for (int i = threadIdx.x; i < N; i += blockDim.x) {
+        uint64_t* row = mrow + (int64_t)i * W;
+        int a = i, pop = 0;
+        for (int w = W - 1; w >= 0; --w) {
+            uint64_t bits = 0;
+            if (a >= 0 && (a >> 6) == w) {
+                bits = inblock[a];
+                a = up[a];
+            }
+            pop += __popcll(bits);
+            row[w] = bits;
+        }
+        if (depth != nullptr) depth[(int64_t)b * N + i] = pop - 1;
     }
 }
 
