@@ -107,6 +107,20 @@ int ddt_build_mask(const int32_t* parents, int B, int N, uint64_t* mask, int32_t
  * Built instances (d_lat, d_rope, dtype): (512, 64, BF16), (64, 16, F32).
  * Alignment: q_lat, q_pe, ckv, kpe 16-byte aligned; every row stride times
  * the element size a multiple of 16 bytes.
+ *
+ * Paged cache (block_table non-NULL).  [Keystone], section "Assumptions
+ * Embedded in the Design": one-token pages leave the cache fragmented,
+ * which the pages name a real performance problem; larger pages named by a
+ * block table keep a request's slots in page-sized runs.  Slot t of
+ * request b is then pool row
+ *   block_table[b*bt_ld + t / page_size] * page_size + t % page_size
+ * (the pool row stride stays ld_ckv / ld_kpe) and kv_base is not read (it
+ * may be NULL).  page_size: a power of two in [32, 65536]; bt_ld >=
+ * ceil((P_b + N) / page_size) for every request (DDT_EINVAL otherwise).
+ * The table entries (device int32, caller-owned) must name pages inside
+ * the pool: they are not checked.  Zero-initialised fields (NULL table)
+ * give the contiguous layout.  ddt_verify_attn, ddt_verify_attn_argmax and
+ * ddt_verify_step (attention, acceptance and compaction) take either.
  */
 typedef struct {
     int B, H, N;
@@ -116,6 +130,9 @@ typedef struct {
     int kv_chunk;
     int64_t ld_ql, ld_qp;
     int64_t ld_ckv, ld_kpe;
+    const int32_t* block_table; /* [B][bt_ld] page numbers, or NULL (contiguous) */
+    int64_t bt_ld;
+    int page_size;
 } ddt_attn_desc;
 
 /* Workspace bytes ddt_verify_attn needs for this shape and these prefix

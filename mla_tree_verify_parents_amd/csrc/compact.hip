@@ -25,7 +25,6 @@ __global__ __launch_bounds__(ddt::kCompactThreads) void compact_kernel(
     const int64_t off = (int64_t)b * N;
     const int k = accept_len[b];
     const int64_t P = prefix_len[b];
-    const int64_t base = kv_base[b];
     if (threadIdx.x == 0) s_bad = (k < 0 || k >= N) ? 1 : 0;
     __syncthreads();
     if (s_bad == 0) {
@@ -43,7 +42,8 @@ __global__ __launch_bounds__(ddt::kCompactThreads) void compact_kernel(
             src_slot[off + j] = (ok && j <= k) ? (int32_t)(P + path[off + j]) : -1;
     }
     if (!ok) return;
-    ddt::copy_path_rows<U>(ckv, ld_ckv, kpe, ld_kpe, ckv_units, kpe_units, base, P, k, rows_per_block,
+    const ddt::SlotMap map{kv_base, nullptr, 0, 0};
+    ddt::copy_path_rows<U>(ckv, ld_ckv, kpe, ld_kpe, ckv_units, kpe_units, map, b, P, k, rows_per_block,
                            reinterpret_cast<U*>(stage_raw), [&](int j) { return path[off + j]; });
     if (threadIdx.x == 0) prefix_len[b] = (int32_t)(P + k + 1);
 }
@@ -97,8 +97,8 @@ extern "C" int ddt_accept_compact(const int32_t* target_ids, const int32_t* draf
     const int rc = ddt::compact_layout(ckv, ld_ckv, kpe, ld_kpe, dtype, d_lat, d_rope, N, &lay);
     if (rc != DDT_OK) return rc;
     ddt::AcceptCompactArgs a{target_ids, draft_ids, parents, N, accept_len, path, tokens, (char*)ckv, (char*)kpe,
-                             lay.lc, lay.lk, lay.ckv_units, lay.kpe_units, lay.rows_per_block, kv_base,
-                             prefix_len, new_prefix_len, src_slot};
+                             lay.lc, lay.lk, lay.ckv_units, lay.kpe_units, lay.rows_per_block,
+                             ddt::SlotMap{kv_base, nullptr, 0, 0}, prefix_len, new_prefix_len, src_slot};
     if (lay.vec16)
         hipLaunchKernelGGL(accept_compact_kernel<uint4>, dim3(B), dim3(ddt::kCompactThreads), lay.stage_bytes,
                            stream, a);

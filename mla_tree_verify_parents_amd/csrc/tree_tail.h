@@ -65,7 +65,23 @@ __device__ inline void write_accept(const int32_t* __restrict__ target, int64_t 
     if (lane == 0) accept_len[b] = n - 1;
 }
 
-// Cache row base+P+j <- cache row base+P+path(j), j = 0..k, for a path that
+// Where the cache slots of a request live in the pool.  Contiguous: slot t
+// of request b is row kv_base[b] + t.  Paged (table non-null): slot t is row
+// table[b*ld + (t >> shift)] * 2^shift + (t mod 2^shift), pages of 2^shift
+// rows named by a block table.
+struct SlotMap {
+    const int64_t* kv_base;
+    const int32_t* table;
+    int64_t ld;
+    int shift;
+    __device__ int64_t row(int b, int64_t t) const {
+        if (table == nullptr) return kv_base[b] + t;
+        const int64_t pg = table[(int64_t)b * ld + (t >> shift)];
+        return (pg << shift) + (t & ((1ll << shift) - 1));
+    }
+};
+
+// Cache slot P+j <- cache slot P+path(j), j = 0..k, for a path that
 // starts at 0 and increases (so path(j) >= j): copies go in blocks of
 // increasing j, each block loaded whole into LDS (stage, rows_per_block
 // rows) before any of its rows is stored.  A copy then never reads a row an
@@ -73,8 +89,8 @@ __device__ inline void write_accept(const int32_t* __restrict__ target, int64_t 
 // workgroup take part; PathAt(j) returns path(j).
 template <typename U, typename PathAt>
 __device__ inline void copy_path_rows(char* __restrict__ ckv, int64_t ld_ckv, char* __restrict__ kpe,
-                                      int64_t ld_kpe, int ckv_units, int kpe_units, int64_t base, int64_t P,
-                                      int k, int rows_per_block, U* stage, PathAt path_at) {
+                                      int64_t ld_kpe, int ckv_units, int kpe_units, const SlotMap& map, int b,
+                                      int64_t P, int k, int rows_per_block, U* stage, PathAt path_at) {
     const int upr = ckv_units + kpe_units;  // U units per cache row
     for (int j0 = 0; j0 <= k; j0 += rows_per_block) {
         const int jn = (k + 1 - j0) < rows_per_block ? (k + 1 - j0) : rows_per_block;
@@ -83,7 +99,7 @@ __device__ inline void copy_path_rows(char* __restrict__ ckv, int64_t ld_ckv, ch
             const int j = j0 + u / upr, part = u % upr;
             const int src = path_at(j);
             if (src == j) continue;  // already in place
-            const int64_t row = base + P + src;
+            const int64_t row = map.row(b, P + src);
             stage[u] = part < ckv_units ? reinterpret_cast<const U*>(ckv + row * ld_ckv)[part]
                                         : reinterpret_cast<const U*>(kpe + row * ld_kpe)[part - ckv_units];
         }
@@ -91,7 +107,7 @@ __device__ inline void copy_path_rows(char* __restrict__ ckv, int64_t ld_ckv, ch
         for (int u = threadIdx.x; u < total; u += blockDim.x) {
             const int j = j0 + u / upr, part = u % upr;
             if (path_at(j) == j) continue;
-            const int64_t row = base + P + j;
+            const int64_t row = map.row(b, P + j);
             if (part < ckv_units)
                 reinterpret_cast<U*>(ckv + row * ld_ckv)[part] = stage[u];
             else
@@ -115,7 +131,7 @@ struct AcceptCompactArgs {
     char* kpe;
     int64_t ld_ckv, ld_kpe;
     int ckv_units, kpe_units, rows_per_block;
-    const int64_t* kv_base;
+    SlotMap map;
     const int32_t* prefix_len;  // [B] committed lengths
     int32_t* new_prefix_len;    // [B] may be prefix_len itself
     int32_t* src_slot;          // [B*N] or null
@@ -149,12 +165,11 @@ __device__ void accept_compact_body(const AcceptCompactArgs& a, int b, U* stage)
     if (threadIdx.x < kWave)
         write_accept(a.target, off, sdraft, spath, n, N, b, threadIdx.x, a.accept_len, a.path, a.tokens);
     const int64_t P = a.prefix_len[b];
-    const int64_t base = a.kv_base[b];
     if (a.src_slot != nullptr) {
         for (int j = threadIdx.x; j < N; j += blockDim.x) a.src_slot[off + j] = j <= k ? (int32_t)(P + spath[j]) : -1;
     }
-    copy_path_rows<U>(a.ckv, a.ld_ckv, a.kpe, a.ld_kpe, a.ckv_units, a.kpe_units, base, P, k, a.rows_per_block, stage,
-                      [&](int j) { return spath[j]; });  // (ends with a barrier: every thread has read P)
+    copy_path_rows<U>(a.ckv, a.ld_ckv, a.kpe, a.ld_kpe, a.ckv_units, a.kpe_units, a.map, b, P, k, a.rows_per_block,
+                      stage, [&](int j) { return spath[j]; });  // (ends with a barrier: every thread has read P)
     if (threadIdx.x == 0) a.new_prefix_len[b] = (int32_t)(P + k + 1);
 }
 

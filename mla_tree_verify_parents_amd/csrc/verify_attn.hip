@@ -432,7 +432,7 @@ struct VerifyParams {
     const void* q_pe;
     const void* ckv;
     const void* kpe;
-    const int64_t* kv_base;
+    ddt::SlotMap map;           // cache slot -> pool row (contiguous from kv_base, or paged)
     const uint64_t* mask;       // ancestor bits from ddt_build_mask, or null:
     const int32_t* parents;     // then each row's bits come from the parents (N <= 128)
     void* out;
@@ -954,9 +954,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     // loads an empty range, i.e. zeros, into its slot, which then holds a
     // consumed tile; so every phase issues DPW loads and the loop body has
     // no branches.
-    const int64_t kvb = p.kv_base[b];
-    const char* ckv_b = uniform_ptr(reinterpret_cast<const char*>(static_cast<const T*>(p.ckv) + kvb * p.ld_ckv));
-    const char* kpe_b = uniform_ptr(reinterpret_cast<const char*>(static_cast<const T*>(p.kpe) + kvb * p.ld_kpe));
+    // A tile's 32 rows are consecutive slots from a multiple of 32, so they
+    // are consecutive pool rows in a contiguous cache and inside one page
+    // (pages of 2^shift >= 32 rows) in a paged one: one row lookup per tile.
+    const int64_t kvb = p.map.table ? 0 : p.map.kv_base[b];
+    auto slot_row = [&](int t0) -> int64_t { return p.map.table ? p.map.row(b, t0) : kvb + t0; };
+    const char* ckv0 = reinterpret_cast<const char*>(p.ckv);
+    const char* kpe0 = reinterpret_cast<const char*>(p.kpe);
     const int ldA = (int)(p.ld_ckv * (int64_t)sizeof(T)), ldB = (int)(p.ld_kpe * (int64_t)sizeof(T));
     uint32_t voff[S::DPW];
 #pragma unroll
@@ -994,9 +998,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         const int t0 = kbeg + (real ? tile : 0) * KT;
         int nrows = kend - t0;
         nrows = real ? (nrows > KT ? KT : nrows) : 0;
+        const int64_t row = slot_row(t0);
         TileDma d;
-        d.ra = buffer_rsrc(ckv_b + (int64_t)t0 * ldA, nrows * ldA);
-        d.rb = buffer_rsrc(kpe_b + (int64_t)t0 * ldB, nrows * ldB);
+        d.ra = buffer_rsrc(uniform_ptr(ckv0 + row * ldA), nrows * ldA);
+        d.rb = buffer_rsrc(uniform_ptr(kpe0 + row * ldB), nrows * ldB);
         d.lds = lds_addr(smem) + (uint32_t)((tile % NSTAGE) * S::STAGE_BYTES);
         return d;
     };
@@ -1277,6 +1282,12 @@ int check_desc(const ddt_attn_desc* d, const int32_t* prefix_len_host) {
     if ((int64_t)d->H * d->N > (1 << 24)) return DDT_EINVAL;
     for (int b = 0; b < d->B; ++b)
         if (prefix_len_host[b] < 0 || (int64_t)prefix_len_host[b] + d->N > 0x7fffffff - 4096) return DDT_EINVAL;
+    if (d->block_table != nullptr) {  // pages: a power of two of at least one key tile; every slot in the table
+        const int ps = d->page_size;
+        if (ps < KT || ps > (1 << 16) || (ps & (ps - 1)) != 0 || d->bt_ld < 1) return DDT_EINVAL;
+        for (int b = 0; b < d->B; ++b)
+            if (((int64_t)prefix_len_host[b] + d->N + ps - 1) / ps > d->bt_ld) return DDT_EINVAL;
+    }
     return DDT_OK;
 }
 
@@ -1495,7 +1506,8 @@ int setup_attn(const ddt_attn_desc* d, const void* q_lat, const void* q_pe, cons
                void* out, float* lse, void* workspace, size_t workspace_bytes, VerifyParams* vp, Plan* pl) {
     int rc = check_desc(d, prefix_len_host);
     if (rc != DDT_OK) return rc;
-    if (!q_lat || !q_pe || !ckv || !kpe || !kv_base || !out || !lse) return DDT_EINVAL;
+    if (!q_lat || !q_pe || !ckv || !kpe || !out || !lse) return DDT_EINVAL;
+    if (!kv_base && !d->block_table) return DDT_EINVAL;
     if (!mask && !parents) return DDT_EINVAL;
     if (!mask && d->N > 128) return DDT_EINVAL;  // in-kernel ancestor bits cover two words
     if (!ddt::aligned(q_lat, 16) || !ddt::aligned(q_pe, 16) || !ddt::aligned(ckv, 16) || !ddt::aligned(kpe, 16) ||
@@ -1512,7 +1524,8 @@ int setup_attn(const ddt_attn_desc* d, const void* q_lat, const void* q_pe, cons
     vp->q_pe = q_pe;
     vp->ckv = ckv;
     vp->kpe = kpe;
-    vp->kv_base = kv_base;
+    vp->map = ddt::SlotMap{kv_base, d->block_table, d->block_table ? d->bt_ld : 0,
+                           d->block_table ? __builtin_ctz((unsigned)d->page_size) : 0};
     vp->mask = mask;
     vp->parents = mask ? nullptr : parents;
     vp->out = out;
@@ -1648,7 +1661,7 @@ extern "C" int ddt_verify_step(const ddt_attn_desc* d, const void* q_lat, const 
     vp.acc_vec16 = lay.vec16 ? 1 : 0;
     vp.acc = ddt::AcceptCompactArgs{am->idx, acc->draft_ids, acc->parents, d->N, acc->accept_len, acc->path,
                                     acc->tokens, static_cast<char*>(ckv), static_cast<char*>(kpe), lay.lc, lay.lk,
-                                    lay.ckv_units, lay.kpe_units, lay.rows_per_block, kv_base, acc->prefix_len,
+                                    lay.ckv_units, lay.kpe_units, lay.rows_per_block, vp.map, acc->prefix_len,
                                     acc->new_prefix_len, acc->src_slot};
     return run(d, vp, pl, wgs, stream);
 }

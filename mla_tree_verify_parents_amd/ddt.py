@@ -34,7 +34,8 @@ class AttnDesc(ctypes.Structure):
                 ("d_lat", ctypes.c_int), ("d_rope", ctypes.c_int), ("dtype", ctypes.c_int),
                 ("scale", ctypes.c_float), ("kv_chunk", ctypes.c_int),
                 ("ld_ql", ctypes.c_int64), ("ld_qp", ctypes.c_int64),
-                ("ld_ckv", ctypes.c_int64), ("ld_kpe", ctypes.c_int64)]
+                ("ld_ckv", ctypes.c_int64), ("ld_kpe", ctypes.c_int64),
+                ("block_table", ctypes.c_void_p), ("bt_ld", ctypes.c_int64), ("page_size", ctypes.c_int)]
 
 
 class ArgmaxTask(ctypes.Structure):
@@ -151,9 +152,19 @@ def build_mask(parents, mask=None, depth=None, tree_err=None, stream=None):
     return mask, depth, tree_err
 
 
-def attn_desc(q_lat, q_pe, ckv, kpe, *, B, H, N, scale, kv_chunk=0):
-    return AttnDesc(B, H, N, q_lat.shape[1], q_pe.shape[1], _dtype_code(q_lat), float(scale), int(kv_chunk),
-                    _rows(q_lat, "q_lat"), _rows(q_pe, "q_pe"), _rows(ckv, "ckv"), _rows(kpe, "kpe"))
+def attn_desc(q_lat, q_pe, ckv, kpe, *, B, H, N, scale, kv_chunk=0, pages=None):
+    """pages: None (contiguous cache from kv_base) or (block_table [B, bt_ld]
+    int32 device, page_size): slot t of request b is pool row
+    block_table[b, t // page_size] * page_size + t % page_size."""
+    d = AttnDesc(B, H, N, q_lat.shape[1], q_pe.shape[1], _dtype_code(q_lat), float(scale), int(kv_chunk),
+                 _rows(q_lat, "q_lat"), _rows(q_pe, "q_pe"), _rows(ckv, "ckv"), _rows(kpe, "kpe"))
+    if pages is not None:
+        table, page_size = pages
+        _contig(table, torch.int32, "block_table")
+        if table.dim() != 2 or table.shape[0] != B:
+            raise ValueError("block_table must be [B, bt_ld]")
+        d.block_table, d.bt_ld, d.page_size = table.data_ptr(), table.shape[1], int(page_size)
+    return d
 
 
 def verify_workspace_bytes(desc: AttnDesc, prefix_len_host) -> int:
@@ -165,10 +176,11 @@ def verify_workspace_bytes(desc: AttnDesc, prefix_len_host) -> int:
 
 
 def _attn_args(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, H, scale, out, lse, workspace, kv_chunk,
-               BN=None):
+               BN=None, pages=None):
     for t, n in ((q_lat, "q_lat"), (q_pe, "q_pe"), (ckv, "ckv"), (kpe, "kpe")):
         _dev(t, q_lat.dtype, n)
-    _contig(kv_base, torch.int64, "kv_base")
+    if pages is None or kv_base is not None:
+        _contig(kv_base, torch.int64, "kv_base")
     if mask is None:  # (B, N) given instead: the kernel derives the ancestor bits
         B, N = BN
     else:
@@ -180,7 +192,7 @@ def _attn_args(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, H, scale, 
     pl = np.ascontiguousarray(prefix_len_host, dtype=np.int32)
     if pl.shape != (B,):
         raise ValueError("prefix_len_host must have B entries")
-    desc = attn_desc(q_lat, q_pe, ckv, kpe, B=B, H=H, N=N, scale=scale, kv_chunk=kv_chunk)
+    desc = attn_desc(q_lat, q_pe, ckv, kpe, B=B, H=H, N=N, scale=scale, kv_chunk=kv_chunk, pages=pages)
     if out is None:
         out = torch.empty((rows, q_lat.shape[1]), dtype=q_lat.dtype, device=q_lat.device)
     if lse is None:
@@ -196,13 +208,14 @@ def _attn_args(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, H, scale, 
 
 
 def verify_attn(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, *, H, scale, out=None, lse=None,
-                workspace=None, kv_chunk=0, stream=None):
+                workspace=None, kv_chunk=0, pages=None, stream=None):
     """Tree-verify attention.  q_lat [B*N*H, d_lat], q_pe [B*N*H, d_rope] (2-D views),
     ckv [pool, d_lat], kpe [pool, d_rope] (2-D views of the cache pool), kv_base [B]
-    int64 (device), prefix_len_host [B] (host), mask [B, N, W] from build_mask.
+    int64 (device; may be None with pages), prefix_len_host [B] (host), mask [B, N, W]
+    from build_mask; pages as for attn_desc.
     Returns (out [B*N*H, d_lat], lse [B*N*H] fp32)."""
     desc, pl, out, lse, workspace, ws_n = _attn_args(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, H,
-                                                     scale, out, lse, workspace, kv_chunk)
+                                                     scale, out, lse, workspace, kv_chunk, pages=pages)
     _check(lib().ddt_verify_attn(ctypes.byref(desc), _p(q_lat), _p(q_pe), _p(ckv), _p(kpe), _p(kv_base),
                                  pl.ctypes.data, _p(mask), _p(out), _p(lse), _p(workspace), ws_n,
                                  _stream(stream)), "ddt_verify_attn")
@@ -224,10 +237,11 @@ def _argmax_task(logits, idx, argmax_workspace):
 
 
 def verify_attn_argmax(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, logits, *, H, scale, out=None,
-                       lse=None, workspace=None, idx=None, argmax_workspace=None, kv_chunk=0, stream=None):
+                       lse=None, workspace=None, idx=None, argmax_workspace=None, kv_chunk=0, pages=None,
+                       stream=None):
     """verify_attn and argmax(logits) in one launch -> (out, lse, idx)."""
     desc, pl, out, lse, workspace, ws_n = _attn_args(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, H,
-                                                     scale, out, lse, workspace, kv_chunk)
+                                                     scale, out, lse, workspace, kv_chunk, pages=pages)
     task, idx = _argmax_task(logits, idx, argmax_workspace)
     _check(lib().ddt_verify_attn_argmax(ctypes.byref(desc), _p(q_lat), _p(q_pe), _p(ckv), _p(kpe), _p(kv_base),
                                         pl.ctypes.data, _p(mask), _p(out), _p(lse), _p(workspace), ws_n,
@@ -251,7 +265,7 @@ def _accept_outputs(parents, accept_len, path, tokens):
 
 def verify_step(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, logits, draft_ids, parents, prefix_len, *,
                 H, scale, new_prefix_len=None, out=None, lse=None, workspace=None, idx=None, argmax_workspace=None,
-                accept_len=None, path=None, tokens=None, src_slot=None, kv_chunk=0, stream=None):
+                accept_len=None, path=None, tokens=None, src_slot=None, kv_chunk=0, pages=None, stream=None):
     """Attention + argmax, then acceptance + compaction, in two launches.
 
     mask: from build_mask, or None for trees of at most 128 nodes (the
@@ -260,10 +274,11 @@ def verify_step(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, logits, d
     int32; prefix_len [B] int32 device (same values as prefix_len_host);
     new_prefix_len [B] int32 device receives the advanced lengths (default:
     prefix_len itself, updated in place).  The cache views ckv / kpe are
-    compacted in place.
+    compacted in place (through the block table with pages).
     -> (out, lse, idx, accept_len, path, tokens, new_prefix_len)."""
     desc, pl, out, lse, workspace, ws_n = _attn_args(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, H,
-                                                     scale, out, lse, workspace, kv_chunk, BN=tuple(parents.shape))
+                                                     scale, out, lse, workspace, kv_chunk, BN=tuple(parents.shape),
+                                                     pages=pages)
     task, idx = _argmax_task(logits, idx, argmax_workspace)
     for t, n in ((draft_ids, "draft_ids"), (parents, "parents"), (prefix_len, "prefix_len")):
         _contig(t, torch.int32, n)

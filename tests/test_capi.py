@@ -125,6 +125,24 @@ def test_draft_validation(lib):
     assert lib.ddt_best_first_tree(None, None, 1, 8, 8, 63, None, None, None, None, None) == -1   # null pointers
 
 
+def test_paged_desc_validation(lib):
+    """Block-table fields of ddt_attn_desc, checked on the host (no launch)."""
+    from mla_tree_verify_parents_amd import ddt
+    P = (ctypes.c_int * 2)(100, 3000)
+    n = ctypes.c_size_t(0)
+
+    def desc(page_size, bt_ld, table=1 << 20):
+        d = ddt.AttnDesc(2, 8, 32, 512, 64, 1, 1 / 24, 0, 576, 576, 576, 576)
+        d.block_table, d.bt_ld, d.page_size = table, bt_ld, page_size
+        return ctypes.byref(d)
+    assert lib.ddt_verify_workspace(desc(64, 48), P, ctypes.byref(n)) == 0      # ceil(3032/64) = 48 pages
+    assert lib.ddt_verify_workspace(desc(64, 47), P, ctypes.byref(n)) == -1     # table row too short
+    assert lib.ddt_verify_workspace(desc(48, 100), P, ctypes.byref(n)) == -1    # not a power of two
+    assert lib.ddt_verify_workspace(desc(16, 400), P, ctypes.byref(n)) == -1    # smaller than a key tile
+    assert lib.ddt_verify_workspace(desc(1 << 17, 1), P, ctypes.byref(n)) == -1  # larger than 65536
+    assert lib.ddt_verify_workspace(desc(0, 0, table=None), P, ctypes.byref(n)) == 0  # contiguous
+
+
 def test_proj_validation(lib):
     a, b, c = ctypes.c_void_p(1 << 20), ctypes.c_void_p(2 << 20), ctypes.c_void_p(3 << 20)  # never dereferenced
     null = None

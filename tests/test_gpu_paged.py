@@ -1,0 +1,115 @@
+"""Paged latent cache on the GPU: the verify attention and the whole verify
+step (attention, argmax, acceptance, compaction through the block table)
+with each request's slots in pages of a shared pool.
+
+Pages are assigned by a random permutation, so requests interleave and no
+request's pages are in order; every pool row no table entry names holds
+NaN, so a wrong row lookup shows in the outputs.  The logical cache of
+request b (slot t -> row table[b][t // ps] * ps + t % ps) is rebuilt on the
+host for the oracle.  Paged attention must equal the contiguous launch bit
+for bit (same plan, same arithmetic, other addresses) and match the oracle
+to the bf16 bar; acceptance, compacted rows and lengths are bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+from mla_tree_verify_parents_amd import ddt, synth
+from tests.helpers import ATTN_TOL, DevWorkload, as_f64, oracle_attn, rel_l2, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def to_paged(w, ps, rng, spare=3):
+    """Physical pool and block table holding w's logical cache in pages of ps rows."""
+    T = w.prefix_len.astype(np.int64) + w.N
+    npg = (T + ps - 1) // ps
+    total = int(npg.sum()) + spare
+    perm = rng.permutation(total).astype(np.int32)
+    table = np.zeros((w.B, int(npg.max())), np.int32)
+    k = 0
+    for b in range(w.B):
+        table[b, : npg[b]] = perm[k: k + npg[b]]
+        k += npg[b]
+    nan = synth.BF16_NAN if w.dtype == "bf16" else synth.F32_NAN
+    phys = np.full((total * ps, w.pool.shape[1]), nan, dtype=w.pool.dtype)
+    for b in range(w.B):
+        t = np.arange(T[b])
+        phys[table[b, t // ps].astype(np.int64) * ps + t % ps] = w.pool[w.kv_base[b] + t]
+    return phys, table
+
+
+def from_paged(phys, table, ps, w):
+    """w.pool with each request's logical rows [0, P+N) read back through the table."""
+    pool = w.pool.copy()
+    for b in range(w.B):
+        t = np.arange(int(w.prefix_len[b]) + w.N)
+        pool[w.kv_base[b] + t] = phys[table[b, t // ps].astype(np.int64) * ps + t % ps]
+    return pool
+
+
+@pytest.mark.parametrize("ps", [32, 64, 512])
+def test_paged_attention_equals_contiguous(orc, ps):
+    w = synth.workload(3, B=4, prefix_range=(100, 3000))
+    rng = np.random.default_rng(ps)
+    phys, table = to_paged(w, ps, rng)
+    dw = DevWorkload(w)
+    mask = ddt.build_mask(dw.parents)[0]
+    out_c, lse_c = ddt.verify_attn(dw.q_lat(), dw.q_pe(), dw.ckv(), dw.kpe(), dw.kv_base, w.prefix_len, mask,
+                                   H=w.H, scale=w.scale)
+    pd, td = to_dev(phys), to_dev(table)
+    dl = w.d_lat
+    out_p, lse_p = ddt.verify_attn(dw.q_lat(), dw.q_pe(), pd[:, :dl], pd[:, dl:], None, w.prefix_len, mask,
+                                   H=w.H, scale=w.scale, pages=(td, ps))
+    torch.cuda.synchronize()
+    assert torch.equal(out_c.view(torch.int16), out_p.view(torch.int16))
+    assert torch.equal(lse_c, lse_p)
+    ref_out, ref_lse = oracle_attn(orc, w)
+    assert rel_l2(as_f64(to_host(out_p)), ref_out) <= ATTN_TOL["bf16"]
+    assert rel_l2(to_host(lse_p), ref_lse) <= ATTN_TOL["bf16"]
+
+
+@pytest.mark.parametrize("ps,with_mask", [(32, False), (128, True), (64, False)])
+def test_paged_verify_step(orc, ps, with_mask):
+    """The whole step on a paged cache: attention + argmax, then acceptance
+    and compaction of the accepted path's latents through the table."""
+    w = synth.workload(3, B=5, prefix_range=(0, 2000))
+    rng = np.random.default_rng(100 + ps)
+    V = 3000
+    w.draft_ids = w.draft_ids % V
+    t = synth.planted_targets(rng, w.parents, w.draft_ids, V, 0.8)
+    x = synth.target_logits(rng, t.reshape(-1), V)
+    phys, table = to_paged(w, ps, rng)
+    B, N, dl = w.B, w.N, w.d_lat
+
+    ref_out, ref_lse = oracle_attn(orc, w)
+    t_ref = orc.argmax(x).reshape(B, N)
+    oa, op, ot = orc.greedy_accept(t_ref, w.draft_ids, w.parents)
+    opool = w.pool.copy()
+    opl, osrc = orc.compact_kv(opool[:, :dl], opool[:, dl:], w.kv_base, w.prefix_len, op, oa)
+
+    pd, td = to_dev(phys), to_dev(table)
+    parents, draft = to_dev(w.parents), to_dev(w.draft_ids)
+    prefix = to_dev(w.prefix_len)
+    q = to_dev(w.q)
+    mask = ddt.build_mask(parents)[0] if with_mask else None
+    new_pl = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    src = torch.empty((B, N), dtype=torch.int32, device="cuda")
+    out, lse, idx, acc, path, tok, npl = ddt.verify_step(
+        q[:, :dl], q[:, dl:], pd[:, :dl], pd[:, dl:], None, w.prefix_len, mask, to_dev(x), draft, parents, prefix,
+        H=w.H, scale=w.scale, new_prefix_len=new_pl, src_slot=src, pages=(td, ps))
+    torch.cuda.synchronize()
+    assert (to_host(idx).reshape(B, N) == t_ref).all()
+    assert rel_l2(as_f64(to_host(out)), ref_out) <= ATTN_TOL["bf16"]
+    assert rel_l2(to_host(lse), ref_lse) <= ATTN_TOL["bf16"]
+    assert (to_host(acc) == oa).all() and (to_host(path) == op).all() and (to_host(tok) == ot).all()
+    assert (to_host(npl) == opl).all() and (to_host(src) == osrc).all()
+    got_phys = np.ascontiguousarray(to_host(pd))
+    got = from_paged(got_phys, table, ps, w)
+    assert (got.view(np.uint8) == opool.view(np.uint8)).all()       # bits: gaps hold NaN
+    # rows no table entry names are untouched
+    named = np.zeros(got_phys.shape[0], bool)
+    for b in range(B):
+        tt = np.arange(int(w.prefix_len[b]) + N)
+        named[table[b, tt // ps].astype(np.int64) * ps + tt % ps] = True
+    assert (got_phys[~named].view(np.uint8) == phys[~named].view(np.uint8)).all()
+    print(f"paged ps={ps}: accepted {oa.tolist()}")
