@@ -274,6 +274,7 @@ def main():
                              "note": "back-to-back launches rotating over distinct copies of the cache "
                                      f"(at least {COLD_BYTES >> 20} MiB in all), so the last-level cache "
                                      "cannot serve the keys"}
+    res["paged"] = time_paged(w, dev, q_lat, q_pe, mask, ms_attn)
     res["prefill"] = time_prefill(dev)
     res["projections"] = [time_projections(B * N, H, dev)]
     if B * N < 2048:
@@ -579,6 +580,63 @@ def time_projections(tokens, H, dev, reps=200, d_nope=128, d_lat=512, d_rope=64,
                      "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
                      "TFLOPs": round(flop / (ms * 1e-3) / 1e12, 2), "bytes": nbytes}
     return res
+
+
+def time_paged(w, dev, q_lat, q_pe, mask, ms_contiguous, page_size=64, reps=100):
+    """The same attention launch with the latent cache in pages of
+    `page_size` rows of one shared pool, scattered by a random permutation
+    (block table; one row lookup per 32-key tile), against the contiguous
+    launch's time."""
+    import torch
+
+    from mla_tree_verify_parents_amd import ddt
+
+    rng = np.random.default_rng(page_size)
+    T = w.prefix_len.astype(np.int64) + w.N
+    npg = (T + page_size - 1) // page_size
+    total = int(npg.sum())
+    perm = rng.permutation(total).astype(np.int32)
+    table = np.zeros((w.B, int(npg.max())), np.int32)
+    src, dst, k = [], [], 0
+    for b in range(w.B):
+        table[b, : npg[b]] = perm[k: k + npg[b]]
+        k += npg[b]
+        t = np.arange(T[b])
+        src.append(w.kv_base[b] + t)
+        dst.append(table[b, t // page_size].astype(np.int64) * page_size + t % page_size)
+    pool = torch.from_numpy(np.ascontiguousarray(w.pool).view(np.int16)).to(dev).view(torch.bfloat16)
+    phys = torch.zeros((total * page_size, pool.shape[1]), dtype=pool.dtype, device=dev)
+    phys[torch.from_numpy(np.concatenate(dst)).to(dev)] = pool[torch.from_numpy(np.concatenate(src)).to(dev)]
+    del pool
+    td = torch.from_numpy(table).to(dev)
+    dl = w.d_lat
+    out = torch.empty((w.rows, dl), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.rows,), dtype=torch.float32, device=dev)
+    pages = (td, page_size)
+    d = ddt.attn_desc(q_lat, q_pe, phys[:, :dl], phys[:, dl:], B=w.B, H=w.H, N=w.N, scale=w.scale, pages=pages)
+    ws = torch.empty((max(1, ddt.verify_workspace_bytes(d, w.prefix_len)),), dtype=torch.uint8, device=dev)
+
+    def f():
+        ddt.verify_attn(q_lat, q_pe, phys[:, :dl], phys[:, dl:], None, w.prefix_len, mask, H=w.H, scale=w.scale,
+                        out=out, lse=lse, workspace=ws, pages=pages)
+
+    f()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(reps):
+            f()
+    graph.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return {"page_size": page_size, "pages": total, "verify_attn_ms": round(ms, 5),
+            "contiguous_ms": round(ms_contiguous, 5), "ratio": round(ms / ms_contiguous, 4)}
 
 
 def time_prefill(dev, T=8192, P0=0, H=8, chunk=1024, reps=5):

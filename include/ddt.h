@@ -120,7 +120,10 @@ int ddt_build_mask(const int32_t* parents, int B, int N, uint64_t* mask, int32_t
  * The table entries (device int32, caller-owned) must name pages inside
  * the pool: they are not checked.  Zero-initialised fields (NULL table)
  * give the contiguous layout.  ddt_verify_attn, ddt_verify_attn_argmax and
- * ddt_verify_step (attention, acceptance and compaction) take either.
+ * ddt_verify_step (attention, acceptance and compaction) take either; the
+ * paged form is built for the bf16 (512, 64) instance (DDT_EUNSUPPORTED
+ * otherwise), and its key splits are at most 767 pages long (a larger
+ * kv_chunk is capped).
  */
 typedef struct {
     int B, H, N;

@@ -718,7 +718,9 @@ __host__ __device__ inline bool work_item(const VerifyParams& p, int blk, int& b
     return true;
 }
 
-template <typename T, int DL, int DR, bool kArgmax, bool kTouch>
+constexpr int kMaxSplitPages = 768;  // pages of a paged split, listed in LDS by its prologue
+
+template <typename T, int DL, int DR, bool kArgmax, bool kTouch, bool kPaged>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void verify_split(
     const VerifyParams p) {
     using S = Shape<T, DL, DR>;
@@ -750,6 +752,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const int kbeg = split * p.chunk;
     const int kend = min(kbeg + p.chunk, P + p.N);
     const int ntiles = (kend - kbeg + KT - 1) / KT;
+    // paged cache: the split's page numbers go to LDS once, so the tile loop
+    // reads them in order with its other LDS traffic (a scalar load per tile
+    // would make every LDS wait in the loop wait for it too)
+    __shared__ int32_t s_pages[kPaged ? kMaxSplitPages : 1];
+    if constexpr (kPaged) {
+        const int pg0 = kbeg >> p.map.shift, npg = ((kend - 1) >> p.map.shift) - pg0 + 1;
+        const int32_t* tb = p.map.table + (int64_t)b * p.map.ld + pg0;
+        for (int i = tid; i < npg; i += kThreads) s_pages[i] = tb[i];
+        __syncthreads();
+    }
 
     const int wrow0 = rt * ROWS_WG + grp * 32;
     const bool active = wrow0 < p.rows;            // the row group has real rows
@@ -957,10 +969,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     // A tile's 32 rows are consecutive slots from a multiple of 32, so they
     // are consecutive pool rows in a contiguous cache and inside one page
     // (pages of 2^shift >= 32 rows) in a paged one: one row lookup per tile.
-    const int64_t kvb = p.map.table ? 0 : p.map.kv_base[b];
-    auto slot_row = [&](int t0) -> int64_t { return p.map.table ? p.map.row(b, t0) : kvb + t0; };
-    const char* ckv0 = reinterpret_cast<const char*>(p.ckv);
-    const char* kpe0 = reinterpret_cast<const char*>(p.kpe);
+    const int64_t kvb = kPaged ? 0 : p.map.kv_base[b];
+    const char* ckv_b = uniform_ptr(reinterpret_cast<const char*>(static_cast<const T*>(p.ckv) + kvb * p.ld_ckv));
+    const char* kpe_b = uniform_ptr(reinterpret_cast<const char*>(static_cast<const T*>(p.kpe) + kvb * p.ld_kpe));
+    const int pshift = kPaged ? p.map.shift : 0;
+    const int ppg0 = kPaged ? (kbeg >> pshift) : 0;
     const int ldA = (int)(p.ld_ckv * (int64_t)sizeof(T)), ldB = (int)(p.ld_kpe * (int64_t)sizeof(T));
     uint32_t voff[S::DPW];
 #pragma unroll
@@ -998,10 +1011,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         const int t0 = kbeg + (real ? tile : 0) * KT;
         int nrows = kend - t0;
         nrows = real ? (nrows > KT ? KT : nrows) : 0;
-        const int64_t row = slot_row(t0);
         TileDma d;
-        d.ra = buffer_rsrc(uniform_ptr(ckv0 + row * ldA), nrows * ldA);
-        d.rb = buffer_rsrc(uniform_ptr(kpe0 + row * ldB), nrows * ldB);
+        if constexpr (kPaged) {  // pool row of slot t0: its page's first row + the offset in the page
+            const int64_t row = ((int64_t)s_pages[(t0 >> pshift) - ppg0] << pshift) + (t0 & ((1 << pshift) - 1));
+            d.ra = buffer_rsrc(uniform_ptr(ckv_b + row * ldA), nrows * ldA);
+            d.rb = buffer_rsrc(uniform_ptr(kpe_b + row * ldB), nrows * ldB);
+        } else {
+            d.ra = buffer_rsrc(ckv_b + (int64_t)t0 * ldA, nrows * ldA);
+            d.rb = buffer_rsrc(kpe_b + (int64_t)t0 * ldB, nrows * ldB);
+        }
         d.lds = lds_addr(smem) + (uint32_t)((tile % NSTAGE) * S::STAGE_BYTES);
         return d;
     };
@@ -1285,6 +1303,7 @@ int check_desc(const ddt_attn_desc* d, const int32_t* prefix_len_host) {
     if (d->block_table != nullptr) {  // pages: a power of two of at least one key tile; every slot in the table
         const int ps = d->page_size;
         if (ps < KT || ps > (1 << 16) || (ps & (ps - 1)) != 0 || d->bt_ld < 1) return DDT_EINVAL;
+        if (d->dtype != DDT_BF16) return DDT_EUNSUPPORTED;
         for (int b = 0; b < d->B; ++b)
             if (((int64_t)prefix_len_host[b] + d->N + ps - 1) / ps > d->bt_ld) return DDT_EINVAL;
     }
@@ -1365,6 +1384,13 @@ int64_t plan_cost(const int64_t* T, int B, int row_tiles, int64_t chunk, int cus
     return finish + (split ? kMergeCost : 0);
 }
 
+// Longest split: a paged split lists at most kMaxSplitPages pages in LDS,
+// and a split of c keys touches at most floor((c-1)/page) + 2 pages.
+int64_t max_chunk(const ddt_attn_desc* d) {
+    if (d->block_table == nullptr) return INT64_MAX;
+    return (int64_t)(kMaxSplitPages - 1) * d->page_size / KT * KT;
+}
+
 // The key chunk with the lowest estimated finish time among chunks that cut
 // the longest request into 1 to 32 equal parts, that give the CUs 1 to 16
 // rounds of equal work (a spread of each), and the smallest chunk (ties go
@@ -1377,7 +1403,8 @@ int64_t choose_chunk(const ddt_attn_desc* d, const int32_t* P, int row_tiles, in
         tmax = T[b] > tmax ? T[b] : tmax;
         work += T[b] * row_tiles;
     }
-    const int64_t top = (int64_t)ddt::round_up((size_t)tmax, KT);
+    int64_t top = (int64_t)ddt::round_up((size_t)tmax, KT);
+    if (top > max_chunk(d)) top = max_chunk(d);
     int64_t best = top, best_cost = plan_cost(T, d->B, row_tiles, top, cus);
     int64_t tried[64];
     int nt = 0;
@@ -1408,7 +1435,7 @@ Plan make_plan(const ddt_attn_desc* d, const int32_t* P, VerifyParams* vp) {
     pl.row_tiles = (rows + ROWS_WG - 1) / ROWS_WG;
     const int cus = num_cus();
     if (d->kv_chunk > 0)
-        pl.chunk = (int)ddt::round_up((size_t)d->kv_chunk, KT);
+        pl.chunk = (int)std::min<int64_t>((int64_t)ddt::round_up((size_t)d->kv_chunk, KT), max_chunk(d));
     else
         pl.chunk = (int)choose_chunk(d, P, pl.row_tiles, cus);
     int64_t total = 0;
@@ -1476,16 +1503,27 @@ Plan make_plan(const ddt_attn_desc* d, const int32_t* P, VerifyParams* vp) {
 template <typename T, int DL, int DR>
 int launch(const VerifyParams& vp, const Plan& pl, int n_argmax, hipStream_t stream) {
     const dim3 grid(pl.n_blocks + n_argmax);
-    if (n_argmax > 0) {
-        if (pl.touch)
-            hipLaunchKernelGGL((verify_split<T, DL, DR, true, true>), grid, dim3(kThreads), 0, stream, vp);
+    auto split = [&](auto paged) {
+        constexpr bool kP = decltype(paged)::value;
+        if (n_argmax > 0) {
+            if (pl.touch)
+                hipLaunchKernelGGL((verify_split<T, DL, DR, true, true, kP>), grid, dim3(kThreads), 0, stream, vp);
+            else
+                hipLaunchKernelGGL((verify_split<T, DL, DR, true, false, kP>), grid, dim3(kThreads), 0, stream, vp);
+        } else {
+            if (pl.touch)
+                hipLaunchKernelGGL((verify_split<T, DL, DR, false, true, kP>), grid, dim3(kThreads), 0, stream, vp);
+            else
+                hipLaunchKernelGGL((verify_split<T, DL, DR, false, false, kP>), grid, dim3(kThreads), 0, stream, vp);
+        }
+    };
+    if constexpr (std::is_same<T, uint16_t>::value) {  // paged caches: the bf16 instance
+        if (vp.map.table != nullptr)
+            split(std::true_type{});
         else
-            hipLaunchKernelGGL((verify_split<T, DL, DR, true, false>), grid, dim3(kThreads), 0, stream, vp);
+            split(std::false_type{});
     } else {
-        if (pl.touch)
-            hipLaunchKernelGGL((verify_split<T, DL, DR, false, true>), grid, dim3(kThreads), 0, stream, vp);
-        else
-            hipLaunchKernelGGL((verify_split<T, DL, DR, false, false>), grid, dim3(kThreads), 0, stream, vp);
+        split(std::false_type{});
     }
     DDT_CHECK_LAUNCH();
     const int nblk = pl.any_split ? vp.B * pl.row_tiles * NW * (DL / 64) : 0;
