@@ -680,6 +680,7 @@ def time_prefill(dev, T=8192, P0=0, H=8, chunk=1024, reps=5):
     pairs = H * (T * P0 + T * (T + 1) // 2)
     tflops = pairs * FLOP_PER_PAIR / (ms * 1e-3) / 1e12
     return {"tokens": T, "prefix": P0, "heads": H, "chunk": chunk, "chunks": len(pf.chunks(T, P0)),
+            "calls": len(pf.calls(T, P0)),
             "ms": round(ms, 4), "visible_pairs": pairs, "TFLOPs": round(tflops, 1),
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "tokens_per_s": round(T / (ms * 1e-3), 1)}
 

@@ -5,15 +5,20 @@ Architecture": prefill, decode and tree verification share one absorbed
 attention and differ only in the mask -- causal for prefill, the tree's
 ancestor relation for verification.  A chain-shaped tree (node i's parent is
 i-1) has exactly the causal mask, so a prefill chunk of N <= 1024 tokens
-placed at cache rows P .. P+N-1 is one ``ddt_verify_attn`` call with a chain
-tree at committed length P, and a prompt of any length is a sequence of
-such calls with P advancing by the chunk length.
+placed at cache rows P .. P+N-1 is a chain tree at committed length P.
 
-This module is host orchestration only (chain masks built once per chunk
-length by ``ddt_build_mask``, one workspace, one library call per chunk); the
-arithmetic is the library's.  One sequence per call: the verify attention
-takes one query row stride for all requests, and a chunk's rows are
-contiguous only within one sequence.
+Within one layer every latent of the prompt exists before the layer's
+attention runs, so the chunks do not depend on each other: chunk c is one
+request of a batched ``ddt_verify_attn`` call whose requests all share the
+prompt's cache region (the same kv_base), with committed length P0 + c*chunk.
+The query rows of the requests, request-major, are exactly the prompt's
+token-major rows, so one call covers every full chunk (and the library's
+work plan balances their ragged key ranges over the CUs); a shorter last
+chunk is a second call.
+
+This module is host orchestration only (chain masks built once per shape by
+``ddt_build_mask``, one workspace, at most two library calls); the
+arithmetic is the library's.  One prompt per call.
 """
 from __future__ import annotations
 
@@ -40,14 +45,26 @@ class ChunkedPrefill:
         self._masks = {}
         self._ws = None
 
-    def mask(self, n: int) -> torch.Tensor:
-        """Ancestor mask of an n-node chain (the causal mask), built once."""
-        m = self._masks.get(n)
+    def mask(self, n: int, reqs: int = 1) -> torch.Tensor:
+        """Ancestor masks of `reqs` n-node chains (the causal mask), built once."""
+        m = self._masks.get((n, reqs))
         if m is None:
-            par = torch.arange(-1, n - 1, dtype=torch.int32, device=self.device).view(1, n)
-            m, _, err = ddt.build_mask(par)
-            self._masks[n] = m
+            par = torch.arange(-1, n - 1, dtype=torch.int32, device=self.device).view(1, n).repeat(reqs, 1)
+            m, _, err = ddt.build_mask(par.contiguous())
+            self._masks[(n, reqs)] = m
         return m
+
+    def calls(self, T: int, P0: int):
+        """(first token, chunks, tokens per chunk) of each library call: the
+        full chunks together (up to MAX_BATCH per call), then the shorter
+        last chunk."""
+        full, rest = divmod(T, self.chunk)
+        out = []
+        for c0 in range(0, full, ddt.MAX_BATCH):          # at most MAX_BATCH requests per call
+            out.append((c0 * self.chunk, min(ddt.MAX_BATCH, full - c0), self.chunk))
+        if rest:
+            out.append((full * self.chunk, 1, rest))
+        return out
 
     def chunks(self, T: int, P0: int):
         """(first token, tokens, committed length) of each chunk."""
@@ -58,12 +75,15 @@ class ChunkedPrefill:
             done += n
         return out
 
+    def _prefix(self, t0: int, reqs: int, n: int, P0: int) -> np.ndarray:
+        return (P0 + t0 + n * np.arange(reqs)).astype(np.int32)
+
     def workspace(self, q_lat, q_pe, ckv, kpe, T: int, P0: int) -> torch.Tensor:
         need = 1
-        for _, n, P in self.chunks(T, P0):
-            d = ddt.attn_desc(q_lat[: n * self.H], q_pe[: n * self.H], ckv, kpe, B=1, H=self.H, N=n,
-                              scale=self.scale)
-            need = max(need, ddt.verify_workspace_bytes(d, np.array([P], np.int32)))
+        for t0, reqs, n in self.calls(T, P0):
+            rows = reqs * n * self.H
+            d = ddt.attn_desc(q_lat[:rows], q_pe[:rows], ckv, kpe, B=reqs, H=self.H, N=n, scale=self.scale)
+            need = max(need, ddt.verify_workspace_bytes(d, self._prefix(t0, reqs, n, P0)))
         if self._ws is None or self._ws.numel() < need:
             self._ws = torch.empty((need,), dtype=torch.uint8, device=self.device)
         return self._ws
@@ -71,7 +91,7 @@ class ChunkedPrefill:
     def run(self, q_lat, q_pe, ckv, kpe, kv_base, P0: int, out=None, lse=None, stream=None):
         """q_lat [T*H, d_lat], q_pe [T*H, d_rope] row views; ckv/kpe views of
         the cache pool; kv_base [1] int64 (device).  Returns (out [T*H,
-        d_lat], lse [T*H]); rows of chunk c are written by its call."""
+        d_lat], lse [T*H])."""
         H = self.H
         if q_lat.shape[0] % H:
             raise ValueError("q rows must be T*H")
@@ -81,8 +101,10 @@ class ChunkedPrefill:
         if lse is None:
             lse = torch.empty((T * H,), dtype=torch.float32, device=q_lat.device)
         ws = self.workspace(q_lat, q_pe, ckv, kpe, T, P0)
-        for t0, n, P in self.chunks(T, P0):
-            r0, r1 = t0 * H, (t0 + n) * H
-            ddt.verify_attn(q_lat[r0:r1], q_pe[r0:r1], ckv, kpe, kv_base, np.array([P], np.int32), self.mask(n),
-                            H=H, scale=self.scale, out=out[r0:r1], lse=lse[r0:r1], workspace=ws, stream=stream)
+        for t0, reqs, n in self.calls(T, P0):
+            r0, r1 = t0 * H, (t0 + reqs * n) * H
+            base = kv_base.expand(reqs).contiguous() if reqs > 1 else kv_base
+            ddt.verify_attn(q_lat[r0:r1], q_pe[r0:r1], ckv, kpe, base, self._prefix(t0, reqs, n, P0),
+                            self.mask(n, reqs), H=H, scale=self.scale, out=out[r0:r1], lse=lse[r0:r1], workspace=ws,
+                            stream=stream)
         return out, lse

@@ -1,8 +1,9 @@
 """Causal prefill through the verify attention, on the GPU.
 
 A chain-shaped tree's ancestor mask is the causal mask, so a prompt is
-prefilled in chunks of up to 1024 tokens, each one verify-attention call at
-the committed length reached so far (mla_tree_verify_parents_amd.prefill).
+prefilled in chunks of up to 1024 tokens, chunk c a request at committed
+length P0 + c*chunk; the full chunks go into one batched verify-attention
+call (mla_tree_verify_parents_amd.prefill).
 The chunked result is compared with the oracle's attention over the whole
 prompt as ONE chain (unchunked), on sampled rows that include every chunk's
 first and last tokens; the bf16 bar (rel-L2 <= 1e-2 on out and lse).  The
@@ -46,6 +47,8 @@ def _prompt(seed, T, P0, H=8):
     (700, 50, 256),      # three chunks, a ragged last one
     (2100, 1500, 1024),  # full-size chunks over a committed prefix
     (64, 0, 1024),       # one chunk, empty prefix: plain causal attention
+    (4096, 0, 1024),     # four full chunks in one call, nothing left over
+    (200 * 32 + 5, 7, 32),  # more full chunks than one call takes (128), then a 5-token chunk
 ])
 def test_chunked_prefill_equals_unchunked_oracle(orc, T, P0, chunk):
     H = 8
@@ -56,8 +59,9 @@ def test_chunked_prefill_equals_unchunked_oracle(orc, T, P0, chunk):
     torch.cuda.synchronize()
 
     rng = np.random.default_rng(T)
-    toks = set(rng.choice(T, size=min(T, 40), replace=False).tolist())
-    for t0, n, _ in pf.chunks(T, P0):
+    toks = set(rng.choice(T, size=min(T, 24), replace=False).tolist())
+    ch = pf.chunks(T, P0)
+    for t0, n, _ in ch[:3] + ch[-3:]:                 # first and last tokens of the outer chunks
         toks |= {t0, t0 + n - 1}
     rows = np.array(sorted(t * H + h for t in toks for h in (0, H - 1)), np.int64)
     chain = np.arange(-1, T - 1, dtype=np.int32)[None]
