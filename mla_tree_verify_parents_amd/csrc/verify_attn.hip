@@ -12,33 +12,38 @@
 // value that is the first 512 columns of the key).
 //
 // How (MI355X-first):
-//  * A workgroup of 4 wavefronts owns 128 query rows (32 per wavefront) of
-//    one request and one contiguous split of its key range.  Key tiles of 32
-//    latent rows are staged HBM -> registers -> LDS once per workgroup and
-//    shared by all 128 rows, double buffered so the next tile's global loads
-//    are in flight while the current tile is multiplied.
-//  * S^T = K . Q^T on MFMA 32x32x16 bf16 (32x32x2 f32 for fp32 data): the K
-//    tile is the A operand (read from LDS), the wavefront's 32 queries are
-//    the B operand and stay in registers for the whole split.  With this
-//    orientation the scores of one query row land in one lane pair (l,
-//    l+32), so the online-softmax max/sum need a single cross-half swap and
-//    the running max, sum and rescale factor are per-lane scalars.
-//  * O^T += V^T . P^T: the probabilities come straight out of the score
-//    accumulators as the B operand; V^T is the A operand, read from a second
-//    LDS copy of the tile written transposed during staging.  Keys inside a
-//    16-key block are stored in the order the score accumulator hands them
-//    out, so every A fragment is one 16-byte LDS read.  The 32x512 fp32
-//    output accumulator lives in AGPR/VGPRs, one row per lane pair.
-//  * fp32 online softmax in the log2 domain; the output rescale is skipped
-//    when no row's running max moved.
-//  * The key range of each request is cut into splits so that the launch
-//    covers the 256 CUs; splits write normalised partial outputs and a
-//    log-sum-exp to the workspace in the MFMA register order (1 KB
-//    contiguous per store instruction), and a combine kernel merges them.
-//    A request with one split writes its final output directly.
-//  * Workgroup ids are remapped so that each XCD runs a contiguous range of
-//    work items: the row tiles sharing one key split run on one XCD and
-//    reuse its L2.
+//  * A workgroup owns one work item = (request, key split, 64 query rows)
+//    and specialises its four wavefronts (one per SIMD).  Key tiles of 32
+//    latent rows (576 columns) reach LDS by LDS-DMA (buffer_load ... lds,
+//    issued as inline asm with hand-built buffer descriptors; rows past the
+//    split end fall outside the descriptor and read as zeros) into a ring of
+//    four slots, and every tile is shared by all 64 rows.
+//  * Score wavefronts (0, 1; 32 rows each, queries resident in AGPRs)
+//    compute S^T = K . Q^T on MFMA 32x32x16 bf16 (32x32x2 f32 for fp32
+//    data) with the K tile as the A operand, so a query row's scores land
+//    in one lane pair and its maximum needs one permlane swap.  They apply
+//    the ancestor bits (from the mask, or derived in the kernel from the
+//    parents by pointer doubling across the wavefront), take the softmax
+//    against a fixed per-row reference (a second pass over the split if a
+//    later scaled score exceeds it by more than 64 in log2) and publish
+//    bf16 P^T to LDS.
+//    The softmax of tile j-1 runs on the VALU under the MFMAs of tile j.
+//  * Value wavefronts (2, 3) each own all 64 rows and half of the 512 value
+//    columns: O^T += V^T . P^T with V^T read by transposing LDS reads
+//    (ds_read_b64_tr_b16), each fragment feeding both row groups; row sums
+//    come from an extra MFMA against ones.  They issue the tile loads (and,
+//    for long key streams, 4-byte L2 touches of tile j+2) between MFMAs.
+//  * Each request's key range is cut into splits (the host picks the chunk
+//    that minimises an estimate of the launch's finish time) and work items
+//    are dealt to the XCDs so that row tiles of one split share an L2.
+//    Split partials (normalised, in the input dtype, MFMA register order)
+//    and their log2-sum-exp go to the workspace; verify_combine merges
+//    them.  A request with one split writes its output directly.
+//  * Optional co-tasks: target-argmax workgroups on the CUs the attention
+//    leaves idle (verify_split), and acceptance + compaction workgroups
+//    beside the merge (verify_combine).
+//  * Paged caches: a paged work item lists its split's page numbers in LDS
+//    and looks up one pool row per tile (a tile never crosses a page).
 #include <math.h>
 
 #include <algorithm>
