@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2, help="workload configuration (2, 3, 4, or 5: the verify loop)")
     ap.add_argument("--loop-steps", type=int, default=100, help="timed iterations of the verify loop (config 5)")
+    ap.add_argument("--page-size", type=int, default=0,
+                    help="config 5: keep the loop's cache in pages of this many rows (0: contiguous)")
     ap.add_argument("--attn-reps", type=int, default=200, help="back-to-back attention launches timed for the roofline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true", help="skip the on-device MFMA / HBM peak probes")
@@ -298,7 +300,7 @@ def run_loop(args, dev):
     from mla_tree_verify_parents_amd import ddt, e2e, synth
 
     W, K = args.warmup, args.loop_steps
-    loop = e2e.VerifyLoop(steps=W + K)
+    loop = e2e.VerifyLoop(steps=W + K, page_size=args.page_size)
     stream = torch.cuda.current_stream()
     t_ms, flops, keys, acc_sum = 0.0, 0, 0, 0
     snap = None
@@ -308,7 +310,7 @@ def run_loop(args, dev):
             snap = (synth.Workload(name="config5", B=loop.B, H=loop.H, N=loop.N, d_lat=loop.d_lat,
                                    d_rope=loop.d_rope, dtype="bf16", scale=loop.scale,
                                    prefix_len=inp.prefix_len.copy(), kv_base=loop.kv_base_host.copy(),
-                                   capacity=loop.capacity.copy(), pool=to_host_bits(loop.pool),
+                                   capacity=loop.capacity.copy(), pool=loop.to_logical(to_host_bits(loop.pool)),
                                    q=to_host_bits(inp.q), parents=inp.parents, draft_ids=inp.draft_ids,
                                    logits=inp.logits.cpu().numpy(), vocab=loop.vocab),
                     inp.visible_pairs(loop.H) * FLOP_PER_PAIR)
@@ -333,8 +335,9 @@ def run_loop(args, dev):
     ws = loop.workspace_for(inp.prefix_len)
 
     def attn():
-        ddt.verify_attn(inp.q[:, :dl], inp.q[:, dl:], loop.ckv(), loop.kpe(), loop.kv_base, inp.prefix_len, mask,
-                        H=loop.H, scale=loop.scale, out=loop.out, lse=loop.lse, workspace=ws)
+        ddt.verify_attn(inp.q[:, :dl], inp.q[:, dl:], loop.ckv(), loop.kpe(), None if loop.page_size else loop.kv_base,
+                        inp.prefix_len, mask, H=loop.H, scale=loop.scale, out=loop.out, lse=loop.lse, workspace=ws,
+                        pages=loop.pages())
 
     reps = max(4, min(args.attn_reps, 50))
     attn()
@@ -368,6 +371,7 @@ def run_loop(args, dev):
         "config": {"workload": "config5 verify loop: B=32, H=8, 512+64 bf16, prefix U[2048,65536] growing, "
                                "64 nodes (best-first, top-8, depth<=8), target logits 2048x163840 fp32",
                    "requests": loop.B, "heads": loop.H, "nodes": loop.N, "iterations": K,
+                   "page_size": args.page_size,
                    "cache_tokens_per_iteration": keys / K, "accepted_drafts_per_request_step": acc_sum / (K * loop.B),
                    "attn_flop_per_step": flops / K},
         "cache_tokens_per_s": round(keys / (t_ms * 1e-3), 1),

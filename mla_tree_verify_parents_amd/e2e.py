@@ -11,7 +11,11 @@ keeps the loop's state and bookkeeping:
   the step's compaction, mirrored on the host for the attention's work
   plan) and the root token of the next tree (the bonus token of the last
   step: the target's prediction after the deepest accepted node);
-* one cache pool with room for the growth of every step.
+* one cache pool with room for the growth of every step: contiguous (each
+  request owns a fixed range of rows), or paged (page_size > 0: the pool is
+  pages of page_size rows, each request's block table row lists its pages,
+  and pages are taken from a shuffled free list as the request grows --
+  the table edits that go with compaction in a paged cache).
 
 Each iteration draws its inputs (synthetic, seeded; untimed) and runs the
 hot path through the C ABI with one `ddt.verify_step` call.  Inputs per
@@ -82,7 +86,7 @@ class VerifyLoop:
     """State of B requests across verify steps, on `device`."""
 
     def __init__(self, B=32, H=8, N=64, prefix_range=(2048, 65536), steps=100, vocab=synth.K2_VOCAB, K=8,
-                 D=8, sigma=3.0, alpha=0.6, d_lat=512, d_rope=64, seed=1005, device="cuda", gap=32):
+                 D=8, sigma=3.0, alpha=0.6, d_lat=512, d_rope=64, seed=1005, device="cuda", gap=32, page_size=0):
         self.B, self.H, self.N, self.steps = B, H, N, steps
         self.vocab, self.K, self.D, self.sigma, self.alpha = vocab, K, D, sigma, alpha
         self.d_lat, self.d_rope = d_lat, d_rope
@@ -100,20 +104,37 @@ class VerifyLoop:
             base[b] = off
             off += int(cap[b]) + gap
         self.capacity = cap
-        self.kv_base_host = base
+        self.kv_base_host = base          # the logical (contiguous) layout: the pool's rows unless paged
+        self.logical_rows = int(off)
         self.P_host = P0.copy()
         self.roots = self.rng.integers(0, vocab, size=B).astype(np.int32)
         dev = self.device
         g = self._gen(-1)
         d_qk = d_lat + d_rope
-        # rows past a request's keys (and the gaps) hold NaN, so a read past
-        # the keys would show in the outputs
-        self.pool = torch.full((int(off), d_qk), float("nan"), dtype=torch.bfloat16, device=dev)
+        self.page_size = page_size
+        if page_size:
+            if page_size < 32 or page_size & (page_size - 1):
+                raise ValueError("page_size must be a power of two >= 32")
+            per_req = (cap + page_size - 1) // page_size
+            n_pages = int(per_req.sum())
+            self.free_pages = list(self.rng.permutation(n_pages).astype(np.int32))
+            self.table_host = np.zeros((B, int(per_req.max())), np.int32)
+            self.n_pages = np.zeros(B, np.int64)
+            self.table_dev = torch.zeros((B, int(per_req.max())), dtype=torch.int32, device=dev)
+            pool_rows = n_pages * page_size
+        else:
+            pool_rows = int(off)
+        # rows past a request's keys (and the gaps, and pages not yet handed
+        # out) hold NaN, so a read past the keys would show in the outputs
+        self.pool = torch.full((pool_rows, d_qk), float("nan"), dtype=torch.bfloat16, device=dev)
+        if page_size:
+            self._ensure_slots(P0.astype(np.int64))
         for b in range(B):
             rows = int(P0[b])
             if rows:
-                self.pool[int(base[b]): int(base[b]) + rows] = torch.randn(
-                    (rows, d_qk), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+                r = torch.from_numpy(self.rows_of(b, np.arange(rows))).to(dev)
+                self.pool[r] = torch.randn((rows, d_qk), generator=g, device=dev, dtype=torch.float32).to(
+                    torch.bfloat16)
         self.kv_base = torch.from_numpy(base).to(dev)
         self.prefix_dev = torch.from_numpy(P0.copy()).to(dev)
         rows = B * N * H
@@ -129,6 +150,42 @@ class VerifyLoop:
         self.logits = torch.empty((B * N, vocab), dtype=torch.float32, device=dev)
         self.q = torch.empty((rows, d_qk), dtype=torch.bfloat16, device=dev)
         self.step_no = 0
+
+    # ------------------------------------------------------------- cache ----
+    def rows_of(self, b: int, t: np.ndarray) -> np.ndarray:
+        """Pool rows of request b's cache slots t."""
+        t = np.asarray(t, np.int64)
+        if not self.page_size:
+            return self.kv_base_host[b] + t
+        ps = self.page_size
+        return self.table_host[b, t // ps].astype(np.int64) * ps + t % ps
+
+    def _ensure_slots(self, T: np.ndarray):
+        """Paged: hand out pages until request b has at least T[b] slots."""
+        grew = False
+        for b in range(self.B):
+            while self.n_pages[b] * self.page_size < T[b]:
+                if not self.free_pages:
+                    raise RuntimeError("cache capacity exceeded")
+                self.table_host[b, self.n_pages[b]] = self.free_pages.pop()
+                self.n_pages[b] += 1
+                grew = True
+        if grew:
+            self.table_dev.copy_(torch.from_numpy(self.table_host))
+
+    def to_logical(self, pool_host: np.ndarray) -> np.ndarray:
+        """A host copy of the pool in the logical layout (request b's slot t
+        at row kv_base_host[b] + t; slots without a page are NaN)."""
+        if not self.page_size:
+            return pool_host
+        out = np.full((self.logical_rows, pool_host.shape[1]), pool_host.dtype.type(0x7FC0), pool_host.dtype)
+        for b in range(self.B):
+            t = np.arange(int(self.n_pages[b]) * self.page_size)
+            out[self.kv_base_host[b] + t] = pool_host[self.rows_of(b, t)]
+        return out
+
+    def pages(self):
+        return (self.table_dev, self.page_size) if self.page_size else None
 
     # ------------------------------------------------------------ inputs ----
     def _gen(self, step: int) -> torch.Generator:
@@ -162,8 +219,9 @@ class VerifyLoop:
         P = self.P_host.copy()
         if np.any(P.astype(np.int64) + N > self.capacity):
             raise RuntimeError("cache capacity exceeded")
-        node_rows = torch.from_numpy((self.kv_base_host[:, None] + P[:, None] + np.arange(N)[None, :])
-                                     .reshape(-1)).to(dev)
+        if self.page_size:
+            self._ensure_slots(P.astype(np.int64) + N)
+        node_rows = torch.from_numpy(np.concatenate([self.rows_of(b, P[b] + np.arange(N)) for b in range(B)])).to(dev)
         d_qk = self.d_lat + self.d_rope
         lat = torch.randn((B * N, d_qk), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
         self.pool.index_copy_(0, node_rows, lat)
@@ -178,7 +236,7 @@ class VerifyLoop:
     # -------------------------------------------------------------- step ----
     def workspace_for(self, P: np.ndarray):
         desc = ddt.attn_desc(self.q[:, : self.d_lat], self.q[:, self.d_lat:], self.ckv(), self.kpe(), B=self.B,
-                             H=self.H, N=self.N, scale=self.scale)
+                             H=self.H, N=self.N, scale=self.scale, pages=self.pages())
         need = ddt.verify_workspace_bytes(desc, P)
         if need > self.ws.numel():
             self.ws = torch.empty((need,), dtype=torch.uint8, device=self.device)
@@ -192,10 +250,11 @@ class VerifyLoop:
         mask = None
         if self.N > 128:
             mask = ddt.build_mask(inp.parents_dev, stream=stream)[0]
-        ddt.verify_step(inp.q[:, :dl], inp.q[:, dl:], self.ckv(), self.kpe(), self.kv_base, inp.prefix_len, mask,
+        kv_base = None if self.page_size else self.kv_base
+        ddt.verify_step(inp.q[:, :dl], inp.q[:, dl:], self.ckv(), self.kpe(), kv_base, inp.prefix_len, mask,
                         inp.logits, inp.draft_dev, inp.parents_dev, self.prefix_dev, H=self.H, scale=self.scale,
                         out=self.out, lse=self.lse, workspace=ws, idx=self.idx, argmax_workspace=self.am_ws,
-                        accept_len=self.acc, path=self.path, tokens=self.tok, stream=stream)
+                        accept_len=self.acc, path=self.path, tokens=self.tok, pages=self.pages(), stream=stream)
         return StepResult(self.out, self.lse, self.idx, self.acc, self.path, self.tok)
 
     def advance(self, res: StepResult):

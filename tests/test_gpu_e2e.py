@@ -16,15 +16,15 @@ pytestmark = pytest.mark.gpu
 
 
 def _check_steps(orc, loop, steps, sample_rows=None):
-    host_pool = to_host(loop.pool)
+    host_pool = loop.to_logical(to_host(loop.pool))     # the mirror, in the logical layout
     base = loop.kv_base_host
     dl = loop.d_lat
     B, N, H = loop.B, loop.N, loop.H
     accepted = []
     for s in range(steps):
         inp = loop.make_inputs()
-        rows = to_host(inp.node_rows).astype(np.int64)
-        host_pool[rows] = to_host(loop.pool[inp.node_rows])      # the step's node latents (inputs)
+        slots = (base[:, None] + inp.prefix_len[:, None] + np.arange(N)[None, :]).reshape(-1)
+        host_pool[slots] = to_host(loop.pool[inp.node_rows])     # the step's node latents (inputs)
         qh = to_host(inp.q)
         logits_h = to_host(inp.logits)
         P = inp.prefix_len.copy()
@@ -44,7 +44,7 @@ def _check_steps(orc, loop, steps, sample_rows=None):
         assert (to_host(res.idx).reshape(B, N) == t_ref).all(), s
         assert (to_host(res.accept_len) == oa).all() and (to_host(res.path) == op).all(), s
         assert (to_host(res.tokens) == ot).all(), s
-        dev_pool = to_host(loop.pool)
+        dev_pool = loop.to_logical(to_host(loop.pool))
         assert (dev_pool.view(np.uint8) == host_pool.view(np.uint8)).all(), s
         acc = loop.advance(res)
         assert (loop.P_host == opl).all(), s
@@ -74,3 +74,16 @@ def test_loop_end_to_end_shape(orc):
     rng = np.random.default_rng(0)
     rows = np.sort(rng.choice(loop.B * loop.N * loop.H, 64, replace=False))
     _check_steps(orc, loop, 2, sample_rows=rows)
+
+
+@pytest.mark.parametrize("page_size", [32, 256])
+def test_loop_paged_every_row(orc, page_size):
+    """The small loop on a paged cache: pages handed out from a shuffled
+    free list as the requests grow; attention, acceptance and compaction go
+    through the block table, checked every step against the oracle on the
+    logical cache (the whole cache, bit for bit)."""
+    loop = e2e.VerifyLoop(B=4, H=2, N=16, prefix_range=(30, 300), steps=12, vocab=3000, K=4, D=4, seed=7,
+                          page_size=page_size)
+    P0 = loop.P_host.copy()
+    acc = _check_steps(orc, loop, 12)
+    assert (loop.P_host == P0 + (acc + 1).sum(axis=0)).all()
