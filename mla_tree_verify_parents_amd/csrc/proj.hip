@@ -28,6 +28,13 @@
 //    LDS tile and written back as 16-byte stores along the output rows.
 //  * Workgroups of one (head, column block) are consecutive on one XCD
 //    (xcd_logical_block), so its L2 serves their shared weight fragments.
+//  * Few rows (a grid of fewer workgroups than CUs, e.g. one verify step's
+//    64 tree nodes): the reduction is split instead.  A workgroup owns 64
+//    rows x 32 columns of one head; each wavefront takes a quarter of the
+//    k-steps with its A fragments loaded straight from the rows (16
+//    contiguous bytes per lane), and the four partial tiles are summed
+//    through LDS -- 4x (n_out/128 x more) workgroups, a quarter of the
+//    dependent MFMA chain each.
 #include "common.h"
 
 namespace {
@@ -141,11 +148,96 @@ __global__ __launch_bounds__(kThreads) void proj_kernel(const uint16_t* __restri
 }
 
 template <int K>
+__global__ __launch_bounds__(kThreads) void proj_splitk_kernel(const uint16_t* __restrict__ x, int64_t ld_x,
+                                                               const bf16x8* __restrict__ wp, int M, int H,
+                                                               int n_out, uint16_t* __restrict__ y, int64_t ld_y,
+                                                               int n_tt, int n_nb) {
+    static_assert(K % 64 == 0 && K <= kMaxK, "reduction depth: four equal shares of whole k-steps");
+    constexpr int KS = K / 16, KQ = KS / 4;    // k-steps, and each wavefront's share
+    constexpr int PROW = 32 * 4 + 4;           // padded LDS row of a partial tile (bytes: 32 fp32 + 4)
+    __shared__ __attribute__((aligned(16))) float part[4][kRows * PROW / 4 + 4];
+
+    const int nblocks = H * n_nb * n_tt;
+    const int wg = ddt::xcd_logical_block(blockIdx.x, nblocks);
+    const int tt = wg % n_tt;
+    const int nb = (wg / n_tt) % n_nb;         // 32-column tile
+    const int h = wg / (n_tt * n_nb);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int t0 = tt * kRows;
+
+    // A fragment of row group rg, k-step ks: row t0 + 32 rg + lane%32, k = 16 ks + 8 (lane/32) .. +8
+    const bf16x8* wf = wp + ((int64_t)(h * (n_out / 32) + nb) * KS) * 64 + lane;
+    const int ra = t0 + (lane & 31), rb = ra + 32;
+    const uint16_t* xa = x + ((int64_t)ra * H + h) * ld_x + (lane >> 5) * 8;
+    const uint16_t* xb = x + ((int64_t)rb * H + h) * ld_x + (lane >> 5) * 8;
+    floatx16 acc0 = {}, acc1 = {};
+#pragma unroll
+    for (int j = 0; j < KQ; ++j) {
+        const int ks = wave * KQ + j;
+        const bf16x8 b = wf[ks * 64];
+        bf16x8 a0 = {}, a1 = {};
+        if (ra < M) a0 = *reinterpret_cast<const bf16x8*>(xa + ks * 16);
+        if (rb < M) a1 = *reinterpret_cast<const bf16x8*>(xb + ks * 16);
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b, acc1, 0, 0, 0);
+    }
+    // partial tile of this wavefront: C[i][j] in lane j + 32*((i/4)%2), register 4*(i/8) + i%4
+    {
+        float* pt = part[wave];
+        const int g = lane >> 5, j = lane & 31;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int i = 8 * (r >> 2) + 4 * g + (r & 3);
+            pt[i * (PROW / 4) + j] = acc0[r];
+            pt[(32 + i) * (PROW / 4) + j] = acc1[r];
+        }
+    }
+    __syncthreads();
+    // 64 rows x 32 columns: each thread sums 8 consecutive columns of one row
+    const int row = tid >> 2, c0 = (tid & 3) * 8;
+    const int t = t0 + row;
+    if (t < M) {
+        uint32_t o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float v[2];
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int off = row * (PROW / 4) + c0 + 2 * e + k;
+                v[k] = (part[0][off] + part[1][off]) + (part[2][off] + part[3][off]);
+            }
+            o[e] = (uint32_t)bf16_bits(v[0]) | ((uint32_t)bf16_bits(v[1]) << 16);
+        }
+        *reinterpret_cast<u32x4*>(y + ((int64_t)t * H + h) * ld_y + nb * 32 + c0) = u32x4{o[0], o[1], o[2], o[3]};
+    }
+}
+
+int num_cus() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+template <int K>
 int launch_proj(const uint16_t* x, int64_t ld_x, const bf16x8* wp, int M, int H, int n_out, uint16_t* y,
                 int64_t ld_y, hipStream_t s) {
     const int n_tt = (M + kRows - 1) / kRows, n_cb = (n_out + kCols - 1) / kCols;
     const int64_t nblocks = (int64_t)H * n_cb * n_tt;
     if (nblocks > 0x7fffffff) return DDT_EINVAL;
+    if (nblocks < num_cus()) {  // too few workgroups to fill the chip: split the reduction
+        const int n_nb = n_out / 32;
+        hipLaunchKernelGGL(proj_splitk_kernel<K>, dim3((unsigned)((int64_t)H * n_nb * n_tt)), dim3(kThreads), 0, s,
+                           x, ld_x, wp, M, H, n_out, y, ld_y, n_tt, n_nb);
+        DDT_CHECK_LAUNCH();
+        return DDT_OK;
+    }
     hipLaunchKernelGGL(proj_kernel<K>, dim3((unsigned)nblocks), dim3(kThreads), 0, s, x, ld_x, wp, M, H, n_out, y,
                        ld_y, n_tt, n_cb);
     DDT_CHECK_LAUNCH();

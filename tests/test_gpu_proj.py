@@ -3,7 +3,9 @@
 whole chain q_nope -> q_lat -> tree-verify attention -> o against the
 oracle's chain.
 
-Bar: rel-L2 <= 1e-2 over the output (bf16 inputs, fp32 accumulation), and
+Shapes whose 64-row x 128-column grid would leave CUs idle run the
+split-reduction variant (small M), the others the row-tile variant; both
+are covered.  Bar: rel-L2 <= 1e-2 over the output (bf16 inputs, fp32 accumulation), and
 per element |y - ref| <= 2^-8 |ref| + 2^-16 sum_k |x_k W_kn| (the bf16
 rounding of the result plus the fp32 summation)."""
 import numpy as np
@@ -40,6 +42,7 @@ def _check(orc, x_bits, w_bits, y_bits):
     (1, 8, 128, 512),      # one token
     (100, 3, 64, 96),      # ragged token tile, a column block of 96
     (70, 2, 256, 32),      # one 32-column tile
+    (6000, 3, 64, 96),     # enough rows for the 128-column workgroups, with a partial column block
     (0, 8, 128, 512),      # nothing to do
 ])
 def test_head_proj(orc, M, H, K, n_out):
