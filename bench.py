@@ -289,12 +289,14 @@ def main():
 
 def run_loop(args, dev):
     """Configuration 5: the verify loop.  Every iteration draws its inputs
-    (untimed: draft candidates, best-first trees, node latents, queries,
-    target logits), runs the hot path (one ddt_verify_step call: ancestor
-    bits, attention, argmax, acceptance, compaction, length update; two
-    launches) between HIP events, then advances the loop (the bonus token is
-    the next root; the host mirrors the grown lengths).  `value` is the
-    attention FLOPs of all timed iterations over their summed device time."""
+    (untimed: draft logits, node latents, queries, target logits planted on
+    the tree), runs the draft stage on the device (top-8 per depth and the
+    best-first trees; timed with HIP events), then the hot path (one
+    ddt_verify_step call: ancestor bits, attention, argmax, acceptance,
+    compaction, length update; two launches; timed with HIP events), then
+    advances the loop (the bonus token is the next root; the host mirrors the
+    grown lengths).  A step's time is the two stages' device time; `value` is
+    the attention FLOPs of all timed iterations over their summed step time."""
     import torch
 
     from mla_tree_verify_parents_amd import ddt, e2e, synth
@@ -303,9 +305,12 @@ def run_loop(args, dev):
     loop = e2e.VerifyLoop(steps=W + K, page_size=args.page_size)
     stream = torch.cuda.current_stream()
     t_ms, flops, keys, acc_sum = 0.0, 0, 0, 0
+    host_s, plan_s, draft_ms, verify_ms = 0.0, 0.0, 0.0, 0.0
     snap = None
     for it in range(W + K):
-        inp = loop.make_inputs()
+        h0 = time.perf_counter()
+        inp = loop.make_inputs()       # draws on the device; the best-first trees are built on the host
+        h1 = time.perf_counter()
         if it == 0 and not args.no_cpu_baseline:  # (a warmup iteration unless W == 0)
             snap = (synth.Workload(name="config5", B=loop.B, H=loop.H, N=loop.N, d_lat=loop.d_lat,
                                    d_rope=loop.d_rope, dtype="bf16", scale=loop.scale,
@@ -319,12 +324,18 @@ def run_loop(args, dev):
         # so e0..e1 is the step's device time
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
+        p0 = time.perf_counter()
         res = loop.run_step(inp)
+        p1 = time.perf_counter()
         e1.record(stream)
         torch.cuda.synchronize()
         acc = loop.advance(res)
         if it >= W:
-            t_ms += e0.elapsed_time(e1)
+            host_s += h1 - h0
+            plan_s += p1 - p0
+            draft_ms += inp.draft_ms
+            verify_ms += e0.elapsed_time(e1)
+            t_ms += inp.draft_ms + e0.elapsed_time(e1)
             flops += inp.visible_pairs(loop.H) * FLOP_PER_PAIR
             keys += int(inp.prefix_len.sum()) + loop.B * loop.N
             acc_sum += int(acc.sum())
@@ -382,6 +393,14 @@ def run_loop(args, dev):
                      "algorithmic_bytes": attn_bytes,
                      "achieved_GBps": round(attn_bytes / (ms_attn * 1e-3) / 1e9, 1)},
         "draft_step": draft,
+        "stage_ms_per_iteration": {"draft_topk_and_trees": round(draft_ms / K, 5),
+                                   "verify_step": round(verify_ms / K, 5),
+                                   "note": "device time; ms_per_step is their sum"},
+        "host_ms_per_iteration": {"inputs_and_trees": round(host_s * 1e3 / K, 3),
+                                  "plan_and_enqueue": round(plan_s * 1e3 / K, 3),
+                                  "note": "host wall time: drawing the inputs and running the draft stage (with "
+                                          "the host copies the input generator needs), then planning + "
+                                          "enqueueing the verify step's two launches"},
     }
     add_peaks(res, args, dev)
     if snap is not None:

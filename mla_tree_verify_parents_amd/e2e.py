@@ -22,9 +22,11 @@ hot path through the C ABI with one `ddt.verify_step` call.  Inputs per
 step, as the end-to-end configuration lays them out:
 
 * draft logits N(0, sigma^2) over the vocabulary, per request and depth; per
-  depth the top-K tokens and their log-probabilities (device, torch);
-* a best-first draft tree of N nodes from those candidates (host,
-  `synth.best_first_tree`), rooted at the request's root token;
+  depth the top-K tokens and their log-probabilities, and the best-first
+  draft tree of N nodes from those candidates rooted at the request's root
+  token -- on the device by the library (`ddt_draft_topk`,
+  `ddt_best_first_tree`; the loop's draft stage, timed on its own), or on
+  the host (torch top-k and `synth.best_first_tree`) with device_draft=False;
 * the node latents c_kv | k_pe (N(0,1), bf16) written at cache slots
   P .. P+N-1, and the absorbed queries q_lat | q_pe (N(0,1), bf16);
 * target logits N(0,1) with +10 on a planted token per node: with
@@ -59,6 +61,10 @@ class StepInputs:
     logits: torch.Tensor     # [B*N, vocab] fp32 (device)
     parents_dev: torch.Tensor
     draft_dev: torch.Tensor
+    roots: np.ndarray = None         # [B] root tokens of the trees (host)
+    cand_ids: np.ndarray = None      # [B, D, K] draft candidates (host copies; device draft stage only)
+    cand_lp: np.ndarray = None       # [B, D, K] fp32 log-probabilities
+    draft_ms: float = 0.0            # device time of the draft stage (top-k + trees)
 
     def visible_pairs(self, H: int) -> int:
         """Visible (query row, key) pairs of the step: prefix plus ancestors and self."""
@@ -86,7 +92,8 @@ class VerifyLoop:
     """State of B requests across verify steps, on `device`."""
 
     def __init__(self, B=32, H=8, N=64, prefix_range=(2048, 65536), steps=100, vocab=synth.K2_VOCAB, K=8,
-                 D=8, sigma=3.0, alpha=0.6, d_lat=512, d_rope=64, seed=1005, device="cuda", gap=32, page_size=0):
+                 D=8, sigma=3.0, alpha=0.6, d_lat=512, d_rope=64, seed=1005, device="cuda", gap=32, page_size=0,
+                 device_draft=True):
         self.B, self.H, self.N, self.steps = B, H, N, steps
         self.vocab, self.K, self.D, self.sigma, self.alpha = vocab, K, D, sigma, alpha
         self.d_lat, self.d_rope = d_lat, d_rope
@@ -149,6 +156,13 @@ class VerifyLoop:
         self.ws = torch.empty((1,), dtype=torch.uint8, device=dev)
         self.logits = torch.empty((B * N, vocab), dtype=torch.float32, device=dev)
         self.q = torch.empty((rows, d_qk), dtype=torch.bfloat16, device=dev)
+        self.device_draft = device_draft
+        if device_draft:
+            self.cand_ids = torch.empty((B * D, K), dtype=torch.int32, device=dev)
+            self.cand_lp = torch.empty((B * D, K), dtype=torch.float32, device=dev)
+            self.topk_ws = torch.empty((max(16, ddt.draft_topk_workspace_bytes(B * D, vocab, K)),),
+                                       dtype=torch.uint8, device=dev)
+            self.tree_out = [torch.empty((B, N), dtype=torch.int32, device=dev) for _ in range(3)]
         self.step_no = 0
 
     # ------------------------------------------------------------- cache ----
@@ -206,14 +220,32 @@ class VerifyLoop:
         g = self._gen(self.step_no)
         # per request and depth: top-K of N(0, sigma^2) draft logits and their log-softmax
         x = torch.randn((B, D, V), generator=g, device=dev, dtype=torch.float32) * self.sigma
-        top = torch.topk(x, K, dim=-1)
-        lp = (top.values - torch.logsumexp(x, dim=-1, keepdim=True)).cpu().numpy()
-        ids = top.indices.to(torch.int32).cpu().numpy()
+        roots = self.roots.copy()
+        cand_ids = cand_lp = None
+        draft_ms = 0.0
+        if self.device_draft:
+            # the draft stage on the device: top-K per (request, depth), then the trees
+            roots_dev = torch.from_numpy(roots).to(dev)
+            stream = torch.cuda.current_stream(dev)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            ddt.draft_topk(x.view(B * D, V), K, self.cand_ids, self.cand_lp, self.topk_ws)
+            par_d, tok_d, _ = ddt.best_first_tree(self.cand_ids.view(B, D, K), self.cand_lp.view(B, D, K), roots_dev,
+                                                  N - 1, *self.tree_out)
+            e1.record(stream)
+            parents, draft = par_d.cpu().numpy(), tok_d.cpu().numpy()   # (synchronises)
+            draft_ms = e0.elapsed_time(e1)
+            cand_ids = self.cand_ids.view(B, D, K).cpu().numpy()
+            cand_lp = self.cand_lp.view(B, D, K).cpu().numpy()
+        else:
+            top = torch.topk(x, K, dim=-1)
+            lp = (top.values - torch.logsumexp(x, dim=-1, keepdim=True)).cpu().numpy()
+            ids = top.indices.to(torch.int32).cpu().numpy()
+            parents = np.empty((B, N), np.int32)
+            draft = np.empty((B, N), np.int32)
+            for b in range(B):
+                parents[b], draft[b], _ = synth.best_first_tree(ids[b], lp[b], N - 1, int(roots[b]))
         del x
-        parents = np.empty((B, N), np.int32)
-        draft = np.empty((B, N), np.int32)
-        for b in range(B):
-            parents[b], draft[b], _ = synth.best_first_tree(ids[b], lp[b], N - 1, int(self.roots[b]))
         targets = synth.planted_targets(self.rng, parents, draft, V, self.alpha)
         # node latents at slots P .. P+N-1 and the queries
         P = self.P_host.copy()
@@ -231,7 +263,8 @@ class VerifyLoop:
         rows = torch.arange(B * N, device=dev)
         self.logits[rows, torch.from_numpy(targets.reshape(-1).astype(np.int64)).to(dev)] += BOOST
         return StepInputs(self.step_no, parents, draft, targets, P, node_rows, self.q, self.logits,
-                          torch.from_numpy(parents).to(dev), torch.from_numpy(draft).to(dev))
+                          torch.from_numpy(parents).to(dev), torch.from_numpy(draft).to(dev), roots, cand_ids, cand_lp,
+                          draft_ms)
 
     # -------------------------------------------------------------- step ----
     def workspace_for(self, P: np.ndarray):

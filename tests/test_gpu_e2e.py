@@ -1,7 +1,9 @@
 """GPU parity of the verify loop (the end-to-end configuration): every step
-of `e2e.VerifyLoop` -- attention, argmax, acceptance, compaction and the
-length update in one `ddt_verify_step` call, then the loop's bookkeeping --
-against the fp64 oracle run on host copies of the same inputs, with the
+of `e2e.VerifyLoop` -- the draft stage (device top-k and best-first trees,
+checked against the oracle's builder on the same candidates), then
+attention, argmax, acceptance, compaction and the length update in one
+`ddt_verify_step` call, then the loop's bookkeeping -- against the fp64
+oracle run on host copies of the same inputs, with the
 host mirror of the cache pool carried from step to step by the oracle's
 compaction.  Discrete results and the whole pool must match bit for bit;
 attention outputs within relative L2 1e-2 (bf16 inputs)."""
@@ -25,6 +27,10 @@ def _check_steps(orc, loop, steps, sample_rows=None):
         inp = loop.make_inputs()
         slots = (base[:, None] + inp.prefix_len[:, None] + np.arange(N)[None, :]).reshape(-1)
         host_pool[slots] = to_host(loop.pool[inp.node_rows])     # the step's node latents (inputs)
+        if inp.cand_ids is not None:                             # trees built on the device
+            for b in range(B):
+                tp, tt, _ = orc.best_first_tree(inp.cand_ids[b], inp.cand_lp[b], N - 1, int(inp.roots[b]))
+                assert (inp.parents[b] == tp).all() and (inp.draft_ids[b] == tt).all(), (s, b)
         qh = to_host(inp.q)
         logits_h = to_host(inp.logits)
         P = inp.prefix_len.copy()
@@ -87,3 +93,10 @@ def test_loop_paged_every_row(orc, page_size):
     P0 = loop.P_host.copy()
     acc = _check_steps(orc, loop, 12)
     assert (loop.P_host == P0 + (acc + 1).sum(axis=0)).all()
+
+
+def test_loop_host_trees(orc):
+    """The loop with its trees built on the host (torch top-k, host builder)."""
+    loop = e2e.VerifyLoop(B=3, H=2, N=16, prefix_range=(30, 300), steps=4, vocab=3000, K=4, D=4, seed=9,
+                          device_draft=False)
+    _check_steps(orc, loop, 4)

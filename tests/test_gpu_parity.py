@@ -380,6 +380,7 @@ def test_attn_config3_ragged_small(orc):
     (3, dict(B=3, N=1, prefix_range=(0, 40))),
     (3, dict(B=2, H=1, N=1024, prefix_range=(31, 33))),
     (2, dict(H=3, N=7, prefix=1, with_logits=False)),
+    (3, dict(B=128, N=4, prefix_range=(0, 300))),   # the maximum batch, ragged prefixes
 ])
 def test_attn_edge_cases(orc, cfg, over):
     _attn_check(orc, synth.workload(cfg, **over), kv_chunks=(0, 32))
