@@ -36,9 +36,9 @@
 //  * Each request's key range is cut into splits (the host picks the chunk
 //    that minimises an estimate of the launch's finish time) and work items
 //    are dealt to the XCDs so that row tiles of one split share an L2.
-//    Split partials (normalised, in the input dtype, MFMA register order)
-//    and their log2-sum-exp go to the workspace; verify_combine merges
-//    them.  A request with one split writes its output directly.
+//    Split partials (unnormalised, in the input dtype, MFMA register
+//    order) with each row's softmax reference and row sum go to the
+//    workspace; verify_combine weighs, sums and normalises them.  A request with one split writes its output directly.
 //  * Optional co-tasks: target-argmax workgroups on the CUs the attention
 //    leaves idle (verify_split), and acceptance + compaction workgroups
 //    beside the merge (verify_combine).
@@ -442,8 +442,8 @@ struct VerifyParams {
     const int32_t* parents;     // then each row's bits come from the parents (N <= 128)
     void* out;
     float* lse;
-    void* ws_o;     // [slot][row group][DL/32][4][64][4] in the input dtype, normalised partial outputs
-    float* ws_lse;  // [slot][ROWS_WG] fp32, log2-domain partial log-sum-exp
+    void* ws_o;     // [slot][row group][DL/32][4][64][4] in the input dtype, unnormalised partial outputs
+    float2* ws_ml;  // [slot][ROWS_WG] (softmax reference m, log2 domain; row sum l) of the unnormalised partials
     int64_t ld_ql, ld_qp, ld_ckv, ld_kpe;
     int B, H, N, W, rows, row_tiles, chunk, total_wg;
     float scale_log2;
@@ -1146,16 +1146,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         const bool ok = r < p.rows;
         const int64_t qr = (int64_t)b * p.rows + (ok ? r : 0);
         const float l = lsum[rb][0];
-        const float inv = l > 0.f ? 1.f / l : 0.f;
+        const bool whole = p.nsplit[b] == 1;  // (uniform)
         if (half == rb && g == 0 && ok) {
-            const float lse2 = l > 0.f ? s_mref[rb * 32 + l32] + __log2f(l) : -INFINITY;
-            if (p.nsplit[b] == 1)
-                p.lse[qr] = lse2 * kLn2;
-            else
-                p.ws_lse[(size_t)wl * ROWS_WG + rb * 32 + l32] = lse2;
+            const float mr = s_mref[rb * 32 + l32];
+            if (whole)
+                p.lse[qr] = (l > 0.f ? mr + __log2f(l) : -INFINITY) * kLn2;
+            else  // the merge weighs the unnormalised partial by 2^(m - M) and divides by the weighed sums
+                p.ws_ml[(size_t)wl * ROWS_WG + rb * 32 + l32] =
+                    l > 0.f ? make_float2(mr, l) : make_float2(-INFINITY, 0.f);
         }
+        if (whole) {  // final output: normalise in place
+            const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) scale_acc(o[rb][c], inv);
+            for (int c = 0; c < NCH; ++c) scale_acc(o[rb][c], inv);
+        }
         asm volatile("s_nop 7" ::: "memory");
         if (!ok) continue;
         if (p.nsplit[b] == 1) {
@@ -1171,8 +1175,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 }
             }
         } else {
-            // partials in the input dtype: one 64-lane store writes 64 x 4
-            // consecutive elements
+            // unnormalised partials in the input dtype (the merge divides):
+            // one 64-lane store writes 64 x 4 consecutive elements
             T* ws = static_cast<T*>(p.ws_o) + (size_t)wl * (ROWS_WG * DL) + (size_t)rb * (32 * DL) +
                     (size_t)half * NCH * (4 * 64 * 4);
 #pragma unroll
@@ -1189,9 +1193,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     }
 }
 
-// Merge the key splits of every row of multi-split requests:
-//   M = max_s lse_s, w_s = 2^(lse_s - M), out = sum_s w_s o_s / sum_s w_s,
-//   lse = (M + log2 sum_s w_s) ln 2.
+// Merge the key splits of every row of multi-split requests.  Split s left
+// its unnormalised output O_s = sum_t 2^(x_t - m_s) c_kv[t] (x: scaled score
+// in log2 units, m_s: the split's softmax reference) and its row sum
+// l_s = sum_t 2^(x_t - m_s):
+//   M = max_s m_s, w_s = 2^(m_s - M),
+//   out = sum_s w_s O_s / sum_s w_s l_s,  lse = (M + log2 sum_s w_s l_s) ln 2.
 // One workgroup per (request, row tile, wavefront, 32-column tile of that
 // wavefront); thread (grp, lane) owns the 4 consecutive outputs that the
 // split kernel's lane `lane` stored at group `grp`.
@@ -1233,18 +1240,18 @@ __global__ __launch_bounds__(256) void verify_combine(const VerifyParams p) {
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     float wsum = 0.f;
     for (int s0 = 0; s0 < ns; s0 += KB) {
-        float l[KB];
+        float2 ml[KB];
         float4 v[KB];
 #pragma unroll
         for (int k = 0; k < KB; ++k) {
             const int slot = slot_of(s0 + k);
-            l[k] = p.ws_lse[(size_t)slot * ROWS_WG + prow];
+            ml[k] = p.ws_ml[(size_t)slot * ROWS_WG + prow];
             v[k] = load4<T>(static_cast<const T*>(p.ws_o) + ((size_t)slot * NW + wave) * (NCTW * 4 * 64 * 4) +
                             ((c * 4 + grp) * 64 + lane) * 4);
         }
         float mb = M;
 #pragma unroll
-        for (int k = 0; k < KB; ++k) mb = fmaxf(mb, s0 + k < ns ? l[k] : -INFINITY);
+        for (int k = 0; k < KB; ++k) mb = fmaxf(mb, s0 + k < ns ? ml[k].x : -INFINITY);
         if (mb != M && M != -INFINITY) {  // rescale what earlier batches summed
             const float r = __builtin_amdgcn_exp2f(M - mb);
 #pragma unroll
@@ -1254,12 +1261,12 @@ __global__ __launch_bounds__(256) void verify_combine(const VerifyParams p) {
         M = mb;
 #pragma unroll
         for (int k = 0; k < KB; ++k) {
-            const float w = (s0 + k >= ns || l[k] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(l[k] - M);
+            const float w = (s0 + k >= ns || ml[k].x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ml[k].x - M);
             acc[0] += w * v[k].x;
             acc[1] += w * v[k].y;
             acc[2] += w * v[k].z;
             acc[3] += w * v[k].w;
-            wsum += w;
+            wsum += w * ml[k].y;
         }
     }
     const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
@@ -1286,7 +1293,7 @@ struct Plan {
     int n_blocks = 0;  // attention blocks launched (work items plus padding of the XCD deal)
     bool touch = false;  // the instance that touches tiles into L2
     bool any_split = false;
-    size_t ws_bytes = 0, ws_lse_off = 0;
+    size_t ws_bytes = 0, ws_ml_off = 0;
 };
 
 int check_desc(const ddt_attn_desc* d, const int32_t* prefix_len_host) {
@@ -1499,8 +1506,8 @@ Plan make_plan(const ddt_attn_desc* d, const int32_t* P, VerifyParams* vp) {
     }
     if (pl.any_split) {
         const size_t o = (size_t)pl.total_wg * ROWS_WG * d->d_lat * (size_t)ddt::elem_bytes(d->dtype);
-        pl.ws_lse_off = ddt::round_up(o, 256);
-        pl.ws_bytes = pl.ws_lse_off + ddt::round_up((size_t)pl.total_wg * ROWS_WG * sizeof(float), 256);
+        pl.ws_ml_off = ddt::round_up(o, 256);
+        pl.ws_bytes = pl.ws_ml_off + ddt::round_up((size_t)pl.total_wg * ROWS_WG * sizeof(float2), 256);
     }
     return pl;
 }
@@ -1561,7 +1568,7 @@ int setup_attn(const ddt_attn_desc* d, const void* q_lat, const void* q_pe, cons
         if (workspace == nullptr || workspace_bytes < pl->ws_bytes || !ddt::aligned(workspace, 256))
             return DDT_EWORKSPACE;
         vp->ws_o = workspace;
-        vp->ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl->ws_lse_off);
+        vp->ws_ml = reinterpret_cast<float2*>(static_cast<char*>(workspace) + pl->ws_ml_off);
     }
     vp->q_lat = q_lat;
     vp->q_pe = q_pe;
