@@ -139,7 +139,9 @@ typedef struct {
 } ddt_attn_desc;
 
 /* Workspace bytes ddt_verify_attn needs for this shape and these prefix
- * lengths (host array [B]); may be 0. */
+ * lengths (host array [B]); may be 0.  The workspace must be 256-byte
+ * aligned; it is scratch between the attention's two launches (no zeroing
+ * needed), and concurrent calls must not share one. */
 int ddt_verify_workspace(const ddt_attn_desc* d, const int32_t* prefix_len_host, size_t* bytes);
 
 /*
