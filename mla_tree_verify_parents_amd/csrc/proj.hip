@@ -26,8 +26,10 @@
 //    own 32 columns with two accumulators (rows 0-31 and 32-63).
 //  * The fp32 results are rounded to bf16 (round to nearest even) into an
 //    LDS tile and written back as 16-byte stores along the output rows.
-//  * Workgroups of one (head, column block) are consecutive on one XCD
-//    (xcd_logical_block), so its L2 serves their shared weight fragments.
+//  * Logical workgroups run column block fastest, then token tile, then
+//    head, each XCD taking a contiguous range (xcd_logical_block): the
+//    column blocks of an input tile share its L2 copy, and a head's weights
+//    stay in the L2 of the XCDs that run it.
 //  * Few rows (a grid of fewer workgroups than CUs, e.g. one verify step's
 //    64 tree nodes): the reduction is split instead.  A workgroup owns 64
 //    rows x 32 columns of one head; each wavefront takes a quarter of the
@@ -88,8 +90,8 @@ __global__ __launch_bounds__(kThreads) void proj_kernel(const uint16_t* __restri
 
     const int nblocks = H * n_cb * n_tt;
     const int wg = ddt::xcd_logical_block(blockIdx.x, nblocks);
-    const int tt = wg % n_tt;
-    const int cb = (wg / n_tt) % n_cb;
+    const int cb = wg % n_cb;                  // the column blocks of one input tile run together
+    const int tt = (wg / n_cb) % n_tt;
     const int h = wg / (n_tt * n_cb);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
