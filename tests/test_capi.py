@@ -141,6 +141,9 @@ def test_paged_desc_validation(lib):
     assert lib.ddt_verify_workspace(desc(16, 400), P, ctypes.byref(n)) == -1    # smaller than a key tile
     assert lib.ddt_verify_workspace(desc(1 << 17, 1), P, ctypes.byref(n)) == -1  # larger than 65536
     assert lib.ddt_verify_workspace(desc(0, 0, table=None), P, ctypes.byref(n)) == 0  # contiguous
+    d = ddt.AttnDesc(2, 2, 8, 64, 16, 0, 0.1, 0, 80, 80, 80, 80)                 # fp32 (64, 16) instance
+    d.block_table, d.bt_ld, d.page_size = 1 << 20, 100, 32
+    assert lib.ddt_verify_workspace(ctypes.byref(d), P, ctypes.byref(n)) == -2  # paged: bf16 instance only
 
 
 def test_proj_validation(lib):
