@@ -153,8 +153,11 @@ int ddt_verify_workspace(const ddt_attn_desc* d, const int32_t* prefix_len_host,
  * out rows are contiguous (row stride d_lat).  prefix_len_host [B] is read
  * on the host during the call (it plans the work split); kv_base [B] int64
  * and mask (from ddt_build_mask) are device arrays.  Keys past T_b are never
- * read.  Accumulation and softmax are fp32; probabilities enter the value
- * product in the input dtype.  Requires B <= DDT_MAX_BATCH,
+ * read; nor are tree keys past a row's own node (nodes are numbered
+ * parents-first, so a mask bit j > i is never set by ddt_build_mask, and a
+ * caller-built mask must not set one).  Accumulation and softmax are fp32;
+ * probabilities enter the value product in the input dtype.  Requires
+ * B <= DDT_MAX_BATCH,
  * N <= DDT_MAX_NODES, P_b >= 0.
  */
 int ddt_verify_attn(const ddt_attn_desc* d, const void* q_lat, const void* q_pe, const void* ckv,

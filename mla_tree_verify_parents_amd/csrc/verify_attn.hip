@@ -725,7 +725,7 @@ __host__ __device__ inline bool work_item(const VerifyParams& p, int blk, int& b
 
 constexpr int kMaxSplitPages = 768;  // pages of a paged split, listed in LDS by its prologue
 
-template <typename T, int DL, int DR, bool kArgmax, bool kTouch, bool kPaged>
+template <typename T, int DL, int DR, bool kArgmax, bool kTouch, bool kPaged, bool kClip>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void verify_split(
     const VerifyParams p) {
     using S = Shape<T, DL, DR>;
@@ -755,7 +755,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const int wl = p.wg_begin[b] + split * p.row_tiles + rt;   // partial-output slot
     const int P = p.P[b];
     const int kbeg = split * p.chunk;
-    const int kend = min(kbeg + p.chunk, P + p.N);
+    // kClip (large trees, e.g. prefill chunks): nodes are numbered
+    // parents-first, so a row of node i sees no tree key past P + i; keys
+    // past P + imax + 1 (imax: the last node among this work item's rows)
+    // are invisible to every row here and are not read.  At least one key
+    // stays, fully masked, so a split past imax is an ordinary work item
+    // with an empty partial.
+    const int kend0 = min(kbeg + p.chunk, P + p.N);
+    const int kend =
+        kClip ? __builtin_amdgcn_readfirstlane(
+                    max(kbeg + 1, min(kend0, P + (min(p.rows, (rt + 1) * ROWS_WG) - 1) / p.H + 1)))
+              : kend0;
     const int ntiles = (kend - kbeg + KT - 1) / KT;
     // paged cache: the split's page numbers go to LDS once, so the tile loop
     // reads them in order with its other LDS traffic (a scalar load per tile
@@ -1515,18 +1525,32 @@ Plan make_plan(const ddt_attn_desc* d, const int32_t* P, VerifyParams* vp) {
 template <typename T, int DL, int DR>
 int launch(const VerifyParams& vp, const Plan& pl, int n_argmax, hipStream_t stream) {
     const dim3 grid(pl.n_blocks + n_argmax);
+    // trees of more than 128 nodes (prefill chunks) skip keys past each
+    // work item's last node; the argmax co-task rides with verify-sized trees
+    const bool clip = vp.N > 128 && n_argmax == 0;
     auto split = [&](auto paged) {
         constexpr bool kP = decltype(paged)::value;
         if (n_argmax > 0) {
             if (pl.touch)
-                hipLaunchKernelGGL((verify_split<T, DL, DR, true, true, kP>), grid, dim3(kThreads), 0, stream, vp);
+                hipLaunchKernelGGL((verify_split<T, DL, DR, true, true, kP, false>), grid, dim3(kThreads), 0, stream,
+                                   vp);
             else
-                hipLaunchKernelGGL((verify_split<T, DL, DR, true, false, kP>), grid, dim3(kThreads), 0, stream, vp);
+                hipLaunchKernelGGL((verify_split<T, DL, DR, true, false, kP, false>), grid, dim3(kThreads), 0, stream,
+                                   vp);
+        } else if (clip) {
+            if (pl.touch)
+                hipLaunchKernelGGL((verify_split<T, DL, DR, false, true, kP, true>), grid, dim3(kThreads), 0, stream,
+                                   vp);
+            else
+                hipLaunchKernelGGL((verify_split<T, DL, DR, false, false, kP, true>), grid, dim3(kThreads), 0, stream,
+                                   vp);
         } else {
             if (pl.touch)
-                hipLaunchKernelGGL((verify_split<T, DL, DR, false, true, kP>), grid, dim3(kThreads), 0, stream, vp);
+                hipLaunchKernelGGL((verify_split<T, DL, DR, false, true, kP, false>), grid, dim3(kThreads), 0, stream,
+                                   vp);
             else
-                hipLaunchKernelGGL((verify_split<T, DL, DR, false, false, kP>), grid, dim3(kThreads), 0, stream, vp);
+                hipLaunchKernelGGL((verify_split<T, DL, DR, false, false, kP, false>), grid, dim3(kThreads), 0,
+                                   stream, vp);
         }
     };
     if constexpr (std::is_same<T, uint16_t>::value) {  // paged caches: the bf16 instance

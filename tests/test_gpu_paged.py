@@ -47,31 +47,32 @@ def from_paged(phys, table, ps, w):
     return pool
 
 
-@pytest.mark.parametrize("ps,prefix_range,kv_chunk", [
-    (32, (100, 3000), 0),
-    (64, (100, 3000), 0),
-    (512, (100, 3000), 0),
-    (32, (25000, 32000), 0),          # splits capped at 767 pages: a plan of its own
-    (64, (100, 3000), 1 << 20),       # an explicit chunk past the cap is capped
+@pytest.mark.parametrize("ps,prefix_range,kv_chunk,N", [
+    (32, (100, 3000), 0, 32),
+    (64, (100, 3000), 0, 32),
+    (512, (100, 3000), 0, 32),
+    (32, (25000, 32000), 0, 32),      # splits capped at 767 pages: a plan of its own
+    (64, (100, 3000), 1 << 20, 32),   # an explicit chunk past the cap is capped
+    (64, (100, 1500), 256, 300),      # a large tree: splits end at each work item's last node
 ])
-def test_paged_attention_equals_contiguous(orc, ps, prefix_range, kv_chunk):
+def test_paged_attention_equals_contiguous(orc, ps, prefix_range, kv_chunk, N):
     """Where the paged split fits the contiguous plan the two launches are
     bit-identical; where the page cap shortens the splits, both still
     match the oracle."""
-    w = synth.workload(3, B=2 if prefix_range[0] > 20000 else 4, prefix_range=prefix_range)
+    w = synth.workload(3, B=2 if prefix_range[0] > 20000 or N > 128 else 4, N=N, prefix_range=prefix_range)
     rng = np.random.default_rng(ps)
     phys, table = to_paged(w, ps, rng)
     dw = DevWorkload(w)
     mask = ddt.build_mask(dw.parents)[0]
     out_c, lse_c = ddt.verify_attn(dw.q_lat(), dw.q_pe(), dw.ckv(), dw.kpe(), dw.kv_base, w.prefix_len, mask,
-                                   H=w.H, scale=w.scale)
+                                   H=w.H, scale=w.scale, kv_chunk=kv_chunk if kv_chunk < (1 << 20) else 0)
     pd, td = to_dev(phys), to_dev(table)
     dl = w.d_lat
     out_p, lse_p = ddt.verify_attn(dw.q_lat(), dw.q_pe(), pd[:, :dl], pd[:, dl:], None, w.prefix_len, mask,
                                    H=w.H, scale=w.scale, pages=(td, ps), kv_chunk=kv_chunk)
     torch.cuda.synchronize()
     cap = 767 * ps
-    same_plan = kv_chunk == 0 and int(w.prefix_len.max()) + w.N <= cap
+    same_plan = kv_chunk < (1 << 20) and int(w.prefix_len.max()) + w.N <= cap
     if same_plan:
         assert torch.equal(out_c.view(torch.int16), out_p.view(torch.int16))
         assert torch.equal(lse_c, lse_p)
