@@ -17,10 +17,12 @@
 // candidates and merges the (maximum, sum) pairs into the row's
 // log-sum-exp.  HBM-bound: 4 bytes per logit.
 //
-// ddt_best_first_tree: one wavefront per request.  The frontier lives in
-// LDS; each pop is a wavefront maximum over packed keys (score, then lower
-// depth, then earlier insertion), then one lane writes the node and inserts
-// the first child and the next sibling.  Scores are fp32 sums along the
+// ddt_best_first_tree: one wavefront per request.  Each pop is a wavefront
+// maximum over packed keys (score, then lower depth, then earlier
+// insertion), then the node is written and the first child and the next
+// sibling enter the frontier.  Trees of at most 64 nodes keep the frontier
+// and the nodes in registers (one per lane); larger trees keep the
+// frontier in LDS.  Scores are fp32 sums along the
 // path, as the tree's definition fixes them.
 #include "argmax_scan.h"
 #include "common.h"
@@ -35,10 +37,37 @@ constexpr int64_t kMaxDraftVocab = (int64_t)kTopkChunk * kTopkThreads * kPerThre
 
 __device__ inline uint64_t umax(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
+// One step of a wavefront maximum of 64-bit keys by DPP: every lane takes the
+// larger of its key and the key of the lane the DPP control names (lanes
+// with no source, or outside row_mask, keep theirs).
+template <int kCtrl, int kRowMask>
+__device__ inline uint64_t dpp_max_step(uint64_t v) {
+    const int lo = (int)(uint32_t)v, hi = (int)(uint32_t)(v >> 32);
+    const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, kCtrl, kRowMask, 0xf, false);
+    const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, kCtrl, kRowMask, 0xf, false);
+    const uint64_t o = ((uint64_t)ohi << 32) | olo;
+    return o > v ? o : v;
+}
+
+// Wavefront maximum of 64-bit keys, returned uniform: prefix maxima inside
+// each row of 16 lanes (row_shr 1, 2, 4, 8), then row 0's and row 2's last
+// lane into rows 1 and 3 (row_bcast:15), then lane 31 into rows 2 and 3
+// (row_bcast:31): lane 63 holds the maximum.
+__device__ inline uint64_t wave_max_u64(uint64_t v) {
+    v = dpp_max_step<0x111, 0xf>(v);
+    v = dpp_max_step<0x112, 0xf>(v);
+    v = dpp_max_step<0x114, 0xf>(v);
+    v = dpp_max_step<0x118, 0xf>(v);
+    v = dpp_max_step<0x142, 0xa>(v);
+    v = dpp_max_step<0x143, 0xc>(v);
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+    return ((uint64_t)hi << 32) | lo;
+}
+
 // Workgroup maximum of one 64-bit key per thread, returned to every thread.
 __device__ inline uint64_t block_max_all(uint64_t v, uint64_t* red) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = umax(v, __shfl_xor(v, o, ddt::kWave));
+    v = wave_max_u64(v);
     const int wave = threadIdx.x / ddt::kWave;
     __syncthreads();  // the previous round's readers are done with red[]
     if ((threadIdx.x & 63) == 0) red[wave] = v;
@@ -274,6 +303,94 @@ __global__ __launch_bounds__(64) void best_first_kernel(const int32_t* __restric
     }
 }
 
+// Trees of at most 64 nodes: the frontier never holds more than 64
+// candidates (a pop adds at most one net), so lane l keeps candidate l in
+// registers and lane n keeps node n.  A pop is a wavefront maximum over the
+// same packed keys, the winner's fields broadcast from its lane; the first
+// child and then the next sibling take the lowest free lanes.  Same
+// arithmetic and order as best_first_kernel, so the trees are identical.
+__global__ __launch_bounds__(64) void best_first_wave_kernel(const int32_t* __restrict__ ids,
+                                                            const float* __restrict__ lp, int D, int K, int budget,
+                                                            const int32_t* __restrict__ roots,
+                                                            int32_t* __restrict__ parents,
+                                                            int32_t* __restrict__ tokens,
+                                                            int32_t* __restrict__ depth) {
+    __shared__ float s_lp[kTreeMaxDK];
+    __shared__ int32_t s_id[kTreeMaxDK];
+    const int b = blockIdx.x, lane = threadIdx.x;
+    const int DK = D * K;
+    for (int i = lane; i < DK; i += 64) {
+        s_lp[i] = lp[(int64_t)b * DK + i];
+        s_id[i] = ids[(int64_t)b * DK + i];
+    }
+    __syncthreads();
+    // this lane's frontier candidate
+    bool valid = false;
+    float fs = 0.f;
+    int fd = 0, fr = 0, fp = 0, fq = 0;
+    // this lane's node (node index == lane): the root in lane 0
+    int np = -1, nt = 0, nd = 0;
+    float ns = 0.f;
+    if (lane == 0) nt = roots[b];
+    int seq = 0;
+    if (budget > 0) {
+        if (lane == 0) {
+            valid = true;
+            fs = 0.f + s_lp[0];
+            fd = 1;
+        }
+        seq = 1;
+    }
+    for (int n = 1; n <= budget; ++n) {
+        const uint64_t key = valid ? frontier_key(fs, fd, fq) : 0;
+        const uint64_t m = wave_max_u64(key);
+        const uint64_t win = __ballot(valid && key == m);
+        if (win == 0) break;  // (cannot happen: the host checked that the candidates suffice)
+        const int wl = __builtin_ctzll(win);  // (uniform: readlane broadcasts into scalar registers)
+        const float sc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, fs), wl));
+        const int d = __builtin_amdgcn_readlane(fd, wl), r = __builtin_amdgcn_readlane(fr, wl);
+        const int par = __builtin_amdgcn_readlane(fp, wl);
+        if (lane == wl) valid = false;
+        if (lane == n) {
+            np = par;
+            nt = s_id[(d - 1) * K + r];
+            nd = d;
+            ns = sc;
+        }
+        const float pscore =  // node par (< n) is already recorded
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ns), par));
+        if (d < D) {  // first child
+            const int fl = __builtin_ctzll(~__ballot(valid));
+            if (lane == fl) {
+                valid = true;
+                fs = sc + s_lp[d * K];
+                fd = d + 1;
+                fr = 0;
+                fp = n;
+                fq = seq;
+            }
+        }
+        if (r + 1 < K) {  // next sibling
+            const int fl = __builtin_ctzll(~__ballot(valid));
+            if (lane == fl) {
+                valid = true;
+                fs = pscore + s_lp[(d - 1) * K + r + 1];
+                fd = d;
+                fr = r + 1;
+                fp = par;
+                fq = seq + 1;
+            }
+        }
+        seq += 2;
+    }
+    const int64_t o = (int64_t)b * (budget + 1);
+    if (lane <= budget) {
+        parents[o + lane] = np;
+        tokens[o + lane] = nt;
+        depth[o + lane] = nd;
+    }
+}
+
 }  // namespace
 
 extern "C" int ddt_draft_topk_workspace(int64_t rows, int64_t V, int K, size_t* bytes) {
@@ -321,8 +438,12 @@ extern "C" int ddt_best_first_tree(const int32_t* ids, const float* logp, int B,
     if (avail < budget) return DDT_EINVAL;
     if (B == 0) return DDT_OK;
     if (!ids || !logp || !root_tokens || !parents || !tokens || !depth) return DDT_EINVAL;
-    hipLaunchKernelGGL(best_first_kernel, dim3(B), dim3(64), 0, stream, ids, logp, D, K, budget, root_tokens,
-                       parents, tokens, depth);
+    if (budget + 1 <= 64)  // the frontier fits one candidate per lane
+        hipLaunchKernelGGL(best_first_wave_kernel, dim3(B), dim3(64), 0, stream, ids, logp, D, K, budget,
+                           root_tokens, parents, tokens, depth);
+    else
+        hipLaunchKernelGGL(best_first_kernel, dim3(B), dim3(64), 0, stream, ids, logp, D, K, budget, root_tokens,
+                           parents, tokens, depth);
     DDT_CHECK_LAUNCH();
     return DDT_OK;
 }

@@ -87,15 +87,17 @@ def test_best_first_tree_ties(orc):
         assert to_host(par)[0].tolist() == g["parents"] and to_host(tok)[0].tolist() == g["tokens"]
         assert to_host(dep)[0].tolist() == g["depth"], g["why"]
     rng = np.random.default_rng(5)
-    B, D, K, budget = 6, 5, 4, 200
-    ids = rng.integers(0, 1000, (B, D, K)).astype(np.int32)
-    lp = np.repeat(-np.sort(rng.integers(1, 4, (B, D, 1)), axis=1).astype(np.float32), K, axis=2)  # equal per depth
-    lp[:, :, 2:] -= 1.0
-    roots = np.arange(B, dtype=np.int32)
-    par, tok, dep = ddt.best_first_tree(to_dev(ids), to_dev(np.ascontiguousarray(lp)), to_dev(roots), budget)
-    for b in range(B):
-        rp, rt, rd = orc.best_first_tree(ids[b], lp[b], budget, int(roots[b]))
-        assert (to_host(par)[b] == rp).all() and (to_host(tok)[b] == rt).all() and (to_host(dep)[b] == rd).all()
+    for budget in (200, 60):            # the frontier in LDS, and one candidate per lane
+        B, D, K = 6, 5, 4
+        ids = rng.integers(0, 1000, (B, D, K)).astype(np.int32)
+        lp = np.repeat(-np.sort(rng.integers(1, 4, (B, D, 1)), axis=1).astype(np.float32), K, axis=2)  # equal per depth
+        lp[:, :, 2:] -= 1.0
+        roots = np.arange(B, dtype=np.int32)
+        par, tok, dep = ddt.best_first_tree(to_dev(ids), to_dev(np.ascontiguousarray(lp)), to_dev(roots), budget)
+        for b in range(B):
+            rp, rt, rd = orc.best_first_tree(ids[b], lp[b], budget, int(roots[b]))
+            assert (to_host(par)[b] == rp).all() and (to_host(tok)[b] == rt).all()
+            assert (to_host(dep)[b] == rd).all(), (budget, b)
 
 
 def test_draft_step_chain(orc):
