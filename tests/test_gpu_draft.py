@@ -64,6 +64,8 @@ def _grids(rng, B, D, K, V=4096, sigma=3.0):
     (2, 1, 16, 16),     # one level
     (2, 8, 8, 1023),    # the largest tree
     (5, 2, 2, 0),       # root only
+    (2, 63, 1, 63),     # one candidate per depth: a chain
+    (3, 2, 7, 55),      # two levels, wide
 ])
 def test_best_first_tree(orc, B, D, K, budget):
     rng = np.random.default_rng(B * 1000 + D * 10 + K + budget)
