@@ -1240,45 +1240,56 @@ __global__ __launch_bounds__(256) void verify_combine(const VerifyParams p) {
     const int row = rt * ROWS_WG + prow;
     if (row >= p.rows) return;
     const int64_t qrow = (int64_t)b * p.rows + row;
-    // splits in batches of KB with all loads of a batch issued together (the
+    // splits in batches with all loads of a batch issued together (the
     // partials sit in L2 / last-level cache: latency, not bandwidth,
-    // decides), merged with a running maximum; indices past the last split
-    // repeat it with weight zero
-    constexpr int KB = 32;
+    // decides), merged with a running maximum
     auto slot_of = [&](int s) { return p.wg_begin[b] + min(s, ns - 1) * p.row_tiles + rt; };
     float M = -INFINITY;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     float wsum = 0.f;
-    for (int s0 = 0; s0 < ns; s0 += KB) {
-        float2 ml[KB];
-        float4 v[KB];
+    // batches of KB splits, KB the smallest of 4, 8, 16, 32 that holds the
+    // request's splits (indices past the last split repeat it with weight 0)
+    auto merge = [&](auto kb) {
+        constexpr int KB = decltype(kb)::value;
+        for (int s0 = 0; s0 < ns; s0 += KB) {
+            float2 ml[KB];
+            float4 v[KB];
 #pragma unroll
-        for (int k = 0; k < KB; ++k) {
-            const int slot = slot_of(s0 + k);
-            ml[k] = p.ws_ml[(size_t)slot * ROWS_WG + prow];
-            v[k] = load4<T>(static_cast<const T*>(p.ws_o) + ((size_t)slot * NW + wave) * (NCTW * 4 * 64 * 4) +
-                            ((c * 4 + grp) * 64 + lane) * 4);
+            for (int k = 0; k < KB; ++k) {
+                const int slot = slot_of(s0 + k);
+                ml[k] = p.ws_ml[(size_t)slot * ROWS_WG + prow];
+                v[k] = load4<T>(static_cast<const T*>(p.ws_o) + ((size_t)slot * NW + wave) * (NCTW * 4 * 64 * 4) +
+                                ((c * 4 + grp) * 64 + lane) * 4);
+            }
+            float mb = M;
+#pragma unroll
+            for (int k = 0; k < KB; ++k) mb = fmaxf(mb, s0 + k < ns ? ml[k].x : -INFINITY);
+            if (mb != M && M != -INFINITY) {  // rescale what earlier batches summed
+                const float r = __builtin_amdgcn_exp2f(M - mb);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] *= r;
+                wsum *= r;
+            }
+            M = mb;
+#pragma unroll
+            for (int k = 0; k < KB; ++k) {
+                const float w = (s0 + k >= ns || ml[k].x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ml[k].x - M);
+                acc[0] += w * v[k].x;
+                acc[1] += w * v[k].y;
+                acc[2] += w * v[k].z;
+                acc[3] += w * v[k].w;
+                wsum += w * ml[k].y;
+            }
         }
-        float mb = M;
-#pragma unroll
-        for (int k = 0; k < KB; ++k) mb = fmaxf(mb, s0 + k < ns ? ml[k].x : -INFINITY);
-        if (mb != M && M != -INFINITY) {  // rescale what earlier batches summed
-            const float r = __builtin_amdgcn_exp2f(M - mb);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] *= r;
-            wsum *= r;
-        }
-        M = mb;
-#pragma unroll
-        for (int k = 0; k < KB; ++k) {
-            const float w = (s0 + k >= ns || ml[k].x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ml[k].x - M);
-            acc[0] += w * v[k].x;
-            acc[1] += w * v[k].y;
-            acc[2] += w * v[k].z;
-            acc[3] += w * v[k].w;
-            wsum += w * ml[k].y;
-        }
-    }
+    };
+    if (ns <= 4)
+        merge(std::integral_constant<int, 4>{});
+    else if (ns <= 8)
+        merge(std::integral_constant<int, 8>{});
+    else if (ns <= 16)
+        merge(std::integral_constant<int, 16>{});
+    else
+        merge(std::integral_constant<int, 32>{});
     const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[e] *= inv;
