@@ -83,6 +83,9 @@ def test_host_side_validation(lib):
     assert lib.ddt_verify_workspace(ctypes.byref(d), pl, ctypes.byref(n)) == 0
     assert lib.ddt_verify_attn(ctypes.byref(d), null, null, null, null, null, pl, null, null, null,
                                null, 0, null) == -1
+    # every other pointer set (never dereferenced): no kv_base and no block table is rejected
+    f = ctypes.c_void_p(1 << 20)
+    assert lib.ddt_verify_attn(ctypes.byref(d), f, f, f, f, null, pl, f, f, f, f, 1 << 30, null) == -1
 
 
 def test_verify_step_validation(lib):
