@@ -202,8 +202,16 @@ def main():
         for _ in range(3):
             step()
     torch.cuda.synchronize()
+    # steps captured 10 to a graph (a device-resident loop replays several
+    # steps per launch); one-step graphs, whose every replay pays the host's
+    # graph launch, are timed beside them
+    spg = 10 if args.steps >= 10 and args.steps % 10 == 0 else 1
     g_step = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g_step):
+        for _ in range(spg):
+            step()
+    g_one = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_one):
         step()
     g_attn = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g_attn):
@@ -212,16 +220,26 @@ def main():
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
-    for _ in range(args.warmup):
+    for _ in range(-(-args.warmup // spg)):
         g_step.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
-    for _ in range(args.steps):
+    for _ in range(args.steps // spg):
         g_step.replay()
     e1.record(stream)
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / args.steps
+    for _ in range(3):
+        g_one.replay()
+    torch.cuda.synchronize()
+    o0, o1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    o0.record(stream)
+    for _ in range(args.steps):
+        g_one.replay()
+    o1.record(stream)
+    torch.cuda.synchronize()
+    ms_step_one = o0.elapsed_time(o1) / args.steps
 
     # the dominant launch alone: attn_reps back-to-back calls in one graph
     g_attn.replay()
@@ -259,6 +277,10 @@ def main():
         "config": {"workload": f"config{args.config} {desc}", "requests": B, "heads": H, "nodes": N,
                    "cache_tokens": keys, "visible_pairs": pairs, "attn_flop_per_step": flops},
         "cache_tokens_per_s": round(keys / (ms_step * 1e-3), 1),
+        "step_timing": {"steps_per_graph": spg, "ms_per_step_one_step_graphs": round(ms_step_one, 5),
+                        "value_one_step_graphs": round(flops / (ms_step_one * 1e-3) / 1e12, 3),
+                        "note": "ms_per_step: the K timed steps replayed as graphs of steps_per_graph steps; "
+                                "one-step graphs add the host's graph launch to every step"},
         "verify_attn_ms": round(ms_attn, 5),
         "verify_attn_cache_tokens_per_s": round(keys / (ms_attn * 1e-3), 1),
         "roofline": {"bound": "mfma", "kernel": "verify_split+verify_combine (ddt_verify_attn)",
