@@ -279,6 +279,18 @@ int ddt_compact_kv(void* ckv, int64_t ld_ckv, void* kpe, int64_t ld_kpe, int dty
                    const int32_t* accept_len, int B, int N, int32_t* src_slot, hipStream_t stream);
 
 /*
+ * ddt_compact_kv on a paged cache (see ddt_attn_desc): slot t of request b
+ * is pool row block_table[b*bt_ld + t/page_size]*page_size + t%page_size.
+ * page_size a power of two in [1, 65536], bt_ld >= 1; the table must name
+ * pages for slots [0, P_b + N) of every request (device data, not checked).
+ * Otherwise as ddt_compact_kv.
+ */
+int ddt_compact_kv_paged(void* ckv, int64_t ld_ckv, void* kpe, int64_t ld_kpe, int dtype, int d_lat, int d_rope,
+                         const int32_t* block_table, int64_t bt_ld, int page_size, int32_t* prefix_len,
+                         const int32_t* path, const int32_t* accept_len, int B, int N, int32_t* src_slot,
+                         hipStream_t stream);
+
+/*
  * Acceptance and compaction in one launch.  [Ambition], section "The
  * Knowledge Architecture"; [Keystone], sections "The Reasoning That
  * Preceded the Header" and "Mistakes and Iterative Refinement".  The same

@@ -9,6 +9,7 @@
 // block-wise LDS-staged copy of ddt::copy_path_rows (tree_tail.h) is race
 // free with no global scratch.  ddt_accept_compact runs acceptance and
 // compaction of a request in one workgroup (ddt::accept_compact_body).
+// ddt_compact_kv_paged maps slots to pool rows through a block table.
 #include "common.h"
 #include "tree_tail.h"
 
@@ -17,7 +18,7 @@ namespace {
 template <typename U>
 __global__ __launch_bounds__(ddt::kCompactThreads) void compact_kernel(
     char* __restrict__ ckv, int64_t ld_ckv, char* __restrict__ kpe, int64_t ld_kpe, int ckv_units, int kpe_units,
-    const int64_t* __restrict__ kv_base, int32_t* __restrict__ prefix_len, const int32_t* __restrict__ path,
+    const ddt::SlotMap map, int32_t* __restrict__ prefix_len, const int32_t* __restrict__ path,
     const int32_t* __restrict__ accept_len, int N, int32_t* __restrict__ src_slot, int rows_per_block) {
     extern __shared__ uint4 stage_raw[];
     __shared__ int s_bad;
@@ -42,7 +43,6 @@ __global__ __launch_bounds__(ddt::kCompactThreads) void compact_kernel(
             src_slot[off + j] = (ok && j <= k) ? (int32_t)(P + path[off + j]) : -1;
     }
     if (!ok) return;
-    const ddt::SlotMap map{kv_base, nullptr, 0, 0};
     ddt::copy_path_rows<U>(ckv, ld_ckv, kpe, ld_kpe, ckv_units, kpe_units, map, b, P, k, rows_per_block,
                            reinterpret_cast<U*>(stage_raw), [&](int j) { return path[off + j]; });
     if (threadIdx.x == 0) prefix_len[b] = (int32_t)(P + k + 1);
@@ -55,6 +55,26 @@ __global__ __launch_bounds__(ddt::kCompactThreads) void accept_compact_kernel(co
     ddt::accept_compact_body<U>(a, blockIdx.x, reinterpret_cast<U*>(stage_raw));
 }
 
+// The copy of ddt_compact_kv and ddt_compact_kv_paged after their checks.
+int launch_compact(void* ckv, int64_t ld_ckv, void* kpe, int64_t ld_kpe, int dtype, int d_lat, int d_rope,
+                   const ddt::SlotMap& map, int32_t* prefix_len, const int32_t* path, const int32_t* accept_len, int B,
+                   int N, int32_t* src_slot, hipStream_t stream) {
+    if (d_rope == 0) kpe = ckv;
+    ddt::CompactLayout lay;
+    const int rc = ddt::compact_layout(ckv, ld_ckv, kpe, ld_kpe, dtype, d_lat, d_rope, N, &lay);
+    if (rc != DDT_OK) return rc;
+    if (lay.vec16)
+        hipLaunchKernelGGL(compact_kernel<uint4>, dim3(B), dim3(ddt::kCompactThreads), lay.stage_bytes, stream,
+                           (char*)ckv, lay.lc, (char*)kpe, lay.lk, lay.ckv_units, lay.kpe_units, map, prefix_len, path,
+                           accept_len, N, src_slot, lay.rows_per_block);
+    else
+        hipLaunchKernelGGL(compact_kernel<uint32_t>, dim3(B), dim3(ddt::kCompactThreads), lay.stage_bytes, stream,
+                           (char*)ckv, lay.lc, (char*)kpe, lay.lk, lay.ckv_units, lay.kpe_units, map, prefix_len, path,
+                           accept_len, N, src_slot, lay.rows_per_block);
+    DDT_CHECK_LAUNCH();
+    return DDT_OK;
+}
+
 }  // namespace
 
 extern "C" int ddt_compact_kv(void* ckv, int64_t ld_ckv, void* kpe, int64_t ld_kpe, int dtype, int d_lat,
@@ -65,20 +85,23 @@ extern "C" int ddt_compact_kv(void* ckv, int64_t ld_ckv, void* kpe, int64_t ld_k
     if (B == 0) return DDT_OK;
     if (!ckv || !kv_base || !prefix_len || !path || !accept_len) return DDT_EINVAL;
     if (d_rope > 0 && !kpe) return DDT_EINVAL;
-    if (d_rope == 0) kpe = ckv;
-    ddt::CompactLayout lay;
-    const int rc = ddt::compact_layout(ckv, ld_ckv, kpe, ld_kpe, dtype, d_lat, d_rope, N, &lay);
-    if (rc != DDT_OK) return rc;
-    if (lay.vec16)
-        hipLaunchKernelGGL(compact_kernel<uint4>, dim3(B), dim3(ddt::kCompactThreads), lay.stage_bytes, stream,
-                           (char*)ckv, lay.lc, (char*)kpe, lay.lk, lay.ckv_units, lay.kpe_units, kv_base, prefix_len,
-                           path, accept_len, N, src_slot, lay.rows_per_block);
-    else
-        hipLaunchKernelGGL(compact_kernel<uint32_t>, dim3(B), dim3(ddt::kCompactThreads), lay.stage_bytes, stream,
-                           (char*)ckv, lay.lc, (char*)kpe, lay.lk, lay.ckv_units, lay.kpe_units, kv_base, prefix_len,
-                           path, accept_len, N, src_slot, lay.rows_per_block);
-    DDT_CHECK_LAUNCH();
-    return DDT_OK;
+    return launch_compact(ckv, ld_ckv, kpe, ld_kpe, dtype, d_lat, d_rope, ddt::SlotMap{kv_base, nullptr, 0, 0},
+                          prefix_len, path, accept_len, B, N, src_slot, stream);
+}
+
+extern "C" int ddt_compact_kv_paged(void* ckv, int64_t ld_ckv, void* kpe, int64_t ld_kpe, int dtype, int d_lat,
+                                    int d_rope, const int32_t* block_table, int64_t bt_ld, int page_size,
+                                    int32_t* prefix_len, const int32_t* path, const int32_t* accept_len, int B, int N,
+                                    int32_t* src_slot, hipStream_t stream) {
+    if (B < 0 || N < 1 || N > DDT_MAX_NODES || d_lat < 1 || d_rope < 0) return DDT_EINVAL;
+    if (dtype != DDT_F32 && dtype != DDT_BF16) return DDT_EUNSUPPORTED;
+    if (page_size < 1 || page_size > (1 << 16) || (page_size & (page_size - 1)) != 0 || bt_ld < 1) return DDT_EINVAL;
+    if (B == 0) return DDT_OK;
+    if (!ckv || !block_table || !prefix_len || !path || !accept_len) return DDT_EINVAL;
+    if (d_rope > 0 && !kpe) return DDT_EINVAL;
+    return launch_compact(ckv, ld_ckv, kpe, ld_kpe, dtype, d_lat, d_rope,
+                          ddt::SlotMap{nullptr, block_table, bt_ld, __builtin_ctz((unsigned)page_size)}, prefix_len,
+                          path, accept_len, B, N, src_slot, stream);
 }
 
 extern "C" int ddt_accept_compact(const int32_t* target_ids, const int32_t* draft_ids, const int32_t* parents,

@@ -67,6 +67,7 @@ def lib():
         L.ddt_argmax.argtypes = [P, i32, i64, i64, i64, P, P, sz, P]
         L.ddt_greedy_accept.argtypes = [P, P, P, i32, i32, P, P, P, P]
         L.ddt_compact_kv.argtypes = [P, i64, P, i64, i32, i32, i32, P, P, P, P, i32, i32, P, P]
+        L.ddt_compact_kv_paged.argtypes = [P, i64, P, i64, i32, i32, i32, P, i64, i32, P, P, P, i32, i32, P, P]
         L.ddt_accept_compact.argtypes = [P, P, P, i32, i32, P, P, P, P, i64, P, i64, i32, i32, i32, P, P, P, P, P]
         L.ddt_verify_attn_argmax.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P, P, P, P, sz,
                                              ctypes.POINTER(ArgmaxTask), P]
@@ -81,7 +82,7 @@ def lib():
         L.ddt_probe_read.argtypes = [P, sz, P, i32, P]
         L.ddt_probe_copy.argtypes = [P, P, sz, i32, P]
         for f in ("ddt_version", "ddt_build_mask", "ddt_verify_workspace", "ddt_verify_attn",
-                  "ddt_argmax_workspace", "ddt_argmax", "ddt_greedy_accept", "ddt_compact_kv",
+                  "ddt_argmax_workspace", "ddt_argmax", "ddt_greedy_accept", "ddt_compact_kv", "ddt_compact_kv_paged",
                   "ddt_accept_compact", "ddt_verify_attn_argmax", "ddt_verify_step",
                   "ddt_draft_topk_workspace", "ddt_draft_topk", "ddt_best_first_tree",
                   "ddt_proj_pack_weight", "ddt_head_proj",
@@ -340,15 +341,27 @@ def greedy_accept(target_ids, draft_ids, parents, accept_len=None, path=None, to
     return accept_len, path, tokens
 
 
-def compact_kv(ckv, kpe, kv_base, prefix_len, path, accept_len, src_slot=None, stream=None):
-    """In-place compaction of the cache pool views; prefix_len [B] int32 (device) is updated."""
+def compact_kv(ckv, kpe, kv_base, prefix_len, path, accept_len, src_slot=None, pages=None, stream=None):
+    """In-place compaction of the cache pool views; prefix_len [B] int32 (device) is updated.
+    pages: None (contiguous from kv_base) or (block_table [B, bt_ld] int32, page_size); kv_base
+    is then unused (may be None)."""
     _dev(ckv, None, "ckv")
     _dev(kpe, ckv.dtype, "kpe")
-    _contig(kv_base, torch.int64, "kv_base")
     _contig(prefix_len, torch.int32, "prefix_len")
     _contig(path, torch.int32, "path")
     _contig(accept_len, torch.int32, "accept_len")
     B, N = path.shape
+    if pages is not None:
+        table, page_size = pages
+        _contig(table, torch.int32, "block_table")
+        if table.dim() != 2 or table.shape[0] != B:
+            raise ValueError("block_table must be [B, bt_ld]")
+        _check(lib().ddt_compact_kv_paged(_p(ckv), _rows(ckv, "ckv"), _p(kpe), _rows(kpe, "kpe"), _dtype_code(ckv),
+                                          ckv.shape[1], kpe.shape[1], _p(table), table.shape[1], int(page_size),
+                                          _p(prefix_len), _p(path), _p(accept_len), B, N, _p(src_slot),
+                                          _stream(stream)), "ddt_compact_kv_paged")
+        return prefix_len, src_slot
+    _contig(kv_base, torch.int64, "kv_base")
     _check(lib().ddt_compact_kv(_p(ckv), _rows(ckv, "ckv"), _p(kpe), _rows(kpe, "kpe"), _dtype_code(ckv),
                                 ckv.shape[1], kpe.shape[1], _p(kv_base), _p(prefix_len), _p(path),
                                 _p(accept_len), B, N, _p(src_slot), _stream(stream)), "ddt_compact_kv")

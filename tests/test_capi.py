@@ -149,6 +149,17 @@ def test_paged_desc_validation(lib):
     assert lib.ddt_verify_workspace(ctypes.byref(d), P, ctypes.byref(n)) == -2  # paged: bf16 instance only
 
 
+def test_compact_paged_validation(lib):
+    f = ctypes.c_void_p(1 << 20)   # never dereferenced: every call below fails validation or has B = 0
+    null = None
+    args = lambda ps, bt_ld, B=1, table=f: (f, 576, f, 576, 1, 512, 64, table, bt_ld, ps, f, f, f, B, 8, null, null)
+    assert lib.ddt_compact_kv_paged(*args(48, 10)) == -1          # page size not a power of two
+    assert lib.ddt_compact_kv_paged(*args(1 << 17, 10)) == -1     # page size too large
+    assert lib.ddt_compact_kv_paged(*args(64, 0)) == -1           # bt_ld < 1
+    assert lib.ddt_compact_kv_paged(*args(64, 10, table=null)) == -1
+    assert lib.ddt_compact_kv_paged(*args(64, 10, B=0)) == 0       # nothing to do
+
+
 def test_proj_validation(lib):
     a, b, c = ctypes.c_void_p(1 << 20), ctypes.c_void_p(2 << 20), ctypes.c_void_p(3 << 20)  # never dereferenced
     null = None

@@ -126,3 +126,37 @@ def test_paged_verify_step(orc, ps, with_mask):
         named[table[b, tt // ps].astype(np.int64) * ps + tt % ps] = True
     assert (got_phys[~named].view(np.uint8) == phys[~named].view(np.uint8)).all()
     print(f"paged ps={ps}: accepted {oa.tolist()}")
+
+
+@pytest.mark.parametrize("ps,cfg", [(1, 3), (32, 1), (256, 3)])
+def test_paged_compact_kv(orc, ps, cfg):
+    """Standalone compaction through a block table (ddt_compact_kv_paged):
+    the accepted path's latents land at logical slots P.. of each request,
+    bit for bit as the oracle's compaction of the logical cache; rows no
+    table entry names are untouched."""
+    w = synth.workload(3, B=6, prefix_range=(0, 900)) if cfg == 3 else synth.workload(1, B=6, N=8, prefix=45)
+    rng = np.random.default_rng(7 + ps)
+    B, N, dl = w.B, w.N, w.d_lat
+    w.draft_ids = w.draft_ids % 50
+    t = synth.planted_targets(rng, w.parents, w.draft_ids, 50, 0.85)
+    oa, op, _ = orc.greedy_accept(t, w.draft_ids, w.parents)
+    oa[1] = 0                                                   # a request that accepts only the root
+    op[1, 1:] = -1
+    phys, table = to_paged(w, ps, rng)
+    opool = w.pool.copy()
+    opl, osrc = orc.compact_kv(opool[:, :dl], opool[:, dl:], w.kv_base, w.prefix_len, op, oa)
+
+    pd, td = to_dev(phys), to_dev(table)
+    dpl = to_dev(w.prefix_len)
+    src = torch.empty((B, N), dtype=torch.int32, device="cuda")
+    ddt.compact_kv(pd[:, :dl], pd[:, dl:], None, dpl, to_dev(op), to_dev(oa), src, pages=(td, ps))
+    torch.cuda.synchronize()
+    assert (to_host(dpl) == opl).all() and (to_host(src) == osrc).all()
+    got_phys = np.ascontiguousarray(to_host(pd))
+    got = from_paged(got_phys, table, ps, w)
+    assert (got.view(np.uint8) == opool.view(np.uint8)).all()
+    named = np.zeros(got_phys.shape[0], bool)
+    for b in range(B):
+        tt = np.arange(int(w.prefix_len[b]) + N)
+        named[table[b, tt // ps].astype(np.int64) * ps + tt % ps] = True
+    assert (got_phys[~named].view(np.uint8) == phys[~named].view(np.uint8)).all()
