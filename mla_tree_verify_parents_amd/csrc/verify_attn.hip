@@ -1247,8 +1247,8 @@ __global__ __launch_bounds__(256) void verify_combine(const VerifyParams p) {
     float M = -INFINITY;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     float wsum = 0.f;
-    // batches of KB splits, KB the smallest of 4, 8, 16, 32 that holds the
-    // request's splits (indices past the last split repeat it with weight 0)
+    // batches of KB splits, KB the smallest of 4, 8, 12, 16, 24, 32 that holds the
+    // request's splits (indices past the last split load nothing and weigh 0)
     auto merge = [&](auto kb) {
         constexpr int KB = decltype(kb)::value;
         for (int s0 = 0; s0 < ns; s0 += KB) {
@@ -1256,10 +1256,14 @@ __global__ __launch_bounds__(256) void verify_combine(const VerifyParams p) {
             float4 v[KB];
 #pragma unroll
             for (int k = 0; k < KB; ++k) {
-                const int slot = slot_of(s0 + k);
-                ml[k] = p.ws_ml[(size_t)slot * ROWS_WG + prow];
-                v[k] = load4<T>(static_cast<const T*>(p.ws_o) + ((size_t)slot * NW + wave) * (NCTW * 4 * 64 * 4) +
-                                ((c * 4 + grp) * 64 + lane) * 4);
+                ml[k] = make_float2(-INFINITY, 0.f);
+                v[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (s0 + k < ns) {  // uniform: no load for the padding
+                    const int slot = slot_of(s0 + k);
+                    ml[k] = p.ws_ml[(size_t)slot * ROWS_WG + prow];
+                    v[k] = load4<T>(static_cast<const T*>(p.ws_o) + ((size_t)slot * NW + wave) * (NCTW * 4 * 64 * 4) +
+                                    ((c * 4 + grp) * 64 + lane) * 4);
+                }
             }
             float mb = M;
 #pragma unroll
@@ -1286,8 +1290,12 @@ __global__ __launch_bounds__(256) void verify_combine(const VerifyParams p) {
         merge(std::integral_constant<int, 4>{});
     else if (ns <= 8)
         merge(std::integral_constant<int, 8>{});
+    else if (ns <= 12)
+        merge(std::integral_constant<int, 12>{});
     else if (ns <= 16)
         merge(std::integral_constant<int, 16>{});
+    else if (ns <= 24)
+        merge(std::integral_constant<int, 24>{});
     else
         merge(std::integral_constant<int, 32>{});
     const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
