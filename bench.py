@@ -1,19 +1,29 @@
 """Benchmark of one DDTree verify step on one MI355X.
 
 A step is one pass of the whole hot path over one batch of synthetic input
-already resident in HBM:
-    parents -> ancestor mask -> tree-verify MLA attention (absorbed, bf16,
-    fp32 accumulate) and argmax over the target logits (one launch) ->
-    greedy acceptance + KV compaction (+ length update, one launch).
-The default workload is the K2-like single-GPU head share: 1 request,
-8 heads, kv_lora_rank 512 + rope 64, prefix 4096, 64 tree nodes (a
-best-first tree from seeded top-4 draft candidates), target logits over a
-163840-token vocabulary.
+already resident in HBM.  The default workload is the largest single-GPU
+configuration, long context with all heads: 4 requests, 64 heads,
+kv_lora_rank 512 + rope 64 (bf16), prefix 131072 each, 128 tree nodes (a
+wide-shallow best-first tree from seeded top-8 draft candidates, depth <= 4),
+and its step is
+    parents -> ancestor mask -> tree-verify MLA attention (absorbed, bf16 in,
+    fp32 accumulate; split-KV kernel + merge) -> greedy acceptance + KV
+    compaction + length update (one launch) on the planted target ids.
+`--config 2` runs the K2-like head share (1 request, 8 heads, prefix 4096,
+64 nodes), whose step also takes the argmax over 64 x 163840 fp32 target
+logits (fused: two launches); `--config 3` the batched ragged workload;
+`--config 5` the verify loop (100 steps with cache growth).
 
 Prints ONE JSON line.  `value` is verify-attention TFLOP/s over the whole
-step (attention FLOPs / step time); `roofline` is the verify-attention
-launch (split-KV kernel + combine) against the bf16 MFMA peak;
-`cpu_baseline` times the fp64 oracle on the host for the same workload.
+step (attention FLOPs / step time); `ms_per_step` and `verify_attn_ms` are
+medians of 5 timed windows of at least 50 ms each (HIP events on the launch
+stream around graph replays), reported with their spread; `roofline` is
+the attention launch against the bf16 MFMA peak; `hbm_stages` the HBM scans
+of the end-to-end step (argmax over 2048 x 163840 fp32 target logits, draft
+top-8 over 256 x 163840) against 8 TB/s; `cpu_baseline` times the fp64
+oracle on the host for a sample of the same workload.  The default run
+also reports the K2-like head share's step and a short verify loop as
+extra keys (`config2`, `config5_loop`).
 
 `--traffic-probe` runs a few attention launches of the workload and one
 device-to-device copy of known size, and exits: it is the program that the
@@ -25,6 +35,7 @@ kernel source still has the hash recorded there.
 import argparse
 import hashlib
 import json
+import math
 import os
 import re
 import sys
@@ -38,20 +49,24 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 FLOP_PER_PAIR = 2 * (512 + 64) + 2 * 512   # QK over 576 + PV over 512
+WINDOWS = 5                     # timed windows per figure (median and spread reported)
+WINDOW_MS = 50.0                # at least this much device time per window
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=2, help="workload configuration (2, 3, 4, or 5: the verify loop)")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=4,
+                    help="workload configuration (2, 3, 4 = the default, or 5: the verify loop)")
     ap.add_argument("--loop-steps", type=int, default=100, help="timed iterations of the verify loop (config 5)")
     ap.add_argument("--page-size", type=int, default=0,
                     help="config 5: keep the loop's cache in pages of this many rows (0: contiguous)")
-    ap.add_argument("--attn-reps", type=int, default=200, help="back-to-back attention launches timed for the roofline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true", help="skip the on-device MFMA / HBM peak probes")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the side measurements (paged, prefill, projections, HBM stages, config 2, loop)")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache attention timing (configs 2 and 3)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget for the oracle timing")
@@ -99,26 +114,106 @@ def workload_for(cfg):
         w = synth.workload(4)
         desc = "long context: B=4, H=64, 512+64 bf16, prefix 131072, 128 nodes (best-first, top-8, depth<=4)"
     else:
-        raise SystemExit(f"bench runs configurations 2, 3 or 4, not {cfg}")
+        raise SystemExit(f"bench runs configurations 2, 3, 4 or 5, not {cfg}")
     return w, desc
+
+
+def spread(xs):
+    """Median, min, max and (max - min) / median of a list of window figures."""
+    med = float(np.median(xs))
+    return {"median": round(med, 6), "min": round(min(xs), 6), "max": round(max(xs), 6),
+            "rel_spread": round((max(xs) - min(xs)) / med, 4) if med > 0 else None}
+
+
+def time_windows(replay, units_per_replay, est_ms_per_unit, stream, min_units=1):
+    """Time WINDOWS windows of back-to-back replays on `stream` (HIP events
+    around each window, synchronised on both sides).  A window holds at
+    least min_units units and at least WINDOW_MS of estimated device time.
+    Returns (ms per unit of every window, units per window)."""
+    import torch
+    reps = max(1, math.ceil(min_units / units_per_replay),
+               math.ceil(WINDOW_MS / max(est_ms_per_unit * units_per_replay, 1e-6)))
+    out = []
+    for _ in range(WINDOWS):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / (reps * units_per_replay))
+    return out, reps * units_per_replay
+
+
+def graph_of(fn, n):
+    """A HIP graph of n back-to-back calls of fn (captured on torch's stream)."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(n):
+            fn()
+    return g
+
+
+def estimate_ms(replay, units, stream, reps=3):
+    import torch
+    replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (reps * units)
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (the verify path has no multi-GPU part); got --gpus {args.gpus}",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU only: this build's verify path runs on a single GPU and has no "
+              f"multi-GPU part (got --gpus {args.gpus})", file=sys.stderr)
         sys.exit(2)
     import torch
-
-    from mla_tree_verify_parents_amd import ddt
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.config == 5:
-        return run_loop(args, dev)
-    w, desc = workload_for(args.config)
+        res = run_loop(args, dev, args.warmup, args.loop_steps)
+        add_peaks(res, args, dev)
+        print(json.dumps(res), flush=True)
+        return
+    res = measure_config(args.config, args, dev, headline=True)
+    if res is None:
+        return
+    if not args.no_extras:
+        res["hbm_stages"] = guarded(lambda: time_hbm_stages(dev))
+        if args.config != 2:
+            res["config2"] = guarded(lambda: measure_config(2, args, dev, headline=False))
+            res["config5_loop"] = guarded(lambda: run_loop(args, dev, 3, 20, brief=True))
+    add_peaks(res, args, dev)
+    print(json.dumps(res), flush=True)
+
+
+def guarded(f):
+    """A side measurement: its failure is reported in the JSON line instead
+    of taking the headline with it."""
+    try:
+        return f()
+    except Exception as e:  # noqa: BLE001
+        return {"error": f"{type(e).__name__}: {e}"}
+
+
+def measure_config(cfg, args, dev, headline):
+    """Time one configuration's step and attention launch; returns the JSON
+    fields (the headline line, or the sub-record of a side configuration)."""
+    import torch
+
+    from mla_tree_verify_parents_amd import ddt
+
+    w, desc = workload_for(cfg)
 
     def to_dev(a):
         if a.dtype == np.uint16:
@@ -184,7 +279,7 @@ def main():
             ddt.accept_compact(target, draft, parents, ckv, kpe, kv_base, prefix0, acc, path, tok,
                                new_prefix_len=new_prefix)
 
-    if args.traffic_probe:
+    if args.traffic_probe and headline:
         ddt.build_mask(parents, mask, depth, terr)
         for _ in range(5):
             attn()
@@ -192,68 +287,40 @@ def main():
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
-        print(json.dumps({"traffic_probe": f"config{args.config}", "attn_launches": 5,
+        print(json.dumps({"traffic_probe": f"config{cfg}", "attn_launches": 5,
                           "calibration_copy_bytes": CALIB_BYTES}), flush=True)
-        return
+        return None
 
     side = torch.cuda.Stream()
     with torch.cuda.stream(side):
         ddt.build_mask(parents, mask, depth, terr)  # for the attention-only launches timed below
-        for _ in range(3):
+        for _ in range(max(1, min(args.warmup, 3))):
             step()
-    torch.cuda.synchronize()
-    # steps captured 10 to a graph (a device-resident loop replays several
-    # steps per launch); one-step graphs, whose every replay pays the host's
-    # graph launch, are timed beside them
-    spg = 10 if args.steps >= 10 and args.steps % 10 == 0 else 1
-    g_step = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_step):
-        for _ in range(spg):
-            step()
-    g_one = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_one):
-        step()
-    g_attn = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_attn):
-        for _ in range(args.attn_reps):
-            attn()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-
+    # steps captured several to a graph when they are short (a device-resident
+    # loop replays several steps per launch); one-step graphs, whose every
+    # replay pays the host's graph launch, are timed beside them
+    g_one = graph_of(step, 1)
+    est_step = estimate_ms(g_one.replay, 1, stream)
+    spg = 10 if est_step < 0.5 else 1
+    g_step = graph_of(step, spg) if spg > 1 else g_one
     for _ in range(-(-args.warmup // spg)):
         g_step.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps // spg):
-        g_step.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / args.steps
-    for _ in range(3):
-        g_one.replay()
-    torch.cuda.synchronize()
-    o0, o1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    o0.record(stream)
-    for _ in range(args.steps):
-        g_one.replay()
-    o1.record(stream)
-    torch.cuda.synchronize()
-    ms_step_one = o0.elapsed_time(o1) / args.steps
+    step_ms, step_units = time_windows(g_step.replay, spg, est_step, stream, min_units=args.steps)
+    one_ms, _ = time_windows(g_one.replay, 1, est_step, stream, min_units=args.steps) if spg > 1 else (step_ms, 0)
+    ms_step = float(np.median(step_ms))
 
-    # the dominant launch alone: attn_reps back-to-back calls in one graph
+    # the dominant launch alone: back-to-back attention calls in one graph
+    # (at least WINDOW_MS per window)
+    g_a1 = graph_of(attn, 1)
+    est_attn = estimate_ms(g_a1.replay, 1, stream)
+    per_graph = max(1, min(200, int(WINDOW_MS / max(est_attn, 1e-4))))
+    g_attn = graph_of(attn, per_graph)
     g_attn.replay()
-    torch.cuda.synchronize()
-    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a0.record(stream)
-    g_attn.replay()
-    a1.record(stream)
-    torch.cuda.synchronize()
-    ms_attn = a0.elapsed_time(a1) / args.attn_reps
-
-    cold = None
-    if args.config in (2, 3) and not args.no_cold:
-        cold = time_cold_attn(pool, dl, q_lat, q_pe, kv_base, P_host, mask, H, w.scale, out, lse, ws, side, stream)
+    attn_ms, attn_units = time_windows(g_attn.replay, per_graph, est_attn, stream)
+    ms_attn = float(np.median(attn_ms))
+    del g_one, g_step, g_a1, g_attn
 
     pairs = w.visible_pairs()
     flops = pairs * FLOP_PER_PAIR
@@ -273,24 +340,35 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) latents and queries, best-first draft tree, N(0,1)+boost logits)",
-        "config": {"workload": f"config{args.config} {desc}", "requests": B, "heads": H, "nodes": N,
+        "data": "synthetic (seeded N(0,1) latents and queries, best-first draft tree, planted targets)",
+        "config": {"workload": f"config{cfg} {desc}", "requests": B, "heads": H, "nodes": N,
                    "cache_tokens": keys, "visible_pairs": pairs, "attn_flop_per_step": flops},
         "cache_tokens_per_s": round(keys / (ms_step * 1e-3), 1),
-        "step_timing": {"steps_per_graph": spg, "ms_per_step_one_step_graphs": round(ms_step_one, 5),
-                        "value_one_step_graphs": round(flops / (ms_step_one * 1e-3) / 1e12, 3),
-                        "note": "ms_per_step: the K timed steps replayed as graphs of steps_per_graph steps; "
-                                "one-step graphs add the host's graph launch to every step"},
+        "step_timing": {"median_of": WINDOWS, "steps_per_window": step_units, "steps_per_graph": spg,
+                        "ms_per_step": spread(step_ms),
+                        "note": "each window: HIP events on the launch stream around back-to-back graph "
+                                "replays of steps_per_window steps, synchronised on both sides; ms_per_step "
+                                "is the median window"},
         "verify_attn_ms": round(ms_attn, 5),
+        "verify_attn_timing": {"median_of": WINDOWS, "launches_per_window": attn_units,
+                               "ms_per_launch": spread(attn_ms)},
         "verify_attn_cache_tokens_per_s": round(keys / (ms_attn * 1e-3), 1),
         "roofline": {"bound": "mfma", "kernel": "verify_split+verify_combine (ddt_verify_attn)",
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": recorded_traffic(args.config),
-                     "algorithmic_bytes": attn_bytes,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": recorded_traffic(cfg),
+                     "algorithmic_flop_per_launch": flops, "algorithmic_bytes": attn_bytes,
                      "achieved_GBps": round(attn_bytes / (ms_attn * 1e-3) / 1e9, 1)},
     }
-    if cold is not None:
-        ms_cold, n_copies = cold
+    if spg > 1:
+        res["step_timing"]["one_step_graphs_ms_per_step"] = spread(one_ms)
+    if not headline:
+        for k in ("metric", "n_gpus", "steps", "warmup", "higher_is_better", "scaling", "vs_baseline", "dtype",
+                  "data", "unit"):
+            res.pop(k, None)
+        return res
+    if cfg in (2, 3) and not args.no_cold:
+        ms_cold, n_copies = time_cold_attn(pool, dl, q_lat, q_pe, kv_base, P_host, mask, H, w.scale, out, lse, ws,
+                                           side, stream)
         res["cold_cache"] = {"verify_attn_ms": round(ms_cold, 5), "cache_copies": n_copies,
                              "copy_bytes": pool.numel() * pool.element_size(),
                              "achieved_TFLOPs": round(flops / (ms_cold * 1e-3) / 1e12, 2),
@@ -298,18 +376,63 @@ def main():
                              "note": "back-to-back launches rotating over distinct copies of the cache "
                                      f"(at least {COLD_BYTES >> 20} MiB in all), so the last-level cache "
                                      "cannot serve the keys"}
-    res["paged"] = time_paged(w, dev, q_lat, q_pe, mask, ms_attn)
-    res["prefill"] = time_prefill(dev)
-    res["projections"] = [time_projections(B * N, H, dev)]
-    if B * N < 2048:
-        res["projections"].append(time_projections(2048, H, dev))   # the verify loop's 32 x 64 nodes
-    add_peaks(res, args, dev)
+    if not args.no_extras:
+        res["paged"] = guarded(lambda: time_paged(w, dev, q_lat, q_pe, mask, ms_attn))
+        res["prefill"] = guarded(lambda: time_prefill(dev))
+        res["projections"] = [guarded(lambda: time_projections(B * N, H, dev))]
+        if B * N < 2048:
+            res["projections"].append(guarded(lambda: time_projections(2048, 8, dev)))   # the loop's 32 x 64 nodes
+    del pool, q
+    torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, flops)
-    print(json.dumps(res), flush=True)
+    return res
 
 
-def run_loop(args, dev):
+def time_hbm_stages(dev):
+    """The HBM scans of the end-to-end step on their own, at its shapes:
+    the target argmax over 2048 x 163840 fp32 logits (ddt_argmax) and the
+    draft top-8 over 256 x 163840 fp32 (ddt_draft_topk); bytes = rows x V x 4,
+    against 8 TB/s."""
+    import torch
+
+    from mla_tree_verify_parents_amd import ddt
+
+    stream = torch.cuda.current_stream()
+    g = torch.Generator(device=dev)
+    g.manual_seed(5005)
+    V = 163840
+    res = {}
+    for name, rows in (("argmax", 2048), ("draft_topk", 256)):
+        x = torch.randn((rows, V), generator=g, device=dev, dtype=torch.float32)
+        if name == "argmax":
+            idx = torch.empty((rows,), dtype=torch.int32, device=dev)
+            ws = torch.zeros((max(16, ddt.argmax_workspace_bytes(rows, V)),), dtype=torch.uint8, device=dev)
+            fn = lambda: ddt.argmax(x, idx, ws)   # noqa: E731
+        else:
+            ids = torch.empty((rows, 8), dtype=torch.int32, device=dev)
+            lp = torch.empty((rows, 8), dtype=torch.float32, device=dev)
+            ws = torch.empty((max(16, ddt.draft_topk_workspace_bytes(rows, V, 8)),), dtype=torch.uint8, device=dev)
+            fn = lambda: ddt.draft_topk(x, 8, ids, lp, ws)   # noqa: E731
+        fn()
+        g1 = graph_of(fn, 1)
+        est = estimate_ms(g1.replay, 1, stream)
+        per = max(1, min(500, int(WINDOW_MS / max(est, 1e-4))))
+        gn = graph_of(fn, per)
+        gn.replay()
+        ms, n = time_windows(gn.replay, per, est, stream)
+        med = float(np.median(ms))
+        nbytes = rows * V * 4
+        gbps = nbytes / (med * 1e-3) / 1e9
+        res[name] = {"rows": rows, "vocab": V, "bytes": nbytes, "us": round(med * 1e3, 3),
+                     "us_spread": spread([m * 1e3 for m in ms]), "launches_per_window": n,
+                     "GBps": round(gbps, 1), "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4)}
+        del gn, g1, x, ws
+    res["note"] = "median of 5 windows of back-to-back launches in one graph; bytes = rows x V x 4 read once"
+    return res
+
+
+def run_loop(args, dev, W, K, brief=False):
     """Configuration 5: the verify loop.  Every iteration draws its inputs
     (untimed: draft logits, node latents, queries, target logits planted on
     the tree), runs the draft stage on the device (top-8 per depth and the
@@ -318,22 +441,23 @@ def run_loop(args, dev):
     compaction, length update; two launches; timed with HIP events), then
     advances the loop (the bonus token is the next root; the host mirrors the
     grown lengths).  A step's time is the two stages' device time; `value` is
-    the attention FLOPs of all timed iterations over their summed step time."""
+    the attention FLOPs of all timed iterations over their summed step time.
+    brief: fewer fields (a side record of another configuration's line)."""
     import torch
 
     from mla_tree_verify_parents_amd import ddt, e2e, synth
 
-    W, K = args.warmup, args.loop_steps
     loop = e2e.VerifyLoop(steps=W + K, page_size=args.page_size)
     stream = torch.cuda.current_stream()
     t_ms, flops, keys, acc_sum = 0.0, 0, 0, 0
     host_s, plan_s, draft_ms, verify_ms = 0.0, 0.0, 0.0, 0.0
+    per_iter = []
     snap = None
     for it in range(W + K):
         h0 = time.perf_counter()
-        inp = loop.make_inputs()       # draws on the device; the best-first trees are built on the host
+        inp = loop.make_inputs()       # draws on the device; the best-first trees are built on the device
         h1 = time.perf_counter()
-        if it == 0 and not args.no_cpu_baseline:  # (a warmup iteration unless W == 0)
+        if it == 0 and not brief and not args.no_cpu_baseline:  # (a warmup iteration unless W == 0)
             snap = (synth.Workload(name="config5", B=loop.B, H=loop.H, N=loop.N, d_lat=loop.d_lat,
                                    d_rope=loop.d_rope, dtype="bf16", scale=loop.scale,
                                    prefix_len=inp.prefix_len.copy(), kv_base=loop.kv_base_host.copy(),
@@ -358,6 +482,7 @@ def run_loop(args, dev):
             draft_ms += inp.draft_ms
             verify_ms += e0.elapsed_time(e1)
             t_ms += inp.draft_ms + e0.elapsed_time(e1)
+            per_iter.append(inp.draft_ms + e0.elapsed_time(e1))
             flops += inp.visible_pairs(loop.H) * FLOP_PER_PAIR
             keys += int(inp.prefix_len.sum()) + loop.B * loop.N
             acc_sum += int(acc.sum())
@@ -372,21 +497,21 @@ def run_loop(args, dev):
                         inp.prefix_len, mask, H=loop.H, scale=loop.scale, out=loop.out, lse=loop.lse, workspace=ws,
                         pages=loop.pages())
 
-    reps = max(4, min(args.attn_reps, 50))
     attn()
     torch.cuda.synchronize()
-    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a0.record(stream)
-    for _ in range(reps):
-        attn()
-    a1.record(stream)
-    torch.cuda.synchronize()
-    ms_attn = a0.elapsed_time(a1) / reps
+    g1 = graph_of(attn, 1)
+    est = estimate_ms(g1.replay, 1, stream)
+    per = max(1, min(100, int(WINDOW_MS / max(est, 1e-4))))
+    gn = graph_of(attn, per)
+    gn.replay()
+    attn_ms, attn_units = time_windows(gn.replay, per, est, stream)
+    ms_attn = float(np.median(attn_ms))
+    del g1, gn
     last_flops = inp.visible_pairs(loop.H) * FLOP_PER_PAIR
     achieved = last_flops / (ms_attn * 1e-3) / 1e12
     last_keys = int(inp.prefix_len.sum()) + loop.B * loop.N
     attn_bytes = last_keys * (dl + loop.d_rope) * 2 + loop.B * loop.N * loop.H * ((dl + loop.d_rope) * 2 + dl * 2 + 4)
-    draft = time_draft_step(loop, stream, reps)
+    draft = time_draft_step(loop, stream)
     res = {
         "metric": "verify-attn TFLOP/s + cache tokens/s; % of MFMA/HBM roofline, 1xMI355X",
         "value": round(flops / (t_ms * 1e-3) / 1e12, 3),
@@ -408,11 +533,16 @@ def run_loop(args, dev):
                    "cache_tokens_per_iteration": keys / K, "accepted_drafts_per_request_step": acc_sum / (K * loop.B),
                    "attn_flop_per_step": flops / K},
         "cache_tokens_per_s": round(keys / (t_ms * 1e-3), 1),
+        "step_timing": {"ms_per_iteration": spread(per_iter),
+                        "note": "ms_per_step is the mean over the timed iterations (the cache grows, so "
+                                "iterations differ); each iteration: HIP events around its two stages"},
         "verify_attn_ms": round(ms_attn, 5),
+        "verify_attn_timing": {"median_of": WINDOWS, "launches_per_window": attn_units,
+                               "ms_per_launch": spread(attn_ms)},
         "roofline": {"bound": "mfma", "kernel": "verify_split+verify_combine (ddt_verify_attn), last iteration",
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "algorithmic_bytes": attn_bytes,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": recorded_traffic(5),
+                     "algorithmic_flop_per_launch": last_flops, "algorithmic_bytes": attn_bytes,
                      "achieved_GBps": round(attn_bytes / (ms_attn * 1e-3) / 1e9, 1)},
         "draft_step": draft,
         "stage_ms_per_iteration": {"draft_topk_and_trees": round(draft_ms / K, 5),
@@ -424,10 +554,15 @@ def run_loop(args, dev):
                                           "the host copies the input generator needs), then planning + "
                                           "enqueueing the verify step's two launches"},
     }
-    add_peaks(res, args, dev)
+    if brief:
+        for k in ("metric", "n_gpus", "warmup", "higher_is_better", "scaling", "vs_baseline", "dtype", "data",
+                  "unit", "host_ms_per_iteration"):
+            res.pop(k, None)
+    del loop
+    torch.cuda.empty_cache()
     if snap is not None:
         res["cpu_baseline"] = cpu_baseline(snap[0], args.cpu_seconds, snap[1])
-    print(json.dumps(res), flush=True)
+    return res
 
 
 COLD_BYTES = 2 * (256 << 20)  # twice the last-level cache
@@ -535,11 +670,11 @@ def add_peaks(res, args, dev):
                                                             pk["mfma_bf16_random_TFLOPs"], 4)
 
 
-def time_draft_step(loop, stream, reps):
+def time_draft_step(loop, stream):
     """The step before the verify path, on the device, at the loop's shape:
     per-depth top-k of N(0, 3^2) draft logits (B*D rows x vocabulary) and
-    the best-first trees (not part of `value`: the loop draws its trees on
-    the host).  The top-k is an HBM scan, reported against 8 TB/s."""
+    the best-first trees (the loop's draft stage).  The top-k is an HBM
+    scan, reported against 8 TB/s."""
     import torch
 
     from mla_tree_verify_parents_amd import ddt
@@ -563,13 +698,13 @@ def time_draft_step(loop, stream, reps):
     def timed(f):
         f()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            f()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps
+        g1 = graph_of(f, 1)
+        est = estimate_ms(g1.replay, 1, stream)
+        per = max(1, min(500, int(WINDOW_MS / max(est, 1e-4))))
+        gn = graph_of(f, per)
+        gn.replay()
+        ms, _ = time_windows(gn.replay, per, est, stream)
+        return float(np.median(ms))
 
     ms_topk, ms_tree = timed(topk), timed(tree)
     gbps = B * D * V * 4 / (ms_topk * 1e-3) / 1e9
@@ -658,6 +793,7 @@ def time_paged(w, dev, q_lat, q_pe, mask, ms_contiguous, page_size=64, reps=100)
     out = torch.empty((w.rows, dl), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((w.rows,), dtype=torch.float32, device=dev)
     pages = (td, page_size)
+    reps = max(3, min(reps, int(WINDOW_MS / max(ms_contiguous, 1e-3))))
     d = ddt.attn_desc(q_lat, q_pe, phys[:, :dl], phys[:, dl:], B=w.B, H=w.H, N=w.N, scale=w.scale, pages=pages)
     ws = torch.empty((max(1, ddt.verify_workspace_bytes(d, w.prefix_len)),), dtype=torch.uint8, device=dev)
 

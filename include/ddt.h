@@ -269,8 +269,10 @@ int ddt_greedy_accept(const int32_t* target_ids, const int32_t* draft_ids, const
  *   prefix_len[b] <- P + k + 1        (device array, updated in place),
  *   src_slot[b][j] = P + path[b][j] for j <= k, else -1   (NULL allowed).
  * Rows from P+k+1 on are left as they were.  A request whose accept_len is
- * outside [0, N) or whose path is not 0 followed by increasing node numbers
- * below N is left untouched (src_slot all -1, prefix_len unchanged).
+ * outside [0, N), whose path is not 0 followed by increasing node numbers
+ * below N, or whose slots P .. P+path[k] cannot be mapped (P < 0; paged:
+ * a slot past the request's table row) is left untouched (src_slot all -1,
+ * prefix_len unchanged); these checks run on the device.
  * Layout arguments as in ddt_attn_desc; row strides times the element size
  * and the pointers must be 4-byte aligned.
  */
@@ -281,9 +283,11 @@ int ddt_compact_kv(void* ckv, int64_t ld_ckv, void* kpe, int64_t ld_kpe, int dty
 /*
  * ddt_compact_kv on a paged cache (see ddt_attn_desc): slot t of request b
  * is pool row block_table[b*bt_ld + t/page_size]*page_size + t%page_size.
- * page_size a power of two in [1, 65536], bt_ld >= 1; the table must name
- * pages for slots [0, P_b + N) of every request (device data, not checked).
- * Otherwise as ddt_compact_kv.
+ * page_size a power of two in [1, 65536], bt_ld >= 1.  A request whose
+ * slots P .. P+path[k] run past its table row (bt_ld pages) is left
+ * untouched, like an invalid path; the page numbers themselves are device
+ * data and must name pages inside the pool (not checked).  Otherwise as
+ * ddt_compact_kv.
  */
 int ddt_compact_kv_paged(void* ckv, int64_t ld_ckv, void* kpe, int64_t ld_kpe, int dtype, int d_lat, int d_rope,
                          const int32_t* block_table, int64_t bt_ld, int page_size, int32_t* prefix_len,
@@ -300,7 +304,9 @@ int ddt_compact_kv_paged(void* ckv, int64_t ld_ckv, void* kpe, int64_t ld_kpe, i
  * from prefix_len and the advanced ones written to new_prefix_len (device
  * arrays of B; the same array for an in-place update).  Other arguments,
  * layouts and errors as for those two calls (the walk's path is always a
- * valid compaction path).
+ * valid compaction path; a request whose slots cannot be mapped still gets
+ * its acceptance outputs, and new_prefix_len = prefix_len with no rows
+ * moved).
  */
 int ddt_accept_compact(const int32_t* target_ids, const int32_t* draft_ids, const int32_t* parents, int B, int N,
                        int32_t* accept_len, int32_t* path, int32_t* tokens, void* ckv, int64_t ld_ckv, void* kpe,

@@ -33,6 +33,9 @@ __global__ __launch_bounds__(ddt::kCompactThreads) void compact_kernel(
         for (int j = threadIdx.x; j <= k; j += blockDim.x) {
             const int p = path[off + j];
             bad |= (j == 0) ? (p != 0) : (p <= path[off + j - 1] || p >= N);
+            // the path's last slot bounds every slot moved: it must be
+            // mappable (P >= 0; paged: inside the request's table row)
+            if (j == k) bad |= !map.covers(P, (int64_t)p + 1);
         }
         if (bad) atomicOr(&s_bad, 1);
     }

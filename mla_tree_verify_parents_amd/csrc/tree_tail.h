@@ -79,6 +79,13 @@ struct SlotMap {
         const int64_t pg = table[(int64_t)b * ld + (t >> shift)];
         return (pg << shift) + (t & ((1ll << shift) - 1));
     }
+    // Whether slots [P, P + n) can be mapped: P >= 0 and, paged, every one of
+    // them falls inside the request's table row (a stale or oversized length
+    // must not reach the next request's table entries or past the table).
+    __device__ bool covers(int64_t P, int64_t n) const {
+        if (P < 0 || n < 1) return false;
+        return table == nullptr || ((P + n - 1) >> shift) < ld;
+    }
 };
 
 // Cache slot P+j <- cache slot P+path(j), j = 0..k, for a path that
@@ -165,8 +172,17 @@ __device__ void accept_compact_body(const AcceptCompactArgs& a, int b, U* stage)
     if (threadIdx.x < kWave)
         write_accept(a.target, off, sdraft, spath, n, N, b, threadIdx.x, a.accept_len, a.path, a.tokens);
     const int64_t P = a.prefix_len[b];
+    // slots P .. P + path[k] must be mappable (a committed length that is
+    // negative or, paged, runs past the table row leaves the request's
+    // cache and length untouched)
+    const bool ok = a.map.covers(P, (int64_t)spath[k] + 1);
     if (a.src_slot != nullptr) {
-        for (int j = threadIdx.x; j < N; j += blockDim.x) a.src_slot[off + j] = j <= k ? (int32_t)(P + spath[j]) : -1;
+        for (int j = threadIdx.x; j < N; j += blockDim.x)
+            a.src_slot[off + j] = (ok && j <= k) ? (int32_t)(P + spath[j]) : -1;
+    }
+    if (!ok) {
+        if (threadIdx.x == 0) a.new_prefix_len[b] = (int32_t)P;  // (the value every thread read: no race if aliased)
+        return;
     }
     copy_path_rows<U>(a.ckv, a.ld_ckv, a.kpe, a.ld_kpe, a.ckv_units, a.kpe_units, a.map, b, P, k, a.rows_per_block,
                       stage, [&](int j) { return spath[j]; });  // (ends with a barrier: every thread has read P)

@@ -121,6 +121,15 @@ def _contig(t, dtype, name):
     return t
 
 
+def _src_slot(src_slot, B, N):
+    """The optional [B, N] int32 src_slot output: the library writes B*N entries."""
+    if src_slot is not None:
+        _contig(src_slot, torch.int32, "src_slot")
+        if tuple(src_slot.shape) != (B, N):
+            raise ValueError(f"src_slot must be [B, N] = [{B}, {N}], got {tuple(src_slot.shape)}")
+    return src_slot
+
+
 def _rows(t, name):
     """2-D view with unit column stride -> row stride in elements."""
     if t.dim() != 2 or t.stride(1) != 1:
@@ -289,6 +298,7 @@ def verify_step(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, logits, d
         new_prefix_len = prefix_len
     _contig(new_prefix_len, torch.int32, "new_prefix_len")
     accept_len, path, tokens = _accept_outputs(parents, accept_len, path, tokens)
+    _src_slot(src_slot, desc.B, desc.N)
     acc = AcceptTask(_p(draft_ids), _p(parents), _p(accept_len), _p(path), _p(tokens), _p(prefix_len),
                      _p(new_prefix_len), _p(src_slot))
     _check(lib().ddt_verify_step(ctypes.byref(desc), _p(q_lat), _p(q_pe), _p(ckv), _p(kpe), _p(kv_base),
@@ -351,6 +361,7 @@ def compact_kv(ckv, kpe, kv_base, prefix_len, path, accept_len, src_slot=None, p
     _contig(path, torch.int32, "path")
     _contig(accept_len, torch.int32, "accept_len")
     B, N = path.shape
+    _src_slot(src_slot, B, N)
     if pages is not None:
         table, page_size = pages
         _contig(table, torch.int32, "block_table")
@@ -384,6 +395,7 @@ def accept_compact(target_ids, draft_ids, parents, ckv, kpe, kv_base, prefix_len
     _contig(new_prefix_len, torch.int32, "new_prefix_len")
     B, N = parents.shape
     accept_len, path, tokens = _accept_outputs(parents, accept_len, path, tokens)
+    _src_slot(src_slot, B, N)
     _check(lib().ddt_accept_compact(_p(target_ids), _p(draft_ids), _p(parents), B, N, _p(accept_len), _p(path),
                                     _p(tokens), _p(ckv), _rows(ckv, "ckv"), _p(kpe), _rows(kpe, "kpe"),
                                     _dtype_code(ckv), ckv.shape[1], kpe.shape[1], _p(kv_base), _p(prefix_len),

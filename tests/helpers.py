@@ -65,4 +65,38 @@ def oracle_attn(orc, w: synth.Workload, rows=None):
                            H=w.H, scale=w.scale, rows=rows)
 
 
+# Whole-tensor relative L2 of out and of lse: the tolerance the method's
+# statement fixes (fp32 inputs 1e-5; bf16 inputs with fp32 accumulation 1e-2).
 ATTN_TOL = {"f32": 1e-5, "bf16": 1e-2}
+# Every row's relative L2 error of out.  On the bf16 path each probability
+# and each stored output element is rounded to nearest even in bf16 (unit
+# roundoff u = 2^-8, independent errors), so a row's relative L2 error is a
+# few times u/sqrt(3) ~ 2.3e-3 whatever the row's key count; 2e-2 leaves a
+# wide margin yet fails one wrong 32-column tile of a row (~0.25).  fp32
+# inputs: fp32 probabilities and outputs, row errors ~1e-6.
+ROW_TOL = {"f32": 2e-5, "bf16": 2e-2}
+# Largest absolute lse error.  lse = m + ln(sum of probabilities) with the
+# probabilities rounded to bf16 before they are summed, so the sum is off
+# by at most a factor 1 +- u: |error| <= ln(1 + 2^-8) ~ 3.9e-3, plus fp32
+# rounding of scores and sums (~1e-6).  fp32 inputs: probabilities in fp32.
+LSE_ABS_TOL = {"f32": 1e-4, "bf16": 5e-3}
+
+
+def attn_errors(out, lse, ref_out, ref_lse):
+    """(rel-L2 of out, rel-L2 of lse, largest per-row rel-L2 of out, largest |lse error|)."""
+    o = as_f64(out) if out.dtype == np.uint16 else np.asarray(out, np.float64)
+    o = o.reshape(ref_out.shape)
+    lse = np.asarray(lse, np.float64).reshape(ref_lse.shape)
+    assert np.isfinite(o).all() and np.isfinite(lse).all(), "non-finite attention output"
+    row = np.linalg.norm(o - ref_out, axis=1) / np.maximum(np.linalg.norm(ref_out, axis=1), 1e-300)
+    return rel_l2(o, ref_out), rel_l2(lse, ref_lse), float(row.max()), float(np.abs(lse - ref_lse).max())
+
+
+def check_attn(out, lse, ref_out, ref_lse, dtype, what=""):
+    """Attention outputs against the oracle: whole-tensor rel-L2 of out and
+    lse within ATTN_TOL, every row of out within ROW_TOL, every lse within
+    LSE_ABS_TOL.  out: host array (bf16 bits or float), rows as ref_out."""
+    e = attn_errors(out, lse, ref_out, ref_lse)
+    ok = e[0] <= ATTN_TOL[dtype] and e[1] <= ATTN_TOL[dtype] and e[2] <= ROW_TOL[dtype] and e[3] <= LSE_ABS_TOL[dtype]
+    assert ok, (what, "rel_l2 out %.3e lse %.3e, max row %.3e, max |lse err| %.3e" % e)
+    return e

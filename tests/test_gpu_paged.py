@@ -14,7 +14,7 @@ import pytest
 import torch
 
 from mla_tree_verify_parents_amd import ddt, synth
-from tests.helpers import ATTN_TOL, DevWorkload, as_f64, oracle_attn, rel_l2, to_dev, to_host
+from tests.helpers import DevWorkload, check_attn, oracle_attn, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -77,8 +77,7 @@ def test_paged_attention_equals_contiguous(orc, ps, prefix_range, kv_chunk, N):
         assert torch.equal(out_c.view(torch.int16), out_p.view(torch.int16))
         assert torch.equal(lse_c, lse_p)
     ref_out, ref_lse = oracle_attn(orc, w)
-    assert rel_l2(as_f64(to_host(out_p)), ref_out) <= ATTN_TOL["bf16"]
-    assert rel_l2(to_host(lse_p), ref_lse) <= ATTN_TOL["bf16"]
+    check_attn(to_host(out_p), to_host(lse_p), ref_out, ref_lse, "bf16")
 
 
 @pytest.mark.parametrize("ps,with_mask", [(32, False), (128, True), (64, False)])
@@ -112,8 +111,7 @@ def test_paged_verify_step(orc, ps, with_mask):
         H=w.H, scale=w.scale, new_prefix_len=new_pl, src_slot=src, pages=(td, ps))
     torch.cuda.synchronize()
     assert (to_host(idx).reshape(B, N) == t_ref).all()
-    assert rel_l2(as_f64(to_host(out)), ref_out) <= ATTN_TOL["bf16"]
-    assert rel_l2(to_host(lse), ref_lse) <= ATTN_TOL["bf16"]
+    check_attn(to_host(out), to_host(lse), ref_out, ref_lse, "bf16")
     assert (to_host(acc) == oa).all() and (to_host(path) == op).all() and (to_host(tok) == ot).all()
     assert (to_host(npl) == opl).all() and (to_host(src) == osrc).all()
     got_phys = np.ascontiguousarray(to_host(pd))
@@ -160,3 +158,145 @@ def test_paged_compact_kv(orc, ps, cfg):
         tt = np.arange(int(w.prefix_len[b]) + N)
         named[table[b, tt // ps].astype(np.int64) * ps + tt % ps] = True
     assert (got_phys[~named].view(np.uint8) == phys[~named].view(np.uint8)).all()
+
+
+def _spare_page(table, w, ps, n_pages):
+    """A page of the pool that no request's table row names."""
+    T = w.prefix_len.astype(np.int64) + w.N
+    owned = set()
+    for b in range(w.B):
+        owned.update(table[b, : (T[b] + ps - 1) // ps].tolist())
+    return min(set(range(n_pages)) - owned)
+
+
+def _padded_table(table, pad_rows, spare_page):
+    """A device copy of `table` with pad_rows extra rows naming spare_page,
+    and the [B, bt_ld] view of its first rows: slots past a request's row
+    then still read valid table entries that name a valid page."""
+    B, L = table.shape
+    full = np.full((B + pad_rows, L), spare_page, np.int32)
+    full[:B] = table
+    d = to_dev(full)
+    return d, d[:B]
+
+
+def _oracle_compact_some(orc, pool, dl, kv_base, P, path, acc, keep):
+    """The oracle's compaction of the requests in `keep` only (in place on
+    pool); the others keep their length and report src_slot -1."""
+    B, N = path.shape
+    keep = np.asarray(keep)
+    opl = np.array(P, np.int32, copy=True)
+    osrc = np.full((B, N), -1, np.int32)
+    if len(keep):
+        pl, src = orc.compact_kv(pool[:, :dl], pool[:, dl:], kv_base[keep], P[keep], path[keep], acc[keep])
+        opl[keep], osrc[keep] = pl, src
+    return opl, osrc
+
+
+def test_paged_compact_unmappable_left_untouched(orc):
+    """ddt_compact_kv_paged with device lengths whose accepted slots run past
+    the request's table row (a stale or oversized length): those requests
+    are left untouched (src_slot -1, length unchanged, no row written),
+    the others compacted as the oracle does."""
+    w = synth.workload(3, B=3, N=8, prefix_range=(40, 90))
+    ps, B, N, dl = 32, 3, 8, 512
+    rng = np.random.default_rng(11)
+    phys, table = to_paged(w, ps, rng, spare=2)
+    spare = _spare_page(table, w, ps, phys.shape[0] // ps)
+    L = table.shape[1]
+    path = np.full((B, N), -1, np.int32)
+    path[:, :3] = [0, 1, 3]
+    acc = np.full(B, 2, np.int32)
+    P_dev = w.prefix_len.copy()
+    P_dev[1] = L * ps - 2                               # slot P+3 is past row 1 (would read row 2's entries)
+    P_dev[2] = L * ps - 1                               # the last request: past the table itself
+    opool = w.pool.copy()
+    opl, osrc = _oracle_compact_some(orc, opool, dl, w.kv_base, w.prefix_len, path, acc, [0])
+    pd = to_dev(phys)
+    td_full, td = _padded_table(table, 2, spare)
+    dpl = to_dev(P_dev)
+    src = torch.empty((B, N), dtype=torch.int32, device="cuda")
+    ddt.compact_kv(pd[:, :dl], pd[:, dl:], None, dpl, to_dev(path), to_dev(acc), src, pages=(td, ps))
+    torch.cuda.synchronize()
+    got_pl = to_host(dpl)
+    assert got_pl[0] == opl[0] and got_pl[1] == P_dev[1] and got_pl[2] == P_dev[2]
+    s = to_host(src)
+    assert (s[0] == osrc[0]).all() and (s[1:] == -1).all()
+    got_phys = np.ascontiguousarray(to_host(pd))
+    assert (from_paged(got_phys, table, ps, w).view(np.uint8) == opool.view(np.uint8)).all()
+    sp = slice(spare * ps, (spare + 1) * ps)
+    assert (got_phys[sp].view(np.uint8) == phys[sp].view(np.uint8)).all()
+
+
+def test_accept_compact_negative_length_left_untouched(orc):
+    """ddt_accept_compact with a negative committed length on the device:
+    acceptance outputs as usual, no row moved, new length = old length."""
+    w = synth.workload(3, B=3, N=16, prefix_range=(40, 90))
+    rng = np.random.default_rng(12)
+    V = 4
+    w.draft_ids = w.draft_ids % V
+    t = synth.planted_targets(rng, w.parents, w.draft_ids, V, 0.9)
+    oa, op, ot = orc.greedy_accept(t, w.draft_ids, w.parents)
+    B, N, dl = w.B, w.N, w.d_lat
+    P_dev = w.prefix_len.copy()
+    P_dev[1] = -int(N)                      # kv_base >= 32 + ...: even a broken guard stays in the pool
+    assert int(w.kv_base[1]) - N >= 0
+    opool = w.pool.copy()
+    opl, osrc = _oracle_compact_some(orc, opool, dl, w.kv_base, w.prefix_len, op, oa, [0, 2])
+    dw = DevWorkload(w)
+    dpl = to_dev(P_dev)
+    npl = torch.full((B,), 99, dtype=torch.int32, device="cuda")
+    src = torch.empty((B, N), dtype=torch.int32, device="cuda")
+    acc, path, tok = ddt.accept_compact(to_dev(t), dw.draft, dw.parents, dw.ckv(), dw.kpe(), dw.kv_base, dpl,
+                                        src_slot=src, new_prefix_len=npl)
+    torch.cuda.synchronize()
+    assert (to_host(acc) == oa).all() and (to_host(path) == op).all() and (to_host(tok) == ot).all()
+    got = to_host(npl)
+    assert got[1] == P_dev[1] and got[0] == opl[0] and got[2] == opl[2]
+    s = to_host(src)
+    assert (s[1] == -1).all() and (s[0] == osrc[0]).all() and (s[2] == osrc[2]).all()
+    assert (to_host(dw.pool).view(np.uint8) == opool.view(np.uint8)).all()
+
+
+def test_paged_verify_step_unmappable_length(orc):
+    """The paged verify step with a device length past the table row for
+    one request (the host length, which plans the attention, is valid):
+    that request's acceptance is reported and its cache left as it was."""
+    w = synth.workload(3, B=3, prefix_range=(100, 600))
+    ps = 32
+    rng = np.random.default_rng(13)
+    V = 3000
+    w.draft_ids = w.draft_ids % V
+    t = synth.planted_targets(rng, w.parents, w.draft_ids, V, 0.8)
+    x = synth.target_logits(rng, t.reshape(-1), V)
+    phys, table = to_paged(w, ps, rng, spare=2)
+    spare = _spare_page(table, w, ps, phys.shape[0] // ps)
+    B, N, dl = w.B, w.N, w.d_lat
+    L = table.shape[1]
+    t_ref = orc.argmax(x).reshape(B, N)
+    oa, op, ot = orc.greedy_accept(t_ref, w.draft_ids, w.parents)
+    P_dev = w.prefix_len.copy()
+    P_dev[2] = L * ps                                   # every slot P.. is past the last request's row
+    opool = w.pool.copy()
+    opl, osrc = _oracle_compact_some(orc, opool, dl, w.kv_base, w.prefix_len, op, oa, [0, 1])
+    pd = to_dev(phys)
+    td_full, td = _padded_table(table, 2 + N // ps, spare)
+    q = to_dev(w.q)
+    parents, draft = to_dev(w.parents), to_dev(w.draft_ids)
+    dpl = to_dev(P_dev)
+    npl = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    src = torch.empty((B, N), dtype=torch.int32, device="cuda")
+    _, _, idx, acc, path, tok, _ = ddt.verify_step(
+        q[:, :dl], q[:, dl:], pd[:, :dl], pd[:, dl:], None, w.prefix_len, None, to_dev(x), draft, parents, dpl,
+        H=w.H, scale=w.scale, new_prefix_len=npl, src_slot=src, pages=(td, ps))
+    torch.cuda.synchronize()
+    assert (to_host(idx).reshape(B, N) == t_ref).all()
+    assert (to_host(acc) == oa).all() and (to_host(path) == op).all() and (to_host(tok) == ot).all()
+    got = to_host(npl)
+    assert got[2] == P_dev[2] and (got[:2] == opl[:2]).all()
+    s = to_host(src)
+    assert (s[2] == -1).all() and (s[:2] == osrc[:2]).all()
+    got_phys = np.ascontiguousarray(to_host(pd))
+    assert (from_paged(got_phys, table, ps, w).view(np.uint8) == opool.view(np.uint8)).all()
+    sp = slice(spare * ps, (spare + 1) * ps)
+    assert (got_phys[sp].view(np.uint8) == phys[sp].view(np.uint8)).all()

@@ -15,7 +15,7 @@ import torch
 
 from mla_tree_verify_parents_amd import ddt, synth
 from mla_tree_verify_parents_amd.prefill import ChunkedPrefill
-from tests.helpers import ATTN_TOL, as_f64, rel_l2, to_dev, to_host
+from tests.helpers import as_f64, check_attn, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -69,5 +69,4 @@ def test_chunked_prefill_equals_unchunked_oracle(orc, T, P0, chunk):
                                        np.array([P0], np.int32), chain, H=H, scale=scale, rows=rows)
     o = as_f64(to_host(out))[rows]
     l_ = to_host(lse).astype(np.float64)[rows]
-    assert rel_l2(o, ref_out) <= ATTN_TOL["bf16"]
-    assert rel_l2(l_, ref_lse) <= ATTN_TOL["bf16"]
+    check_attn(o, l_, ref_out, ref_lse, "bf16")
