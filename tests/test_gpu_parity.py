@@ -230,7 +230,7 @@ def _attn_check(orc, w, kv_chunks=(0,), rows=None):
             o, lse = o[rows], lse[rows]
         e = check_attn(o, lse, ref_out, ref_lse, w.dtype, f"{w.name} kv_chunk={ch}")
         print(f"{w.name} kv_chunk={ch}: rel_l2 out {e[0]:.3e} lse {e[1]:.3e}, max row {e[2]:.3e}, "
-              f"max |lse err| {e[3]:.3e}")
+              f"max lse error {e[3]:.3f} of its bound")
         results.append(o)
     return results
 
