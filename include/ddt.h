@@ -166,6 +166,28 @@ int ddt_verify_attn(const ddt_attn_desc* d, const void* q_lat, const void* q_pe,
                     size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * ddt_verify_attn for callers that cannot allocate device memory or pass a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, plan, kernels and results as
+ * ddt_verify_attn, without the workspace: the split partials go to a
+ * device array inside the library, DDT_NOALLOC_SCRATCH_BYTES bytes per
+ * device (held by every device the library runs on until the process
+ * ends).  A call whose partials need more than that (the figure
+ * ddt_verify_workspace returns) fails with DDT_EWORKSPACE before anything
+ * is launched; use ddt_verify_attn with a workspace then.  Nothing is
+ * allocated and nothing needs clearing (every partial is written before
+ * the merge reads it).  All calls on one device share that device's
+ * array, so calls that overlap on one device (different streams or host
+ * threads without ordering) race: the caller must order them.
+ * ddt_verify_noalloc_scratch_bytes() returns DDT_NOALLOC_SCRATCH_BYTES.
+ */
+#define DDT_NOALLOC_SCRATCH_BYTES (64u << 20)
+int ddt_verify_attn_noalloc(const ddt_attn_desc* d, const void* q_lat, const void* q_pe, const void* ckv,
+                            const void* kpe, const int64_t* kv_base, const int32_t* prefix_len_host,
+                            const uint64_t* mask, void* out, float* lse, hipStream_t stream);
+size_t ddt_verify_noalloc_scratch_bytes(void);
+
+/*
  * Target argmax.  [Ambition], section "The Decision Architecture": greedy
  * token selection from logits.  idx[r] = lowest index of the maximum of row
  * r of logits (row r at logits + r*ld, V entries, dtype fp32 or bf16).  -0

@@ -47,6 +47,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "argmax_scan.h"
@@ -1693,6 +1694,35 @@ int setup_argmax(const ddt_argmax_task* am, const Plan& pl, VerifyParams* vp, in
     return DDT_OK;
 }
 
+// Scratch of ddt_verify_attn_noalloc: the split partials in a file-scope
+// device array instead of a caller workspace (each device the library runs
+// on holds its own copy until the process ends).  Host code never uses the
+// array's name as an address: scratch_ptr() asks the runtime for this
+// device's copy once and keeps it.
+constexpr size_t kNoAllocScratchBytes = (size_t)DDT_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// The current device's copy of `scratch` (looked up on the first call on
+// that device, with that device current); DDT_OK or DDT_EHIP.
+int scratch_ptr(void** ptr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DDT_EHIP;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        // (two threads may both look it up: the runtime returns the same address)
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+            (void)hipGetLastError();
+            return DDT_EHIP;
+        }
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    *ptr = p;
+    return DDT_OK;
+}
+
 }  // namespace
 
 extern "C" int ddt_verify_workspace(const ddt_attn_desc* d, const int32_t* prefix_len_host, size_t* bytes) {
@@ -1714,6 +1744,26 @@ extern "C" int ddt_verify_attn(const ddt_attn_desc* d, const void* q_lat, const 
     if (rc != DDT_OK) return rc;
     return run(d, vp, pl, 0, stream);
 }
+
+extern "C" int ddt_verify_attn_noalloc(const ddt_attn_desc* d, const void* q_lat, const void* q_pe, const void* ckv,
+                                       const void* kpe, const int64_t* kv_base, const int32_t* prefix_len_host,
+                                       const uint64_t* mask, void* out, float* lse, hipStream_t stream) {
+    const int rc0 = check_desc(d, prefix_len_host);
+    if (rc0 != DDT_OK) return rc0;
+    // the same plan as ddt_verify_attn; its partials must fit the scratch
+    if (make_plan(d, prefix_len_host, nullptr).ws_bytes > kNoAllocScratchBytes) return DDT_EWORKSPACE;
+    void* ws = nullptr;
+    const int rs = scratch_ptr(&ws);
+    if (rs != DDT_OK) return rs;
+    VerifyParams vp{};
+    Plan pl;
+    const int rc = setup_attn(d, q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, nullptr, out, lse, ws,
+                              kNoAllocScratchBytes, &vp, &pl);
+    if (rc != DDT_OK) return rc;
+    return run(d, vp, pl, 0, stream);
+}
+
+extern "C" size_t ddt_verify_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
 
 extern "C" int ddt_verify_attn_argmax(const ddt_attn_desc* d, const void* q_lat, const void* q_pe, const void* ckv,
                                       const void* kpe, const int64_t* kv_base, const int32_t* prefix_len_host,

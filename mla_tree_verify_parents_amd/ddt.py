@@ -63,6 +63,9 @@ def lib():
         L.ddt_build_mask.argtypes = [P, i32, i32, P, P, P, P]
         L.ddt_verify_workspace.argtypes = [ctypes.POINTER(AttnDesc), P, ctypes.POINTER(sz)]
         L.ddt_verify_attn.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P, P, P, P, sz, P]
+        L.ddt_verify_attn_noalloc.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P, P, P, P]
+        L.ddt_verify_noalloc_scratch_bytes.argtypes = []
+        L.ddt_verify_noalloc_scratch_bytes.restype = ctypes.c_size_t
         L.ddt_argmax_workspace.argtypes = [i64, i64, ctypes.POINTER(sz)]
         L.ddt_argmax.argtypes = [P, i32, i64, i64, i64, P, P, sz, P]
         L.ddt_greedy_accept.argtypes = [P, P, P, i32, i32, P, P, P, P]
@@ -81,7 +84,7 @@ def lib():
         L.ddt_probe_mfma_bf16.argtypes = [P, P, P, i32, i32, P]
         L.ddt_probe_read.argtypes = [P, sz, P, i32, P]
         L.ddt_probe_copy.argtypes = [P, P, sz, i32, P]
-        for f in ("ddt_version", "ddt_build_mask", "ddt_verify_workspace", "ddt_verify_attn",
+        for f in ("ddt_version", "ddt_build_mask", "ddt_verify_workspace", "ddt_verify_attn", "ddt_verify_attn_noalloc",
                   "ddt_argmax_workspace", "ddt_argmax", "ddt_greedy_accept", "ddt_compact_kv", "ddt_compact_kv_paged",
                   "ddt_accept_compact", "ddt_verify_attn_argmax", "ddt_verify_step",
                   "ddt_draft_topk_workspace", "ddt_draft_topk", "ddt_best_first_tree",
@@ -186,7 +189,7 @@ def verify_workspace_bytes(desc: AttnDesc, prefix_len_host) -> int:
 
 
 def _attn_args(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, H, scale, out, lse, workspace, kv_chunk,
-               BN=None, pages=None):
+               BN=None, pages=None, alloc_workspace=True):
     for t, n in ((q_lat, "q_lat"), (q_pe, "q_pe"), (ckv, "ckv"), (kpe, "kpe")):
         _dev(t, q_lat.dtype, n)
     if pages is None or kv_base is not None:
@@ -209,7 +212,7 @@ def _attn_args(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, H, scale, 
         lse = torch.empty((rows,), dtype=torch.float32, device=q_lat.device)
     _contig(out, q_lat.dtype, "out")
     _contig(lse, torch.float32, "lse")
-    if workspace is None:  # (a caller's workspace is checked by the library)
+    if workspace is None and alloc_workspace:  # (a caller's workspace is checked by the library)
         need = verify_workspace_bytes(desc, pl)
         if need > 0:
             workspace = torch.empty((need,), dtype=torch.uint8, device=q_lat.device)
@@ -230,6 +233,26 @@ def verify_attn(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, *, H, sca
                                  pl.ctypes.data, _p(mask), _p(out), _p(lse), _p(workspace), ws_n,
                                  _stream(stream)), "ddt_verify_attn")
     return out, lse
+
+
+def verify_attn_noalloc(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, *, H, scale, out, lse, kv_chunk=0,
+                        pages=None, stream=None):
+    """verify_attn without a workspace and without allocating: the library
+    keeps the split partials in its own per-device scratch
+    (noalloc_scratch_bytes()); out and lse must be given.  Calls on one
+    device share that scratch and must not overlap."""
+    if out is None or lse is None:
+        raise ValueError("verify_attn_noalloc allocates nothing: pass out and lse")
+    desc, pl, out, lse, _, _ = _attn_args(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, H, scale, out, lse,
+                                          None, kv_chunk, pages=pages, alloc_workspace=False)
+    _check(lib().ddt_verify_attn_noalloc(ctypes.byref(desc), _p(q_lat), _p(q_pe), _p(ckv), _p(kpe), _p(kv_base),
+                                         pl.ctypes.data, _p(mask), _p(out), _p(lse), _stream(stream)),
+           "ddt_verify_attn_noalloc")
+    return out, lse
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(lib().ddt_verify_noalloc_scratch_bytes())
 
 
 def _argmax_task(logits, idx, argmax_workspace):

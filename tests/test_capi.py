@@ -88,6 +88,25 @@ def test_host_side_validation(lib):
     assert lib.ddt_verify_attn(ctypes.byref(d), f, f, f, f, null, pl, f, f, f, f, 1 << 30, null) == -1
 
 
+def test_noalloc_validation(lib):
+    """ddt_verify_attn_noalloc: its scratch size, and the host-side refusals
+    that come before any device call (placeholder pointers, never
+    dereferenced)."""
+    assert lib.ddt_verify_noalloc_scratch_bytes() == 64 << 20
+    null = None
+    pl = (ctypes.c_int32 * 1)(100)
+    assert lib.ddt_verify_attn_noalloc(null, null, null, null, null, null, pl, null, null, null, null) == -1
+    bad = ddt.AttnDesc(1, 8, 64, 256, 64, ddt.DDT_BF16, 0.04, 0, 576, 576, 576, 576)
+    f = ctypes.c_void_p(1 << 20)
+    assert lib.ddt_verify_attn_noalloc(ctypes.byref(bad), f, f, f, f, f, pl, f, f, f, null) == -2   # not built
+    # 32 requests x 5 splits x 8 row tiles of bf16 partials (80 MiB): beyond the scratch
+    P = (ctypes.c_int32 * 32)(*([1024] * 32))
+    d = ddt.AttnDesc(32, 8, 64, 512, 64, ddt.DDT_BF16, 0.04, 256, 576, 576, 576, 576)
+    n = ctypes.c_size_t(0)
+    assert lib.ddt_verify_workspace(ctypes.byref(d), P, ctypes.byref(n)) == 0 and n.value > 64 << 20
+    assert lib.ddt_verify_attn_noalloc(ctypes.byref(d), f, f, f, f, f, P, f, f, f, null) == -3
+
+
 def test_verify_step_validation(lib):
     """ddt_verify_step rejects a missing or mismatched argmax task and a
     missing acceptance output before launching.  The device pointers are
