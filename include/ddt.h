@@ -102,7 +102,8 @@ int ddt_build_mask(const int32_t* parents, int B, int N, uint64_t* mask, int32_t
  * kv_chunk: keys per split of the key range (rounded up to a multiple of
  * 32); 0 lets the library choose.  Results do not depend on it beyond
  * rounding: the partial outputs of a split request pass through the
- * workspace in the input dtype.
+ * workspace in fp32 (accumulation stays fp32 from the products to the
+ * merged output).
  *
  * Built instances (d_lat, d_rope, dtype): (512, 64, BF16), (64, 16, F32).
  * Alignment: q_lat, q_pe, ckv, kpe 16-byte aligned; every row stride times

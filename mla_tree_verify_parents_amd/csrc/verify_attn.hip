@@ -36,8 +36,8 @@
 //  * Each request's key range is cut into splits (the host picks the chunk
 //    that minimises an estimate of the launch's finish time) and work items
 //    are dealt to the XCDs so that row tiles of one split share an L2.
-//    Split partials (unnormalised, in the input dtype, MFMA register
-//    order) with each row's softmax reference and row sum go to the
+//    Split partials (unnormalised, fp32, MFMA register order) with each
+//    row's softmax reference and row sum go to the
 //    workspace; verify_combine weighs, sums and normalises them.  A request with one split writes its output directly.
 //  * Optional co-tasks: target-argmax workgroups on the CUs the attention
 //    leaves idle (verify_split), and acceptance + compaction workgroups
@@ -443,7 +443,7 @@ struct VerifyParams {
     const int32_t* parents;     // then each row's bits come from the parents (N <= 128)
     void* out;
     float* lse;
-    void* ws_o;     // [slot][row group][DL/32][4][64][4] in the input dtype, unnormalised partial outputs
+    void* ws_o;     // [slot][row group][DL/32][4][64][4] fp32, unnormalised partial outputs
     float2* ws_ml;  // [slot][ROWS_WG] (softmax reference m, log2 domain; row sum l) of the unnormalised partials
     int64_t ld_ql, ld_qp, ld_ckv, ld_kpe;
     int B, H, N, W, rows, row_tiles, chunk, total_wg;
@@ -1186,9 +1186,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 }
             }
         } else {
-            // unnormalised partials in the input dtype (the merge divides):
-            // one 64-lane store writes 64 x 4 consecutive elements
-            T* ws = static_cast<T*>(p.ws_o) + (size_t)wl * (ROWS_WG * DL) + (size_t)rb * (32 * DL) +
+            // unnormalised fp32 partials (the merge divides): one 64-lane
+            // store writes 64 x 4 consecutive elements
+            float* ws = static_cast<float*>(p.ws_o) + (size_t)wl * (ROWS_WG * DL) + (size_t)rb * (32 * DL) +
                     (size_t)half * NCH * (4 * 64 * 4);
 #pragma unroll
             for (int c = 0; c < NCH; ++c) {
@@ -1197,7 +1197,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                     float v[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) v[e] = o[rb][c][v4 * 4 + e];
-                    store4_nt<T>(ws + ((c * 4 + v4) * 64 + lane) * 4, v);
+                    store4_nt<float>(ws + ((c * 4 + v4) * 64 + lane) * 4, v);
                 }
             }
         }
@@ -1262,7 +1262,7 @@ __global__ __launch_bounds__(256) void verify_combine(const VerifyParams p) {
                 if (s0 + k < ns) {  // uniform: no load for the padding
                     const int slot = slot_of(s0 + k);
                     ml[k] = p.ws_ml[(size_t)slot * ROWS_WG + prow];
-                    v[k] = load4<T>(static_cast<const T*>(p.ws_o) + ((size_t)slot * NW + wave) * (NCTW * 4 * 64 * 4) +
+                    v[k] = load4<float>(static_cast<const float*>(p.ws_o) + ((size_t)slot * NW + wave) * (NCTW * 4 * 64 * 4) +
                                     ((c * 4 + grp) * 64 + lane) * 4);
                 }
             }
@@ -1360,6 +1360,7 @@ int check_desc(const ddt_attn_desc* d, const int32_t* prefix_len_host) {
 // workgroup); a merge launch is added when any request is split.
 constexpr int64_t kItemOverhead = 10;   // prologue, pipeline fill and epilogue of a workgroup, in tiles
 constexpr int64_t kMergeCost = 8;       // the split merge launch, in tiles
+constexpr int64_t kPartialRowBytes = 512 * 4;  // fp32 partial output of one row (K2 latent width)
 
 // `T` holds the requests' key counts in descending order.
 int64_t plan_cost(const int64_t* T, int B, int row_tiles, int64_t chunk, int cus) {
@@ -1423,7 +1424,18 @@ int64_t plan_cost(const int64_t* T, int B, int row_tiles, int64_t chunk, int cus
                 heap[0].n += loaded[j].n;
         }
     }
-    return finish + (split ? kMergeCost : 0);
+    // the split partials: in a launch of one round every split work item
+    // writes its fp32 partials at once at the end and the merge reads them
+    // back right after, all exposed; with several rounds the writes overlap
+    // other work items and mostly the merge's read is left (measured at the
+    // K2-like head share: 25.9 us at 256 keys per split, 23.9 at 384)
+    int64_t part_items = 0;
+    for (int b = 0; b < B; ++b)
+        if (T[b] > chunk) part_items += (T[b] + chunk - 1) / chunk * row_tiles;
+    const int64_t part_mib = part_items * ROWS_WG * kPartialRowBytes >> 20;
+    const int64_t items_all = items + (int64_t)nt * row_tiles;
+    const int64_t part_cost = items_all <= cus ? part_mib : part_mib / 16;
+    return finish + (split ? kMergeCost : 0) + part_cost;
 }
 
 // Longest split: a paged split lists at most kMaxSplitPages pages in LDS,
@@ -1535,7 +1547,7 @@ Plan make_plan(const ddt_attn_desc* d, const int32_t* P, VerifyParams* vp) {
         vp->units_per_group = upg;
     }
     if (pl.any_split) {
-        const size_t o = (size_t)pl.total_wg * ROWS_WG * d->d_lat * (size_t)ddt::elem_bytes(d->dtype);
+        const size_t o = (size_t)pl.total_wg * ROWS_WG * d->d_lat * sizeof(float);
         pl.ws_ml_off = ddt::round_up(o, 256);
         pl.ws_bytes = pl.ws_ml_off + ddt::round_up((size_t)pl.total_wg * ROWS_WG * sizeof(float2), 256);
     }

@@ -99,7 +99,7 @@ def test_noalloc_validation(lib):
     bad = ddt.AttnDesc(1, 8, 64, 256, 64, ddt.DDT_BF16, 0.04, 0, 576, 576, 576, 576)
     f = ctypes.c_void_p(1 << 20)
     assert lib.ddt_verify_attn_noalloc(ctypes.byref(bad), f, f, f, f, f, pl, f, f, f, null) == -2   # not built
-    # 32 requests x 5 splits x 8 row tiles of bf16 partials (80 MiB): beyond the scratch
+    # 32 requests x 5 splits x 8 row tiles of fp32 partials (160 MiB): beyond the scratch
     P = (ctypes.c_int32 * 32)(*([1024] * 32))
     d = ddt.AttnDesc(32, 8, 64, 512, 64, ddt.DDT_BF16, 0.04, 256, 576, 576, 576, 576)
     n = ctypes.c_size_t(0)
