@@ -181,6 +181,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.config == 5:
+        if args.traffic_probe:
+            return loop_traffic_probe(dev)
         res = run_loop(args, dev, args.warmup, args.loop_steps)
         add_peaks(res, args, dev)
         print(json.dumps(res), flush=True)
@@ -190,11 +192,22 @@ def main():
         return
     if not args.no_extras:
         res["hbm_stages"] = guarded(lambda: time_hbm_stages(dev))
+        progress("HBM stages timed")
         if args.config != 2:
             res["config2"] = guarded(lambda: measure_config(2, args, dev, headline=False))
+            progress("config 2 timed")
             res["config5_loop"] = guarded(lambda: run_loop(args, dev, 3, 20, brief=True))
+            progress("verify loop timed")
     add_peaks(res, args, dev)
     print(json.dumps(res), flush=True)
+
+
+def progress(msg):
+    """A progress line on stderr (stdout carries only the JSON line)."""
+    print(f"bench: {msg} ({time.perf_counter() - T_START:.1f} s)", file=sys.stderr, flush=True)
+
+
+T_START = time.perf_counter()
 
 
 def guarded(f):
@@ -214,6 +227,7 @@ def measure_config(cfg, args, dev, headline):
     from mla_tree_verify_parents_amd import ddt
 
     w, desc = workload_for(cfg)
+    progress(f"config {cfg} inputs drawn")
 
     def to_dev(a):
         if a.dtype == np.uint16:
@@ -321,6 +335,7 @@ def measure_config(cfg, args, dev, headline):
     attn_ms, attn_units = time_windows(g_attn.replay, per_graph, est_attn, stream)
     ms_attn = float(np.median(attn_ms))
     del g_one, g_step, g_a1, g_attn
+    progress(f"config {cfg} step and attention timed")
 
     pairs = w.visible_pairs()
     flops = pairs * FLOP_PER_PAIR
@@ -377,6 +392,7 @@ def measure_config(cfg, args, dev, headline):
                                      f"(at least {COLD_BYTES >> 20} MiB in all), so the last-level cache "
                                      "cannot serve the keys"}
     if not args.no_extras:
+        progress("side measurements (paged, prefill, projections)")
         res["paged"] = guarded(lambda: time_paged(w, dev, q_lat, q_pe, mask, ms_attn))
         res["prefill"] = guarded(lambda: time_prefill(dev))
         res["projections"] = [guarded(lambda: time_projections(B * N, H, dev))]
@@ -385,6 +401,7 @@ def measure_config(cfg, args, dev, headline):
     del pool, q
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
+        progress("oracle timing on the host")
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, flops)
     return res
 
@@ -430,6 +447,30 @@ def time_hbm_stages(dev):
         del gn, g1, x, ws
     res["note"] = "median of 5 windows of back-to-back launches in one graph; bytes = rows x V x 4 read once"
     return res
+
+
+def loop_traffic_probe(dev):
+    """The verify loop's attention launch (first iteration's inputs: 32
+    requests, prefixes U[2048, 65536], 64 nodes) 5 times, then the 256 MiB
+    calibration copy: the program the HBM-traffic counters profile."""
+    import torch
+
+    from mla_tree_verify_parents_amd import ddt, e2e
+
+    loop = e2e.VerifyLoop(steps=1)
+    inp = loop.make_inputs()
+    mask = ddt.build_mask(inp.parents_dev)[0]
+    dl = loop.d_lat
+    ws = loop.workspace_for(inp.prefix_len)
+    for _ in range(5):
+        ddt.verify_attn(inp.q[:, :dl], inp.q[:, dl:], loop.ckv(), loop.kpe(), loop.kv_base, inp.prefix_len, mask,
+                        H=loop.H, scale=loop.scale, out=loop.out, lse=loop.lse, workspace=ws)
+    src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"traffic_probe": "config5", "attn_launches": 5, "calibration_copy_bytes": CALIB_BYTES}),
+          flush=True)
 
 
 def run_loop(args, dev, W, K, brief=False):
