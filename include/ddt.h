@@ -214,7 +214,7 @@ int ddt_argmax(const void* logits, int dtype, int64_t rows, int64_t V, int64_t l
  *                   V = 163840 against fp64)                     fp32
  * Finite logits; 1 <= K <= 16, K <= V <= 2^20, ld >= V.
  * Workspace: ddt_draft_topk_workspace bytes (16-byte aligned), scratch
- * between the two launches (no zeroing needed).
+ * between its launches (no zeroing needed).
  */
 int ddt_draft_topk_workspace(int64_t rows, int64_t V, int K, size_t* bytes);
 int ddt_draft_topk(const float* logits, int64_t rows, int64_t V, int64_t ld, int K, int32_t* ids, float* logp,

@@ -6,16 +6,23 @@
 // ...", section "The Context: Building an Engine from First Principles":
 // the GPU builder replaced a per-request heap on the CPU).
 //
-// ddt_draft_topk: a row of draft logits is cut into chunks of 4096 entries,
-// 16 contiguous entries per thread.  A chunk workgroup keeps each thread's
-// 16 entries in registers and takes the chunk's top K in K rounds of a
-// workgroup maximum over 64-bit keys (order-preserving value bits, then
+// ddt_draft_topk: a row of draft logits is cut into chunks of 16384
+// entries, 64 per thread (16 coalesced 16-byte loads, in registers).  A
+// chunk workgroup reduces the chunk's (maximum, sum of exp(x - maximum))
+// and finds its top K through a threshold: each wavefront takes the K-th
+// largest of its 64 threads' maxima, so at least K entries of the chunk
+// reach the largest of those four values T, and every entry of the chunk's
+// top K is at least T.  The entries >= T (typically K to 2K of them) go to
+// an LDS list, and one wavefront takes the top K of the list in K rounds of
+// a wavefront maximum over 64-bit keys (order-preserving value bits, then
 // the inverted index: the largest key is the largest value at the lowest
-// index); the round's owner thread marks its entry taken.  It also reduces
-// the chunk's (maximum, sum of exp(x - maximum)).  A second launch, one
-// workgroup per row, runs the same K-round selection over the chunks'
+// index).  When the list overflows (many equal values) the workgroup falls
+// back to K rounds of a workgroup maximum over every entry.  A second
+// launch, one workgroup per row, selects the top K among the chunks'
 // candidates and merges the (maximum, sum) pairs into the row's
-// log-sum-exp.  HBM-bound: 4 bytes per logit.
+// log-sum-exp.  HBM-bound: 4 bytes per logit.  (Chunks of 4096 entries with
+// the K workgroup rounds per chunk measured 91 us at 256 x 163840, the
+// rounds dominating.)
 //
 // ddt_best_first_tree: one wavefront per request.  Each pop is a wavefront
 // maximum over packed keys (score, then lower depth, then earlier
@@ -30,16 +37,24 @@
 namespace {
 
 constexpr int kTopkThreads = 256;
-constexpr int kPerThread = 16;                               // entries (or candidates) per thread
-constexpr int kTopkChunk = kTopkThreads * kPerThread;        // 4096 entries per chunk workgroup
+constexpr int kChunkPerThread = 64;                          // entries per thread in a chunk
+constexpr int kTopkChunk = kTopkThreads * kChunkPerThread;   // 16384 entries per chunk workgroup
+constexpr int kCandCap = 1024;                               // LDS list of a chunk's entries >= T
 constexpr int kMaxTopK = 16;
-constexpr int64_t kMaxDraftVocab = (int64_t)kTopkChunk * kTopkThreads * kPerThread / kMaxTopK;  // 2^20
+constexpr int kMergePerLane = 16;                            // candidates per lane in the row merge
+constexpr int64_t kMaxDraftVocab = 1 << 20;
+static_assert(kMaxDraftVocab / kTopkChunk * kMaxTopK <= 64 * kMergePerLane, "the merge holds every candidate");
 
 __device__ inline uint64_t umax(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
-// One step of a wavefront maximum of 64-bit keys by DPP: every lane takes the
-// larger of its key and the key of the lane the DPP control names (lanes
-// with no source, or outside row_mask, keep theirs).
+// One step of a wavefront maximum by DPP: every lane takes the larger of its
+// value and the value of the lane the DPP control names (lanes with no
+// source, or outside row_mask, keep theirs).
+template <int kCtrl, int kRowMask>
+__device__ inline uint32_t dpp_max_step(uint32_t v) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, kCtrl, kRowMask, 0xf, false);
+    return o > v ? o : v;
+}
 template <int kCtrl, int kRowMask>
 __device__ inline uint64_t dpp_max_step(uint64_t v) {
     const int lo = (int)(uint32_t)v, hi = (int)(uint32_t)(v >> 32);
@@ -49,25 +64,30 @@ __device__ inline uint64_t dpp_max_step(uint64_t v) {
     return o > v ? o : v;
 }
 
-// Wavefront maximum of 64-bit keys, returned uniform: prefix maxima inside
+// Wavefront maximum of unsigned keys, returned uniform: prefix maxima inside
 // each row of 16 lanes (row_shr 1, 2, 4, 8), then row 0's and row 2's last
 // lane into rows 1 and 3 (row_bcast:15), then lane 31 into rows 2 and 3
 // (row_bcast:31): lane 63 holds the maximum.
-__device__ inline uint64_t wave_max_u64(uint64_t v) {
+template <typename U>
+__device__ inline U wave_max(U v) {
     v = dpp_max_step<0x111, 0xf>(v);
     v = dpp_max_step<0x112, 0xf>(v);
     v = dpp_max_step<0x114, 0xf>(v);
     v = dpp_max_step<0x118, 0xf>(v);
     v = dpp_max_step<0x142, 0xa>(v);
     v = dpp_max_step<0x143, 0xc>(v);
-    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, 63);
-    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
-    return ((uint64_t)hi << 32) | lo;
+    if constexpr (sizeof(U) == 8) {
+        const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+        const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+        return ((uint64_t)hi << 32) | lo;
+    } else {
+        return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+    }
 }
 
 // Workgroup maximum of one 64-bit key per thread, returned to every thread.
 __device__ inline uint64_t block_max_all(uint64_t v, uint64_t* red) {
-    v = wave_max_u64(v);
+    v = wave_max(v);
     const int wave = threadIdx.x / ddt::kWave;
     __syncthreads();  // the previous round's readers are done with red[]
     if ((threadIdx.x & 63) == 0) red[wave] = v;
@@ -78,129 +98,201 @@ __device__ inline uint64_t block_max_all(uint64_t v, uint64_t* red) {
     return m;
 }
 
-// The K largest keys among every thread's kPerThread keys (0 = empty), in
-// descending order, into out[0..K) (thread 0 writes).  Keys are distinct.
-__device__ inline void select_top(uint64_t (&key)[kPerThread], int K, uint64_t* out, uint64_t* red) {
-    uint32_t taken = 0;
-    auto best = [&]() {
-        uint64_t b = 0;
-#pragma unroll
-        for (int i = 0; i < kPerThread; ++i) b = ((taken >> i) & 1u) ? b : umax(b, key[i]);
-        return b;
-    };
-    uint64_t cand = best();
-    for (int k = 0; k < K; ++k) {
-        const uint64_t m = block_max_all(cand, red);
-        if (threadIdx.x == 0) out[k] = m;
-        if (m != 0 && cand == m) {  // this thread owns the winner: take it
-#pragma unroll
-            for (int i = 0; i < kPerThread; ++i)
-                if (key[i] == m) taken |= 1u << i;
-            cand = best();
-        }
-    }
+// Merge of (maximum, sum of exp(x - maximum)) pairs; a pair with maximum
+// -inf holds nothing.
+__device__ inline void ms_merge(float& m, float& s, float mo, float so) {
+    const float mn = fmaxf(m, mo);
+    s = (m == -INFINITY ? 0.f : s * __expf(m - mn)) + (mo == -INFINITY ? 0.f : so * __expf(mo - mn));
+    m = mn;
 }
 
-// Chunk c of row r: top-K keys and (max, sum exp(x - max)) into the workspace.
-__global__ __launch_bounds__(kTopkThreads) void topk_chunks(const float* __restrict__ logits, int64_t V, int64_t ld,
-                                                           int nchunk, int K, bool vec, uint64_t* __restrict__ ws_keys,
-                                                           float2* __restrict__ ws_ms) {
-    __shared__ uint64_t red[kTopkThreads / ddt::kWave];
-    __shared__ float2 red_ms[kTopkThreads / ddt::kWave];
-    const int64_t r = blockIdx.x / nchunk;
-    const int c = (int)(blockIdx.x - r * nchunk);
-    const float* row = logits + r * ld;
-    const int64_t e0 = (int64_t)c * kTopkChunk + (int64_t)threadIdx.x * kPerThread;
-    float x[kPerThread];
-    if (vec && e0 + kPerThread <= V) {
-        typedef float F4 __attribute__((ext_vector_type(4)));
-        const F4* p = reinterpret_cast<const F4*>(row + e0);
+// The float whose order key is u (the inverse of ddt::order_key on numbers).
+__device__ inline float key_float(uint32_t u) {
+    return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
+
+// The K largest of the wavefront's keys (J per lane, 0 = empty, distinct)
+// in K rounds of a wavefront maximum; round k's key lands in lane k.
+template <int J>
+__device__ inline uint64_t wave_top(uint64_t (&key)[J], int K, int lane) {
+    uint32_t taken = 0;
+    uint64_t res = 0;
+    for (int k = 0; k < K; ++k) {
+        uint64_t b = 0;
 #pragma unroll
-        for (int q = 0; q < kPerThread / 4; ++q) {
-            const F4 v = __builtin_nontemporal_load(p + q);
+        for (int j = 0; j < J; ++j) b = ((taken >> j) & 1u) ? b : umax(b, key[j]);
+        const uint64_t mk = wave_max(b);
+        if (lane == k) res = mk;
+        if (mk != 0 && b == mk) {
+#pragma unroll
+            for (int j = 0; j < J; ++j)
+                if (key[j] == mk) taken |= 1u << j;
+        }
+    }
+    return res;
+}
+
+template <int J>
+__device__ inline uint64_t list_top(const uint64_t* list, int n, int K, int lane) {
+    uint64_t key[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) key[j] = j * 64 + lane < n ? list[j * 64 + lane] : 0;
+    return wave_top<J>(key, K, lane);
+}
+
+// Chunk c of row r: top-K keys and (max, sum exp(x - max)) into the
+// workspace.  Entry i of thread t is column c*16384 + ((i/4)*256 + t)*4 +
+// i%4 (16-byte loads, consecutive threads on consecutive 16 bytes).  kVec:
+// every column of the chunk lies in the row and the row is 16-byte aligned;
+// otherwise scalar loads, columns past the row padded with -inf and left
+// out.  Workgroup g takes chunk c0 + g % cn of row g / cn.
+template <bool kVec>
+__global__ __launch_bounds__(kTopkThreads) void topk_chunks(const float* __restrict__ logits, int64_t V, int64_t ld,
+                                                           int nchunk, int c0, int cn, int K,
+                                                           uint64_t* __restrict__ ws_keys,
+                                                           float2* __restrict__ ws_ms) {
+    constexpr int NW = kTopkThreads / ddt::kWave;
+    __shared__ uint64_t red[NW];
+    __shared__ float2 red_ms[NW];
+    __shared__ uint32_t red_thr[NW];
+    __shared__ uint64_t s_cand[kCandCap];
+    __shared__ uint64_t out[kMaxTopK];
+    __shared__ int s_n;
+    const int64_t r = blockIdx.x / cn;
+    const int c = c0 + (int)(blockIdx.x - r * cn);
+    const float* row = logits + r * ld;
+    const int64_t base = (int64_t)c * kTopkChunk;
+    const int lim = V - base < kTopkChunk ? (int)(V - base) : kTopkChunk;  // columns of the chunk in the row
+    const uint32_t idx0 = (uint32_t)base;  // (V <= 2^20)
+    uint64_t* keys_out = ws_keys + (r * nchunk + c) * K;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid / ddt::kWave;
+    if (tid == 0) s_n = 0;
+    auto cidx = [&](int i) { return ((i / 4) * kTopkThreads + tid) * 4 + (i % 4); };
+    auto valid = [&](int i) { return kVec || cidx(i) < lim; };
+    float x[kChunkPerThread];
+    if constexpr (kVec) {
+        typedef float F4 __attribute__((ext_vector_type(4)));
+        const F4* p = reinterpret_cast<const F4*>(row + base) + tid;
+#pragma unroll
+        for (int q = 0; q < kChunkPerThread / 4; ++q) {
+            const F4 v = __builtin_nontemporal_load(p + q * kTopkThreads);
             x[4 * q] = v.x, x[4 * q + 1] = v.y, x[4 * q + 2] = v.z, x[4 * q + 3] = v.w;
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < kPerThread; ++i) x[i] = e0 + i < V ? row[e0 + i] : -INFINITY;
+        for (int i = 0; i < kChunkPerThread; ++i) x[i] = valid(i) ? row[base + cidx(i)] : -INFINITY;
     }
-    uint64_t key[kPerThread];
+    // this thread's maximum (NaN ignored) and sum of exp(x - maximum)
     float m = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-        const bool ok = e0 + i < V;
-        key[i] = ok ? ddt::pack_key(__float_as_uint(x[i]), e0 + i) : 0;
-        m = ok ? fmaxf(m, x[i]) : m;
-    }
-    float s = 0.f;
+    for (int i = 0; i < kChunkPerThread; ++i) m = fmaxf(m, x[i]);  // (padding is -inf)
+    float sm = 0.f;
 #pragma unroll
-    for (int i = 0; i < kPerThread; ++i) s += e0 + i < V ? __expf(x[i] - m) : 0.f;
-    // chunk (max, sum): wavefront then workgroup
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const float mo = __shfl_xor(m, o, ddt::kWave), so = __shfl_xor(s, o, ddt::kWave);
-        const float mn = fmaxf(m, mo);
-        s = (m == -INFINITY ? 0.f : s * __expf(m - mn)) + (mo == -INFINITY ? 0.f : so * __expf(mo - mn));
-        m = mn;
-    }
-    const int wave = threadIdx.x / ddt::kWave;
-    if ((threadIdx.x & 63) == 0) red_ms[wave] = make_float2(m, s);
-    __shared__ uint64_t out[kMaxTopK];
-    select_top(key, K, out, red);  // (its barriers also publish red_ms)
-    if (threadIdx.x == 0) {
-        float M = red_ms[0].x, S = red_ms[0].y;
-        for (int w = 1; w < kTopkThreads / ddt::kWave; ++w) {
-            const float mw = red_ms[w].x, sw = red_ms[w].y;
-            const float mn = fmaxf(M, mw);
-            S = (M == -INFINITY ? 0.f : S * __expf(M - mn)) + (mw == -INFINITY ? 0.f : sw * __expf(mw - mn));
-            M = mn;
+    for (int i = 0; i < kChunkPerThread; ++i) sm += valid(i) ? __expf(x[i] - m) : 0.f;
+    const bool any = valid(0);  // entry 0 is the thread's first column
+    // The threshold: this wavefront's K-th largest thread maximum (ties
+    // taken together), when at least K of its threads hold columns.  Each
+    // such thread holds an entry whose key is at least its maximum's (a NaN
+    // entry's key is above every number), so at least K entries reach it.
+    {
+        const uint32_t u = any ? ddt::order_key(__float_as_uint(m)) : 0u;
+        bool live = any;
+        int removed = 0;
+        uint32_t tw = 0;
+        for (int k = 0; k < K && removed < K; ++k) {
+            const uint32_t mx = wave_max(live ? u : 0u);
+            if (mx == 0) break;
+            tw = mx;
+            const bool hit = live && u == mx;
+            removed += __popcll(__ballot(hit));
+            live = live && !hit;
         }
-        ws_ms[blockIdx.x] = make_float2(M, S);
-        for (int k = 0; k < K; ++k) ws_keys[(int64_t)blockIdx.x * K + k] = out[k];
+        if (lane == 0) red_thr[wave] = removed >= K ? tw : 0u;
+    }
+    // the chunk's (max, sum): wavefront, then workgroup (at the end)
+    {
+        float mw = m, sw = sm;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) ms_merge(mw, sw, __shfl_xor(mw, o, ddt::kWave), __shfl_xor(sw, o, ddt::kWave));
+        if (lane == 0) red_ms[wave] = make_float2(mw, sw);
+    }
+    __syncthreads();
+    uint32_t T = red_thr[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) T = red_thr[w] > T ? red_thr[w] : T;
+    // Every entry whose key is >= T onto the list: for numbers that is
+    // x >= key_float(T); NaN keys are above every threshold.  T = 0: every
+    // column.
+    const float tf = T == 0 ? -INFINITY : key_float(T);
+#pragma unroll
+    for (int i = 0; i < kChunkPerThread; ++i) {
+        if (valid(i) && !(x[i] < tf)) {
+            const int at = atomicAdd(&s_n, 1);
+            if (at < kCandCap) s_cand[at] = ddt::pack_key(__float_as_uint(x[i]), idx0 + cidx(i));
+        }
+    }
+    __syncthreads();
+    const int n = s_n;
+    if (n <= kCandCap) {
+        if (wave != 0) return;
+        const uint64_t res = n <= 64    ? list_top<1>(s_cand, n, K, lane)
+                             : n <= 256 ? list_top<4>(s_cand, n, K, lane)
+                                        : list_top<kCandCap / 64>(s_cand, n, K, lane);
+        if (lane < K) keys_out[lane] = res;
+    } else {
+        // many equal values: K rounds of a workgroup maximum over every
+        // entry (a thread's entries ascend in column, so its first largest
+        // key is its best)
+        uint64_t taken = 0;
+        for (int k = 0; k < K; ++k) {
+            uint32_t bk = 0;
+            int bi = -1;
+#pragma unroll
+            for (int i = 0; i < kChunkPerThread; ++i) {
+                const uint32_t u = ddt::order_key(__float_as_uint(x[i]));
+                if (valid(i) && !((taken >> i) & 1u) && u > bk) bk = u, bi = i;
+            }
+            const uint64_t b = bi < 0 ? 0 : ((uint64_t)bk << 32) | (0xffffffffu - (idx0 + (uint32_t)cidx(bi)));
+            const uint64_t mk = block_max_all(b, red);
+            if (tid == 0) out[k] = mk;
+            if (mk != 0 && b == mk) taken |= 1ull << bi;
+        }
+        __syncthreads();
+        if (tid < K) keys_out[tid] = out[tid];
+    }
+    if (tid == 0) {
+        float M = red_ms[0].x, S = red_ms[0].y;
+#pragma unroll
+        for (int w = 1; w < NW; ++w) ms_merge(M, S, red_ms[w].x, red_ms[w].y);
+        ws_ms[r * nchunk + c] = make_float2(M, S);
     }
 }
 
-// Row r: top K among its chunks' candidates, then the log-softmax values.
-__global__ __launch_bounds__(kTopkThreads) void topk_merge(const float* __restrict__ logits, int64_t ld, int nchunk,
-                                                          int K, const uint64_t* __restrict__ ws_keys,
-                                                          const float2* __restrict__ ws_ms, int32_t* __restrict__ ids,
-                                                          float* __restrict__ logp) {
-    __shared__ uint64_t red[kTopkThreads / ddt::kWave];
-    __shared__ uint64_t out[kMaxTopK];
-    __shared__ float s_lse;
+// Row r, one wavefront: top K among its chunks' candidates, then the
+// log-softmax values (the row's log-sum-exp from the chunks' pairs).
+__global__ __launch_bounds__(64) void topk_merge(const float* __restrict__ logits, int64_t ld, int nchunk, int K,
+                                                const uint64_t* __restrict__ ws_keys,
+                                                const float2* __restrict__ ws_ms, int32_t* __restrict__ ids,
+                                                float* __restrict__ logp) {
     const int64_t r = blockIdx.x;
-    const int n = nchunk * K;  // candidates of the row (at most kTopkThreads * kPerThread)
+    const int lane = threadIdx.x;
+    const int n = nchunk * K;  // at most 64 * kMergePerLane
+    float m = -INFINITY, s = 0.f;
+    for (int c = lane; c < nchunk; c += ddt::kWave) {
+        const float2 p = ws_ms[r * nchunk + c];
+        ms_merge(m, s, p.x, p.y);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ms_merge(m, s, __shfl_xor(m, o, ddt::kWave), __shfl_xor(s, o, ddt::kWave));
+    const float lse = m + __logf(s);
     const uint64_t* cand = ws_keys + r * n;
-    uint64_t key[kPerThread];
-#pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-        const int j = threadIdx.x * kPerThread + i;
-        key[i] = j < n ? cand[j] : 0;
-    }
-    if (threadIdx.x < ddt::kWave) {
-        // the row's log-sum-exp from the chunks' (max, sum) pairs
-        float m = -INFINITY, s = 0.f;
-        for (int c = threadIdx.x; c < nchunk; c += ddt::kWave) {
-            const float2 p = ws_ms[r * nchunk + c];
-            const float mn = fmaxf(m, p.x);
-            s = (m == -INFINITY ? 0.f : s * __expf(m - mn)) + (p.x == -INFINITY ? 0.f : p.y * __expf(p.x - mn));
-            m = mn;
-        }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            const float mo = __shfl_xor(m, o, ddt::kWave), so = __shfl_xor(s, o, ddt::kWave);
-            const float mn = fmaxf(m, mo);
-            s = (m == -INFINITY ? 0.f : s * __expf(m - mn)) + (mo == -INFINITY ? 0.f : so * __expf(mo - mn));
-            m = mn;
-        }
-        if (threadIdx.x == 0) s_lse = m + __logf(s);
-    }
-    select_top(key, K, out, red);
-    if (threadIdx.x < K) {
-        const uint64_t k = out[threadIdx.x];
-        const int32_t id = (int32_t)(0xffffffffu - (uint32_t)k);
-        ids[r * K + threadIdx.x] = id;
-        logp[r * K + threadIdx.x] = logits[r * ld + id] - s_lse;
+    const uint64_t res = n <= 64    ? list_top<1>(cand, n, K, lane)
+                         : n <= 256 ? list_top<4>(cand, n, K, lane)
+                                    : list_top<kMergePerLane>(cand, n, K, lane);
+    if (lane < K) {
+        const int32_t id = (int32_t)(0xffffffffu - (uint32_t)res);
+        ids[r * K + lane] = id;
+        logp[r * K + lane] = logits[r * ld + id] - lse;
     }
 }
 
@@ -343,7 +435,7 @@ __global__ __launch_bounds__(64) void best_first_wave_kernel(const int32_t* __re
     }
     for (int n = 1; n <= budget; ++n) {
         const uint64_t key = valid ? frontier_key(fs, fd, fq) : 0;
-        const uint64_t m = wave_max_u64(key);
+        const uint64_t m = wave_max(key);
         const uint64_t win = __ballot(valid && key == m);
         if (win == 0) break;  // (cannot happen: the host checked that the candidates suffice)
         const int wl = __builtin_ctzll(win);  // (uniform: readlane broadcasts into scalar registers)
@@ -414,10 +506,19 @@ extern "C" int ddt_draft_topk(const float* logits, int64_t rows, int64_t V, int6
     uint64_t* keys = static_cast<uint64_t*>(workspace);
     float2* ms = reinterpret_cast<float2*>(keys + rows * nchunk * K);
     const bool vec = ddt::aligned(logits, 16) && (ld * 4) % 16 == 0;
-    hipLaunchKernelGGL(topk_chunks, dim3((unsigned)(rows * nchunk)), dim3(kTopkThreads), 0, stream, logits, V, ld,
-                       (int)nchunk, K, vec, keys, ms);
-    DDT_CHECK_LAUNCH();
-    hipLaunchKernelGGL(topk_merge, dim3((unsigned)rows), dim3(kTopkThreads), 0, stream, logits, ld, (int)nchunk, K,
+    const int nfull = vec ? (int)(V / kTopkChunk) : 0;  // chunks taken by 16-byte loads
+    if (nfull > 0) {
+        hipLaunchKernelGGL(topk_chunks<true>, dim3((unsigned)(rows * nfull)), dim3(kTopkThreads), 0, stream, logits,
+                           V, ld, (int)nchunk, 0, nfull, K, keys, ms);
+        DDT_CHECK_LAUNCH();
+    }
+    if (nchunk > nfull) {
+        const int nrest = (int)nchunk - nfull;
+        hipLaunchKernelGGL(topk_chunks<false>, dim3((unsigned)(rows * nrest)), dim3(kTopkThreads), 0, stream,
+                           logits, V, ld, (int)nchunk, nfull, nrest, K, keys, ms);
+        DDT_CHECK_LAUNCH();
+    }
+    hipLaunchKernelGGL(topk_merge, dim3((unsigned)rows), dim3(64), 0, stream, logits, ld, (int)nchunk, K,
                        keys, ms, ids, logp);
     DDT_CHECK_LAUNCH();
     return DDT_OK;

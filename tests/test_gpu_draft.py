@@ -21,9 +21,11 @@ LOGP_TOL = 1e-4
 @pytest.mark.parametrize("rows,V,K,sigma", [
     (256, 163840, 8, 3.0),   # the verify loop's draft step: 32 requests x 8 depths
     (8, 163840, 4, 3.0),     # the K2-like head share's draft step
-    (5, 5000, 16, 1.0),      # ragged last chunk
-    (3, 4097, 1, 1.0),       # one entry past a chunk
-    (7, 100, 5, 1.0),        # one partial chunk
+    (5, 5000, 16, 1.0),      # one partial chunk
+    (3, 16385, 1, 1.0),      # one entry past a chunk
+    (4, 16389, 16, 1.0),     # a last chunk with fewer entries than K
+    (6, 40000, 8, 2.0),      # two whole chunks and a ragged one
+    (7, 100, 5, 1.0),        # one small chunk
 ])
 def test_draft_topk(orc, rows, V, K, sigma):
     rng = np.random.default_rng(rows + V + K)
@@ -31,6 +33,36 @@ def test_draft_topk(orc, rows, V, K, sigma):
     x[0, [V // 3, V // 2, V - 1]] = 40.0                      # ties at the top: lower index first
     if rows > 2:
         x[2, :] = 0.25                                         # all equal: indices 0..K-1
+    ids, lp = ddt.draft_topk(to_dev(x), K)
+    ref_ids, ref_lp = orc.draft_topk(x, K)
+    assert (to_host(ids) == ref_ids).all()
+    assert np.abs(to_host(lp).astype(np.float64) - ref_lp).max() <= LOGP_TOL
+
+
+def _bf16_round(x):
+    b = x.view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) & 0xFFFF0000
+    return b.astype(np.uint32).view(np.float32)
+
+
+def test_draft_topk_tied_values(orc):
+    """Equal values in every amount a chunk's candidate list meets: fewer
+    than 64, up to 256, up to 1024 and past 1024 entries tied at the top of
+    a chunk (the last falls back to the exact selection over every entry),
+    ties across chunks and in the ragged chunk, and logits rounded to bf16
+    (many equal values near the top).  Ids bit-exact: equal values by
+    ascending index."""
+    rng = np.random.default_rng(77)
+    rows, V, K = 9, 40000, 16
+    x = rng.standard_normal((rows, V)).astype(np.float32)
+    for r, count in enumerate([40, 100, 600, 3000]):
+        cols = rng.choice(16384, count, replace=False) + 16384   # inside chunk 1
+        x[r, cols] = 7.5
+    x[4, rng.choice(V, 50, replace=False)] = 6.0                 # ties spread over every chunk
+    x[5, 32768 + rng.choice(V - 32768, 20, replace=False)] = 9.0  # ties in the ragged chunk
+    x[6] = _bf16_round(x[6] * 3.0)
+    x[7] = np.round(x[7] * 2.0) / 2.0                            # few distinct values
+    x[8, 16384:32768] = -3.0                                     # a constant chunk beside random ones
     ids, lp = ddt.draft_topk(to_dev(x), K)
     ref_ids, ref_lp = orc.draft_topk(x, K)
     assert (to_host(ids) == ref_ids).all()
