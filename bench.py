@@ -70,6 +70,8 @@ def parse():
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache attention timing (configs 2 and 3)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget for the oracle timing")
+    ap.add_argument("--hbm-stages", action="store_true",
+                    help="time only the HBM scans (target argmax, draft top-k) and print their record")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run 5 attention launches and a 256 MiB calibration copy, then exit")
     return ap.parse_args()
@@ -180,6 +182,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.hbm_stages:
+        print(json.dumps({"hbm_stages": time_hbm_stages(dev)}), flush=True)
+        return
     if args.config == 5:
         if args.traffic_probe:
             return loop_traffic_probe(dev)
