@@ -69,6 +69,19 @@ def test_draft_topk_tied_values(orc):
     assert np.abs(to_host(lp).astype(np.float64) - ref_lp).max() <= LOGP_TOL
 
 
+def test_draft_topk_largest_vocabulary(orc):
+    """V = 2^20 (the largest vocabulary) and K = 16: 64 chunks per row, so
+    the row merge picks the top 16 of 1024 candidates (its widest path)."""
+    rng = np.random.default_rng(31)
+    rows, V, K = 3, 1 << 20, 16
+    x = (rng.standard_normal((rows, V)) * 2.0).astype(np.float32)
+    x[1, rng.choice(V, 40, replace=False)] = 12.0     # ties spread over many chunks
+    ids, lp = ddt.draft_topk(to_dev(x), K)
+    ref_ids, ref_lp = orc.draft_topk(x, K)
+    assert (to_host(ids) == ref_ids).all()
+    assert np.abs(to_host(lp).astype(np.float64) - ref_lp).max() <= LOGP_TOL
+
+
 def test_draft_topk_row_view(orc):
     """A column range of a wider array (row stride != V, unaligned start)."""
     rng = np.random.default_rng(9)
