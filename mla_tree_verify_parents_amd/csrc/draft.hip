@@ -398,24 +398,51 @@ __global__ __launch_bounds__(64) void best_first_kernel(const int32_t* __restric
 // Trees of at most 64 nodes: the frontier never holds more than 64
 // candidates (a pop adds at most one net), so lane l keeps candidate l in
 // registers and lane n keeps node n.  A pop is a wavefront maximum over the
-// same packed keys, the winner's fields broadcast from its lane; the first
-// child and then the next sibling take the lowest free lanes.  Same
-// arithmetic and order as best_first_kernel, so the trees are identical.
+// same packed keys, taken in two 32-bit steps (the score word; then, only
+// when scores tie, the depth / insertion word of the tied lanes), the
+// winner's fields broadcast from its lane; the first child and then the
+// next sibling take the lowest free lanes.  With at most 64 candidates per
+// request (kRegTables) lane i also holds candidate i's log-probability and
+// token, read by v_readlane instead of LDS.  Same arithmetic and order as
+// best_first_kernel, so the trees are identical.
+template <bool kRegTables>
 __global__ __launch_bounds__(64) void best_first_wave_kernel(const int32_t* __restrict__ ids,
                                                             const float* __restrict__ lp, int D, int K, int budget,
                                                             const int32_t* __restrict__ roots,
                                                             int32_t* __restrict__ parents,
                                                             int32_t* __restrict__ tokens,
                                                             int32_t* __restrict__ depth) {
-    __shared__ float s_lp[kTreeMaxDK];
-    __shared__ int32_t s_id[kTreeMaxDK];
+    __shared__ float s_lp[kRegTables ? 1 : kTreeMaxDK];
+    __shared__ int32_t s_id[kRegTables ? 1 : kTreeMaxDK];
     const int b = blockIdx.x, lane = threadIdx.x;
     const int DK = D * K;
-    for (int i = lane; i < DK; i += 64) {
-        s_lp[i] = lp[(int64_t)b * DK + i];
-        s_id[i] = ids[(int64_t)b * DK + i];
+    float r_lp = 0.f;
+    int r_id = 0;
+    if constexpr (kRegTables) {
+        if (lane < DK) {
+            r_lp = lp[(int64_t)b * DK + lane];
+            r_id = ids[(int64_t)b * DK + lane];
+        }
+    } else {
+        for (int i = lane; i < DK; i += 64) {
+            s_lp[i] = lp[(int64_t)b * DK + i];
+            s_id[i] = ids[(int64_t)b * DK + i];
+        }
+        __syncthreads();
     }
-    __syncthreads();
+    // candidate i's log-probability and token (i wave-uniform)
+    auto cand_lp = [&](int i) {
+        if constexpr (kRegTables)
+            return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, r_lp), i));
+        else
+            return s_lp[i];
+    };
+    auto cand_id = [&](int i) {
+        if constexpr (kRegTables)
+            return __builtin_amdgcn_readlane(r_id, i);
+        else
+            return s_id[i];
+    };
     // this lane's frontier candidate
     bool valid = false;
     float fs = 0.f;
@@ -426,36 +453,46 @@ __global__ __launch_bounds__(64) void best_first_wave_kernel(const int32_t* __re
     if (lane == 0) nt = roots[b];
     int seq = 0;
     if (budget > 0) {
+        const float l0 = cand_lp(0);
         if (lane == 0) {
             valid = true;
-            fs = 0.f + s_lp[0];
+            fs = 0.f + l0;
             fd = 1;
         }
         seq = 1;
     }
     for (int n = 1; n <= budget; ++n) {
-        const uint64_t key = valid ? frontier_key(fs, fd, fq) : 0;
-        const uint64_t m = wave_max(key);
-        const uint64_t win = __ballot(valid && key == m);
+        // the frontier key, (score word) << 32 | (depth / insertion word)
+        const uint32_t hi = valid ? ddt::order_key(__float_as_uint(fs)) : 0u;
+        const uint32_t lo = ((uint32_t)(255 - fd) << 24) | (uint32_t)(0xffffff - fq);
+        const uint32_t mhi = wave_max(hi);
+        uint64_t win = __ballot(valid && hi == mhi);
         if (win == 0) break;  // (cannot happen: the host checked that the candidates suffice)
+        if (__popcll(win) > 1) {  // tied scores: the depth / insertion word decides
+            const bool tied = valid && hi == mhi;
+            const uint32_t mlo = wave_max(tied ? lo : 0u);
+            win = __ballot(tied && lo == mlo);
+        }
         const int wl = __builtin_ctzll(win);  // (uniform: readlane broadcasts into scalar registers)
         const float sc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, fs), wl));
         const int d = __builtin_amdgcn_readlane(fd, wl), r = __builtin_amdgcn_readlane(fr, wl);
         const int par = __builtin_amdgcn_readlane(fp, wl);
         if (lane == wl) valid = false;
+        const int tok = cand_id((d - 1) * K + r);
         if (lane == n) {
             np = par;
-            nt = s_id[(d - 1) * K + r];
+            nt = tok;
             nd = d;
             ns = sc;
         }
         const float pscore =  // node par (< n) is already recorded
             __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ns), par));
         if (d < D) {  // first child
+            const float lc = cand_lp(d * K);
             const int fl = __builtin_ctzll(~__ballot(valid));
             if (lane == fl) {
                 valid = true;
-                fs = sc + s_lp[d * K];
+                fs = sc + lc;
                 fd = d + 1;
                 fr = 0;
                 fp = n;
@@ -463,10 +500,11 @@ __global__ __launch_bounds__(64) void best_first_wave_kernel(const int32_t* __re
             }
         }
         if (r + 1 < K) {  // next sibling
+            const float ls = cand_lp((d - 1) * K + r + 1);
             const int fl = __builtin_ctzll(~__ballot(valid));
             if (lane == fl) {
                 valid = true;
-                fs = pscore + s_lp[(d - 1) * K + r + 1];
+                fs = pscore + ls;
                 fd = d;
                 fr = r + 1;
                 fp = par;
@@ -539,8 +577,11 @@ extern "C" int ddt_best_first_tree(const int32_t* ids, const float* logp, int B,
     if (avail < budget) return DDT_EINVAL;
     if (B == 0) return DDT_OK;
     if (!ids || !logp || !root_tokens || !parents || !tokens || !depth) return DDT_EINVAL;
-    if (budget + 1 <= 64)  // the frontier fits one candidate per lane
-        hipLaunchKernelGGL(best_first_wave_kernel, dim3(B), dim3(64), 0, stream, ids, logp, D, K, budget,
+    if (budget + 1 <= 64 && D * K <= 64)  // frontier and candidate tables one per lane
+        hipLaunchKernelGGL(best_first_wave_kernel<true>, dim3(B), dim3(64), 0, stream, ids, logp, D, K, budget,
+                           root_tokens, parents, tokens, depth);
+    else if (budget + 1 <= 64)  // the frontier fits one candidate per lane
+        hipLaunchKernelGGL(best_first_wave_kernel<false>, dim3(B), dim3(64), 0, stream, ids, logp, D, K, budget,
                            root_tokens, parents, tokens, depth);
     else
         hipLaunchKernelGGL(best_first_kernel, dim3(B), dim3(64), 0, stream, ids, logp, D, K, budget, root_tokens,
