@@ -97,6 +97,15 @@ __global__ __launch_bounds__(kThreads) void proj_kernel(const uint16_t* __restri
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int t0 = tt * kRows;
 
+    // the B fragments of the first KP k-steps load before the input tile, so
+    // their (L2) latency overlaps the tile's
+    const int nb = cb * (kCols / 32) + wave;  // this wavefront's 32-column tile
+    const bool has_cols = nb * 32 < n_out;
+    const bf16x8* wf = wp + ((int64_t)(h * (n_out / 32) + (has_cols ? nb : 0)) * KS) * 64 + lane;
+    constexpr int KP = KS < 8 ? KS : 8;
+    bf16x8 bpre[KP];
+#pragma unroll
+    for (int ks = 0; ks < KP; ++ks) bpre[ks] = wf[ks * 64];
     // input tile: rows t0..t0+63 of head h, zero past M
     for (int c = tid; c < kRows * XCH; c += kThreads) {
         const int row = c / XCH, ch = c % XCH;
@@ -107,15 +116,13 @@ __global__ __launch_bounds__(kThreads) void proj_kernel(const uint16_t* __restri
     }
     __syncthreads();
 
-    const int nb = cb * (kCols / 32) + wave;  // this wavefront's 32-column tile
     floatx16 acc0 = {}, acc1 = {};
-    if (nb * 32 < n_out) {
-        const bf16x8* wf = wp + ((int64_t)(h * (n_out / 32) + nb) * KS) * 64 + lane;
+    if (has_cols) {
         const unsigned char* a0p = smem + (lane & 31) * XROW + (lane >> 5) * 16;
         const unsigned char* a1p = a0p + 32 * XROW;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 b = wf[ks * 64];
+            const bf16x8 b = ks < KP ? bpre[ks < KP ? ks : 0] : wf[ks * 64];
             const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(a0p + ks * 32);
             const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(a1p + ks * 32);
             acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b, acc0, 0, 0, 0);
