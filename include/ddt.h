@@ -125,6 +125,20 @@ int ddt_build_mask(const int32_t* parents, int B, int N, uint64_t* mask, int32_t
  * paged form is built for the bf16 (512, 64) instance (DDT_EUNSUPPORTED
  * otherwise), and its key splits are at most 767 pages long (a larger
  * kv_chunk is capped).
+ *
+ * Device-resident lengths (prefix_len_dev non-NULL).  [Keystone], section
+ * "The Reasoning That Preceded the Header": the committed length advances
+ * on the device every step (by accept_len + 1 <= N).  With prefix_len_dev
+ * set, prefix_len_host[b] is only an upper bound: the launch is planned,
+ * validated and sized (workspace, block-table width) for the bounds, and
+ * the kernels read request b's committed length P_b = min(prefix_len_dev[b],
+ * prefix_len_host[b]) (negative values as 0) from device memory when they
+ * run, so a caller can enqueue or capture several steps without reading the
+ * lengths back.  Results are those for the lengths P_b; key splits past
+ * P_b + N contribute nothing; no cache row at or past P_b + N (nor any page
+ * past it) is read.  prefix_len_dev must stay unchanged while the call's
+ * kernels run (ddt_verify_step updates acc->new_prefix_len in its last
+ * launch, after the attention).
  */
 typedef struct {
     int B, H, N;
@@ -137,6 +151,7 @@ typedef struct {
     const int32_t* block_table; /* [B][bt_ld] page numbers, or NULL (contiguous) */
     int64_t bt_ld;
     int page_size;
+    const int32_t* prefix_len_dev; /* [B] device committed lengths, or NULL */
 } ddt_attn_desc;
 
 /* Workspace bytes ddt_verify_attn needs for this shape and these prefix
@@ -350,7 +365,9 @@ int ddt_accept_compact(const int32_t* target_ids, const int32_t* draft_ids, cons
  * acceptance + compaction workgroup per request beside it (the compaction
  * writes the cache only after the attention has read it).
  * am->rows must be B*N (one target row per tree node, request-major).
- * acc->prefix_len (device) must hold the same lengths as prefix_len_host.
+ * acc->prefix_len (device) must hold the same lengths as prefix_len_host,
+ * or lengths at most those when d->prefix_len_dev is set (normally
+ * d->prefix_len_dev == acc->prefix_len).
  * mask may be NULL when N <= 128: the attention then derives each row's
  * ancestor bits from acc->parents itself (pointer doubling across a
  * wavefront), so the step needs no ddt_build_mask launch; a request whose

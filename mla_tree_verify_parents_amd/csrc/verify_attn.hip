@@ -439,6 +439,7 @@ struct VerifyParams {
     const void* ckv;
     const void* kpe;
     ddt::SlotMap map;           // cache slot -> pool row (contiguous from kv_base, or paged)
+    const int32_t* P_dev;       // committed lengths on the device (at most P[]), or null
     const uint64_t* mask;       // ancestor bits from ddt_build_mask, or null:
     const int32_t* parents;     // then each row's bits come from the parents (N <= 128)
     void* out;
@@ -754,15 +755,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     int b = 0, split = 0, rt = 0;
     if (!work_item(p, (int)blockIdx.x, b, split, rt)) return;  // (uniform: the whole workgroup)
     const int wl = p.wg_begin[b] + split * p.row_tiles + rt;   // partial-output slot
-    const int P = p.P[b];
+    // committed length: the planned one, or the device's (at most the
+    // planned bound, which the work items cover)
+    const int P = p.P_dev == nullptr ? p.P[b]
+                                     : __builtin_amdgcn_readfirstlane(max(0, min(p.P_dev[b], p.P[b])));
+    const int kT = P + p.N;  // the request's keys: rows [0, kT) are read, no further
     const int kbeg = split * p.chunk;
     // kClip (large trees, e.g. prefill chunks): nodes are numbered
     // parents-first, so a row of node i sees no tree key past P + i; keys
     // past P + imax + 1 (imax: the last node among this work item's rows)
     // are invisible to every row here and are not read.  At least one key
     // stays, fully masked, so a split past imax is an ordinary work item
-    // with an empty partial.
-    const int kend0 = min(kbeg + p.chunk, P + p.N);
+    // with an empty partial; so is a split past a device length below the
+    // planned one (its key, at or past kT, is neither read nor visible).
+    const int kend0 = max(kbeg + 1, min(kbeg + p.chunk, kT));
     const int kend =
         kClip ? __builtin_amdgcn_readfirstlane(
                     max(kbeg + 1, min(kend0, P + (min(p.rows, (rt + 1) * ROWS_WG) - 1) / p.H + 1)))
@@ -856,7 +862,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 // bit (jn mod 64) of the word holding jn, tested with 32-bit operations
                 const uint64_t word = (jn >> 6) == wlo ? mw0 : mw1;
                 const uint32_t half = (jn & 32) ? (uint32_t)(word >> 32) : (uint32_t)word;
-                const uint32_t vis = (uint32_t)(t < kend) & ((uint32_t)(t < P) | ((half >> (jn & 31)) & 1u));
+                const uint32_t vis = (uint32_t)(t < kend) & (uint32_t)(t < kT) &
+                                     ((uint32_t)(t < P) | ((half >> (jn & 31)) & 1u));
                 x[v] = vis ? x[v] : -INFINITY;
             }
         };
@@ -1017,7 +1024,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                               : (j < KT * LB ? (uint32_t)((j / LB) * ldB + (j % LB) * 128) : 0xFFFFFFF0u);
         pin_reg(toff[k]);
     }
-    // per-tile descriptors of the two regions (rows [t0, min(t0 + KT, kend)))
+    // per-tile descriptors of the two regions (rows [t0, min(t0 + KT, kend, kT)))
     struct TileDma {
         u32x4 ra, rb;    // raw buffer descriptors of the tile's rows in c_kv / k_pe
         uint32_t lds;    // LDS byte address of the tile's ring slot
@@ -1025,7 +1032,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     auto tile_dma = [&](int tile) {
         const bool real = tile < ntiles;
         const int t0 = kbeg + (real ? tile : 0) * KT;
-        int nrows = kend - t0;
+        int nrows = min(kend, kT) - t0;
+        nrows = nrows < 0 ? 0 : nrows;
         nrows = real ? (nrows > KT ? KT : nrows) : 0;
         TileDma d;
         if constexpr (kPaged) {  // pool row of slot t0: its page's first row + the offset in the page
@@ -1632,6 +1640,7 @@ int setup_attn(const ddt_attn_desc* d, const void* q_lat, const void* q_pe, cons
     vp->kpe = kpe;
     vp->map = ddt::SlotMap{kv_base, d->block_table, d->block_table ? d->bt_ld : 0,
                            d->block_table ? __builtin_ctz((unsigned)d->page_size) : 0};
+    vp->P_dev = d->prefix_len_dev;
     vp->mask = mask;
     vp->parents = mask ? nullptr : parents;
     vp->out = out;

@@ -35,7 +35,8 @@ class AttnDesc(ctypes.Structure):
                 ("scale", ctypes.c_float), ("kv_chunk", ctypes.c_int),
                 ("ld_ql", ctypes.c_int64), ("ld_qp", ctypes.c_int64),
                 ("ld_ckv", ctypes.c_int64), ("ld_kpe", ctypes.c_int64),
-                ("block_table", ctypes.c_void_p), ("bt_ld", ctypes.c_int64), ("page_size", ctypes.c_int)]
+                ("block_table", ctypes.c_void_p), ("bt_ld", ctypes.c_int64), ("page_size", ctypes.c_int),
+                ("prefix_len_dev", ctypes.c_void_p)]
 
 
 class ArgmaxTask(ctypes.Structure):
@@ -165,10 +166,12 @@ def build_mask(parents, mask=None, depth=None, tree_err=None, stream=None):
     return mask, depth, tree_err
 
 
-def attn_desc(q_lat, q_pe, ckv, kpe, *, B, H, N, scale, kv_chunk=0, pages=None):
+def attn_desc(q_lat, q_pe, ckv, kpe, *, B, H, N, scale, kv_chunk=0, pages=None, prefix_len_dev=None):
     """pages: None (contiguous cache from kv_base) or (block_table [B, bt_ld]
     int32 device, page_size): slot t of request b is pool row
-    block_table[b, t // page_size] * page_size + t % page_size."""
+    block_table[b, t // page_size] * page_size + t % page_size.
+    prefix_len_dev: None, or [B] int32 device committed lengths read by the
+    kernels when they run; the host lengths are then upper bounds."""
     d = AttnDesc(B, H, N, q_lat.shape[1], q_pe.shape[1], _dtype_code(q_lat), float(scale), int(kv_chunk),
                  _rows(q_lat, "q_lat"), _rows(q_pe, "q_pe"), _rows(ckv, "ckv"), _rows(kpe, "kpe"))
     if pages is not None:
@@ -177,6 +180,11 @@ def attn_desc(q_lat, q_pe, ckv, kpe, *, B, H, N, scale, kv_chunk=0, pages=None):
         if table.dim() != 2 or table.shape[0] != B:
             raise ValueError("block_table must be [B, bt_ld]")
         d.block_table, d.bt_ld, d.page_size = table.data_ptr(), table.shape[1], int(page_size)
+    if prefix_len_dev is not None:
+        _contig(prefix_len_dev, torch.int32, "prefix_len_dev")
+        if tuple(prefix_len_dev.shape) != (B,):
+            raise ValueError("prefix_len_dev must be [B]")
+        d.prefix_len_dev = prefix_len_dev.data_ptr()
     return d
 
 
@@ -189,7 +197,7 @@ def verify_workspace_bytes(desc: AttnDesc, prefix_len_host) -> int:
 
 
 def _attn_args(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, H, scale, out, lse, workspace, kv_chunk,
-               BN=None, pages=None, alloc_workspace=True):
+               BN=None, pages=None, alloc_workspace=True, prefix_len_dev=None):
     for t, n in ((q_lat, "q_lat"), (q_pe, "q_pe"), (ckv, "ckv"), (kpe, "kpe")):
         _dev(t, q_lat.dtype, n)
     if pages is None or kv_base is not None:
@@ -205,7 +213,8 @@ def _attn_args(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, H, scale, 
     pl = np.ascontiguousarray(prefix_len_host, dtype=np.int32)
     if pl.shape != (B,):
         raise ValueError("prefix_len_host must have B entries")
-    desc = attn_desc(q_lat, q_pe, ckv, kpe, B=B, H=H, N=N, scale=scale, kv_chunk=kv_chunk, pages=pages)
+    desc = attn_desc(q_lat, q_pe, ckv, kpe, B=B, H=H, N=N, scale=scale, kv_chunk=kv_chunk, pages=pages,
+                     prefix_len_dev=prefix_len_dev)
     if out is None:
         out = torch.empty((rows, q_lat.shape[1]), dtype=q_lat.dtype, device=q_lat.device)
     if lse is None:
@@ -221,14 +230,15 @@ def _attn_args(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, H, scale, 
 
 
 def verify_attn(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, *, H, scale, out=None, lse=None,
-                workspace=None, kv_chunk=0, pages=None, stream=None):
+                workspace=None, kv_chunk=0, pages=None, prefix_len_dev=None, stream=None):
     """Tree-verify attention.  q_lat [B*N*H, d_lat], q_pe [B*N*H, d_rope] (2-D views),
     ckv [pool, d_lat], kpe [pool, d_rope] (2-D views of the cache pool), kv_base [B]
     int64 (device; may be None with pages), prefix_len_host [B] (host), mask [B, N, W]
-    from build_mask; pages as for attn_desc.
+    from build_mask; pages and prefix_len_dev as for attn_desc.
     Returns (out [B*N*H, d_lat], lse [B*N*H] fp32)."""
     desc, pl, out, lse, workspace, ws_n = _attn_args(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, H,
-                                                     scale, out, lse, workspace, kv_chunk, pages=pages)
+                                                     scale, out, lse, workspace, kv_chunk, pages=pages,
+                                                     prefix_len_dev=prefix_len_dev)
     _check(lib().ddt_verify_attn(ctypes.byref(desc), _p(q_lat), _p(q_pe), _p(ckv), _p(kpe), _p(kv_base),
                                  pl.ctypes.data, _p(mask), _p(out), _p(lse), _p(workspace), ws_n,
                                  _stream(stream)), "ddt_verify_attn")
@@ -236,7 +246,7 @@ def verify_attn(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, *, H, sca
 
 
 def verify_attn_noalloc(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, *, H, scale, out, lse, kv_chunk=0,
-                        pages=None, stream=None):
+                        pages=None, prefix_len_dev=None, stream=None):
     """verify_attn without a workspace and without allocating: the library
     keeps the split partials in its own per-device scratch
     (noalloc_scratch_bytes()); out and lse must be given.  Calls on one
@@ -244,7 +254,8 @@ def verify_attn_noalloc(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, *
     if out is None or lse is None:
         raise ValueError("verify_attn_noalloc allocates nothing: pass out and lse")
     desc, pl, out, lse, _, _ = _attn_args(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, H, scale, out, lse,
-                                          None, kv_chunk, pages=pages, alloc_workspace=False)
+                                          None, kv_chunk, pages=pages, alloc_workspace=False,
+                                          prefix_len_dev=prefix_len_dev)
     _check(lib().ddt_verify_attn_noalloc(ctypes.byref(desc), _p(q_lat), _p(q_pe), _p(ckv), _p(kpe), _p(kv_base),
                                          pl.ctypes.data, _p(mask), _p(out), _p(lse), _stream(stream)),
            "ddt_verify_attn_noalloc")
@@ -271,10 +282,11 @@ def _argmax_task(logits, idx, argmax_workspace):
 
 def verify_attn_argmax(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, logits, *, H, scale, out=None,
                        lse=None, workspace=None, idx=None, argmax_workspace=None, kv_chunk=0, pages=None,
-                       stream=None):
+                       prefix_len_dev=None, stream=None):
     """verify_attn and argmax(logits) in one launch -> (out, lse, idx)."""
     desc, pl, out, lse, workspace, ws_n = _attn_args(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, H,
-                                                     scale, out, lse, workspace, kv_chunk, pages=pages)
+                                                     scale, out, lse, workspace, kv_chunk, pages=pages,
+                                                     prefix_len_dev=prefix_len_dev)
     task, idx = _argmax_task(logits, idx, argmax_workspace)
     _check(lib().ddt_verify_attn_argmax(ctypes.byref(desc), _p(q_lat), _p(q_pe), _p(ckv), _p(kpe), _p(kv_base),
                                         pl.ctypes.data, _p(mask), _p(out), _p(lse), _p(workspace), ws_n,
@@ -298,7 +310,8 @@ def _accept_outputs(parents, accept_len, path, tokens):
 
 def verify_step(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, logits, draft_ids, parents, prefix_len, *,
                 H, scale, new_prefix_len=None, out=None, lse=None, workspace=None, idx=None, argmax_workspace=None,
-                accept_len=None, path=None, tokens=None, src_slot=None, kv_chunk=0, pages=None, stream=None):
+                accept_len=None, path=None, tokens=None, src_slot=None, kv_chunk=0, pages=None,
+                device_lengths=False, stream=None):
     """Attention + argmax, then acceptance + compaction, in two launches.
 
     mask: from build_mask, or None for trees of at most 128 nodes (the
@@ -308,10 +321,13 @@ def verify_step(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, logits, d
     new_prefix_len [B] int32 device receives the advanced lengths (default:
     prefix_len itself, updated in place).  The cache views ckv / kpe are
     compacted in place (through the block table with pages).
+    device_lengths: the attention reads the committed lengths from
+    prefix_len on the device, and prefix_len_host holds upper bounds of them
+    (so steps can be enqueued or captured without reading lengths back).
     -> (out, lse, idx, accept_len, path, tokens, new_prefix_len)."""
     desc, pl, out, lse, workspace, ws_n = _attn_args(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, H,
                                                      scale, out, lse, workspace, kv_chunk, BN=tuple(parents.shape),
-                                                     pages=pages)
+                                                     pages=pages, prefix_len_dev=prefix_len if device_lengths else None)
     task, idx = _argmax_task(logits, idx, argmax_workspace)
     for t, n in ((draft_ids, "draft_ids"), (parents, "parents"), (prefix_len, "prefix_len")):
         _contig(t, torch.int32, n)
