@@ -774,6 +774,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                     max(kbeg + 1, min(kend0, P + (min(p.rows, (rt + 1) * ROWS_WG) - 1) / p.H + 1)))
               : kend0;
     const int ntiles = (kend - kbeg + KT - 1) / KT;
+    // rows the tiles read: [kbeg, kread), kread <= kT (an empty split reads none)
+    const int kread = max(kbeg, min(kend, kT));
     // paged cache: the split's page numbers go to LDS once, so the tile loop
     // reads them in order with its other LDS traffic (a scalar load per tile
     // would make every LDS wait in the loop wait for it too)
@@ -1024,7 +1026,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                               : (j < KT * LB ? (uint32_t)((j / LB) * ldB + (j % LB) * 128) : 0xFFFFFFF0u);
         pin_reg(toff[k]);
     }
-    // per-tile descriptors of the two regions (rows [t0, min(t0 + KT, kend, kT)))
+    // per-tile descriptors of the two regions (rows [t0, min(t0 + KT, kread)))
     struct TileDma {
         u32x4 ra, rb;    // raw buffer descriptors of the tile's rows in c_kv / k_pe
         uint32_t lds;    // LDS byte address of the tile's ring slot
@@ -1032,8 +1034,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     auto tile_dma = [&](int tile) {
         const bool real = tile < ntiles;
         const int t0 = kbeg + (real ? tile : 0) * KT;
-        int nrows = min(kend, kT) - t0;
-        nrows = nrows < 0 ? 0 : nrows;
+        int nrows = kread - t0;
         nrows = real ? (nrows > KT ? KT : nrows) : 0;
         TileDma d;
         if constexpr (kPaged) {  // pool row of slot t0: its page's first row + the offset in the page
