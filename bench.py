@@ -808,11 +808,12 @@ def time_projections(tokens, H, dev, reps=200, d_nope=128, d_lat=512, d_rope=64,
     return res
 
 
-def time_paged(w, dev, q_lat, q_pe, mask, ms_contiguous, page_size=64, reps=100):
+def time_paged(w, dev, q_lat, q_pe, mask, ms_contiguous, page_size=64):
     """The same attention launch with the latent cache in pages of
     `page_size` rows of one shared pool, scattered by a random permutation
     (block table; one row lookup per 32-key tile), against the contiguous
-    launch's time."""
+    launch's time (both the median of WINDOWS windows of at least WINDOW_MS
+    of back-to-back launches)."""
     import torch
 
     from mla_tree_verify_parents_amd import ddt
@@ -839,7 +840,6 @@ def time_paged(w, dev, q_lat, q_pe, mask, ms_contiguous, page_size=64, reps=100)
     out = torch.empty((w.rows, dl), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((w.rows,), dtype=torch.float32, device=dev)
     pages = (td, page_size)
-    reps = max(3, min(reps, int(WINDOW_MS / max(ms_contiguous, 1e-3))))
     d = ddt.attn_desc(q_lat, q_pe, phys[:, :dl], phys[:, dl:], B=w.B, H=w.H, N=w.N, scale=w.scale, pages=pages)
     ws = torch.empty((max(1, ddt.verify_workspace_bytes(d, w.prefix_len)),), dtype=torch.uint8, device=dev)
 
@@ -849,27 +849,20 @@ def time_paged(w, dev, q_lat, q_pe, mask, ms_contiguous, page_size=64, reps=100)
 
     f()
     torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for _ in range(reps):
-            f()
-    graph.replay()
-    torch.cuda.synchronize()
+    graph = graph_of(f, 1)
     stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    graph.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
-    return {"page_size": page_size, "pages": total, "verify_attn_ms": round(ms, 5),
-            "contiguous_ms": round(ms_contiguous, 5), "ratio": round(ms / ms_contiguous, 4)}
+    wins, per_window = time_windows(graph.replay, 1, ms_contiguous, stream)
+    ms = float(np.median(wins))
+    return {"page_size": page_size, "pages": total, "verify_attn_ms": round(ms, 5), "ms_spread": spread(wins),
+            "launches_per_window": per_window, "contiguous_ms": round(ms_contiguous, 5),
+            "ratio": round(ms / ms_contiguous, 4)}
 
 
-def time_prefill(dev, T=8192, P0=0, H=8, chunk=1024, reps=5):
+def time_prefill(dev, T=8192, P0=0, H=8, chunk=1024):
     """Causal prefill of a T-token prompt through the verify attention
     (chain-tree masks, chunks of `chunk` tokens, one verify call each; the
-    chunk loop captured in one graph).  Visible pairs: H * sum_t (P0+t+1)."""
+    chunk loop captured in one graph, timed in WINDOWS windows of at least
+    WINDOW_MS of replays, median window).  Visible pairs: H * sum_t (P0+t+1)."""
     import torch
 
     from mla_tree_verify_parents_amd import synth
@@ -894,22 +887,17 @@ def time_prefill(dev, T=8192, P0=0, H=8, chunk=1024, reps=5):
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         run()
-    graph.replay()
-    torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(reps):
-        graph.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
+    est = estimate_ms(graph.replay, 1, stream)
+    wins, per_window = time_windows(graph.replay, 1, est, stream)
+    ms = float(np.median(wins))
     pairs = H * (T * P0 + T * (T + 1) // 2)
     tflops = pairs * FLOP_PER_PAIR / (ms * 1e-3) / 1e12
     return {"tokens": T, "prefix": P0, "heads": H, "chunk": chunk, "chunks": len(pf.chunks(T, P0)),
             "calls": len(pf.calls(T, P0)),
-            "ms": round(ms, 4), "visible_pairs": pairs, "TFLOPs": round(tflops, 1),
-            "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "tokens_per_s": round(T / (ms * 1e-3), 1)}
+            "ms": round(ms, 4), "ms_spread": spread(wins), "prompts_per_window": per_window,
+            "visible_pairs": pairs, "TFLOPs": round(tflops, 1), "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "tokens_per_s": round(T / (ms * 1e-3), 1)}
 
 
 def to_host_bits(t):

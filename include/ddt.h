@@ -107,7 +107,7 @@ int ddt_build_mask(const int32_t* parents, int B, int N, uint64_t* mask, int32_t
  *
  * Built instances (d_lat, d_rope, dtype): (512, 64, BF16), (64, 16, F32).
  * Alignment: q_lat, q_pe, ckv, kpe 16-byte aligned; every row stride times
- * the element size a multiple of 16 bytes.
+ * the element size a multiple of 16 bytes, and below 2 GiB for ckv and kpe.
  *
  * Paged cache (block_table non-NULL).  [Keystone], section "Assumptions
  * Embedded in the Design": one-token pages leave the cache fragmented,
@@ -116,15 +116,16 @@ int ddt_build_mask(const int32_t* parents, int B, int N, uint64_t* mask, int32_t
  * request b is then pool row
  *   block_table[b*bt_ld + t / page_size] * page_size + t % page_size
  * (the pool row stride stays ld_ckv / ld_kpe) and kv_base is not read (it
- * may be NULL).  page_size: a power of two in [32, 65536]; bt_ld >=
- * ceil((P_b + N) / page_size) for every request (DDT_EINVAL otherwise).
+ * may be NULL).  page_size: a power of two in [32, 65536], with a page's
+ * bytes (page_size times the row stride of c_kv, and of k_pe) below 4 GiB;
+ * bt_ld >= ceil((P_b + N) / page_size) for every request (DDT_EINVAL
+ * otherwise).
  * The table entries (device int32, caller-owned) must name pages inside
  * the pool: they are not checked.  Zero-initialised fields (NULL table)
  * give the contiguous layout.  ddt_verify_attn, ddt_verify_attn_argmax and
  * ddt_verify_step (attention, acceptance and compaction) take either; the
  * paged form is built for the bf16 (512, 64) instance (DDT_EUNSUPPORTED
- * otherwise), and its key splits are at most 767 pages long (a larger
- * kv_chunk is capped).
+ * otherwise) and has the contiguous form's work plan (any split length).
  *
  * Device-resident lengths (prefix_len_dev non-NULL).  [Keystone], section
  * "The Reasoning That Preceded the Header": the committed length advances

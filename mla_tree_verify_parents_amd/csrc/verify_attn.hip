@@ -279,11 +279,10 @@ __device__ inline void dma16(u32x4 rsrc, uint32_t lds, uint32_t voff) {
         : "m0");
 }
 
-// Touch 4 bytes per lane at rsrc + voff, delivered into LDS at `lds`
-// (64 lanes x 4 bytes of scratch): pulls the lines into L2 with no register
-// destination for the compiler to track.  Offsets outside the descriptor's
-// range read nothing.
-__device__ inline void l2_touch(u32x4 rsrc, uint32_t lds, uint32_t voff) {
+// LDS-DMA of 4 bytes per lane: lane l's word at byte voff of the buffer
+// goes to LDS address lds + 4 l (offsets outside the descriptor's range
+// deliver zeros).  Inline asm and uncounted by the compiler, like dma16.
+__device__ inline void dma4(u32x4 rsrc, uint32_t lds, uint32_t voff) {
     asm volatile(
         "s_mov_b32 m0, %2\n\t"
         "s_nop 0\n\t"
@@ -292,6 +291,26 @@ __device__ inline void l2_touch(u32x4 rsrc, uint32_t lds, uint32_t voff) {
         : "v"(voff), "s"(rsrc), "s"(lds)
         : "m0");
 }
+
+// Two LDS-DMAs of 16 bytes per lane under one M0: the second lands 2048
+// bytes after the first in LDS, from byte voff1 + 2048 of the buffer (the
+// instruction offset moves both addresses).
+__device__ inline void dma16x2(u32x4 rsrc, uint32_t lds, uint32_t voff0, uint32_t voff1) {
+    asm volatile(
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %0, %2, 0 offen lds\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen offset:2048 lds"
+        :
+        : "v"(voff0), "v"(voff1), "s"(rsrc), "s"(lds)
+        : "m0");
+}
+
+// Touch 4 bytes per lane at rsrc + voff, delivered into LDS at `lds`
+// (64 lanes x 4 bytes of scratch): pulls the lines into L2 with no register
+// destination for the compiler to track.  Offsets outside the descriptor's
+// range read nothing.
+__device__ inline void l2_touch(u32x4 rsrc, uint32_t lds, uint32_t voff) { dma4(rsrc, lds, voff); }
 
 // An opaque (empty) redefinition of a register value.
 template <typename V>
@@ -729,7 +748,9 @@ __host__ __device__ inline bool work_item(const VerifyParams& p, int blk, int& b
     return true;
 }
 
-constexpr int kMaxSplitPages = 768;  // pages of a paged split, listed in LDS by its prologue
+// paged cache: a split's page numbers stream through a ring of kPgSlots
+// windows of kPgWin consecutive table entries in LDS
+constexpr int kPgWin = 64, kPgSlots = 4;
 
 template <typename T, int DL, int DR, bool kArgmax, bool kTouch, bool kPaged, bool kClip>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void verify_split(
@@ -780,16 +801,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const int ntiles = (kend - kbeg + KT - 1) / KT;
     // rows the tiles read: [kbeg, kread), kread <= kT (an empty split reads none)
     const int kread = max(kbeg, min(kend, kT));
-    // paged cache: the split's page numbers go to LDS once, so the tile loop
-    // reads them in order with its other LDS traffic (a scalar load per tile
-    // would make every LDS wait in the loop wait for it too)
-    __shared__ int32_t s_pages[kPaged ? kMaxSplitPages : 1];
-    if constexpr (kPaged) {
-        const int pg0 = kbeg >> p.map.shift, npg = ((kend - 1) >> p.map.shift) - pg0 + 1;
-        const int32_t* tb = p.map.table + (int64_t)b * p.map.ld + pg0;
-        for (int i = tid; i < npg; i += kThreads) s_pages[i] = tb[i];
-        __syncthreads();
-    }
+    // paged cache: the split's page numbers, window w (entries [w*kPgWin,
+    // (w+1)*kPgWin) from the split's first page) in ring slot w % kPgSlots;
+    // the value wavefronts fill and read them (the tile loop reads them in
+    // order with its other LDS traffic: a scalar load per tile would make
+    // every LDS wait in the loop wait for it too)
+    __shared__ __attribute__((aligned(16))) int32_t s_pgwin[kPaged ? kPgWin * kPgSlots : 1];
 
     const int wrow0 = rt * ROWS_WG + grp * 32;
     const bool active = wrow0 < p.rows;            // the row group has real rows
@@ -1003,7 +1020,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const char* kpe_b = uniform_ptr(reinterpret_cast<const char*>(static_cast<const T*>(p.kpe) + kvb * p.ld_kpe));
     const int pshift = kPaged ? p.map.shift : 0;
     const int ppg0 = kPaged ? (kbeg >> pshift) : 0;
+    const int npg = kPaged ? ((kend - 1) >> pshift) - ppg0 + 1 : 0;  // pages of the split
+    // the split's table entries (entries past them deliver zeros); value
+    // wavefront 0 streams them into the window ring by LDS-DMA, landing
+    // under the same waits and barriers as the tiles
+    u32x4 pg_rsrc = {};
+    if constexpr (kPaged)
+        pg_rsrc = buffer_rsrc(p.map.table + (int64_t)b * p.map.ld + ppg0, npg * (int)sizeof(int32_t));
+    auto pg_fill = [&](int w) {
+        if constexpr (kPaged) {
+            if (grp == 0)
+                dma4(pg_rsrc, lds_addr(s_pgwin) + (uint32_t)((w % kPgSlots) * kPgWin * (int)sizeof(int32_t)),
+                     (uint32_t)((w * kPgWin + lane) * (int)sizeof(int32_t)));
+        }
+    };
+    int pg_filled = 0;  // windows [0, pg_filled] are in the ring (or on their way)
     const int ldA = (int)(p.ld_ckv * (int64_t)sizeof(T)), ldB = (int)(p.ld_kpe * (int64_t)sizeof(T));
+    const uint32_t pg_bytesA = (uint32_t)ldA << pshift, pg_bytesB = (uint32_t)ldB << pshift;  // (paged)
+    // instructions 2k and 2k+1 of a wavefront (same region, 2048 bytes apart
+    // in LDS) go out as one pair under one M0: half the M0 writes and their
+    // wait states in the value wavefronts' instruction stream (measured 1.7 %
+    // faster at 32 ragged requests of 8 heads, neutral at 131072 keys)
+    constexpr bool kPairDma = sizeof(T) == 2 && S::IA % 2 == 0 && S::IB % 2 == 0 && S::NDW * 64 * 16 == 2048;
     uint32_t voff[S::DPW];
 #pragma unroll
     for (int i = 0; i < S::DPW; ++i) {
@@ -1012,6 +1050,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         const int r = jj * (ra ? S::RPI_A : S::RPI_B) + lane / (ra ? S::CA : S::CB);
         const int chunk = ra ? (lane % S::CA) ^ Tr::swA(r) : (lane % S::CB) ^ Tr::swB(r);
         voff[i] = (uint32_t)(r * (ra ? ldA : ldB) + chunk * 16);
+        if (kPairDma && (i & 1)) voff[i] -= 2048;  // the pair's instruction offset adds it back
         pin_reg(voff[i]);
     }
     // L2 touches of a tile: every 128-byte line of its rows (LA lines of
@@ -1035,16 +1074,44 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         u32x4 ra, rb;    // raw buffer descriptors of the tile's rows in c_kv / k_pe
         uint32_t lds;    // LDS byte address of the tile's ring slot
     };
-    auto tile_dma = [&](int tile) {
+    // paged: the page holding a tile's rows (a tile past the split: the
+    // last tile's page; its descriptor is empty), read from the window ring;
+    // the loop reads the next phase's page number at the end of a phase, so
+    // no phase starts with a wait on an LDS read before its first load.
+    // page_direct reads the table itself (the prologue's tiles).
+    auto page_index = [&](int tile) { return ((kbeg + (tile < ntiles ? tile : ntiles - 1) * KT) >> pshift) - ppg0; };
+    auto page_of = [&](int tile) -> int32_t {
+        if constexpr (kPaged) {
+            const int pi = page_index(tile);
+            return s_pgwin[(pi / kPgWin) % kPgSlots * kPgWin + pi % kPgWin];
+        } else {
+            return 0;
+        }
+    };
+    auto page_direct = [&](int tile) -> int32_t {
+        if constexpr (kPaged) {
+            return p.map.table[(int64_t)b * p.map.ld + ppg0 + page_index(tile)];
+        } else {
+            return 0;
+        }
+    };
+    auto tile_dma = [&](int tile, int32_t page) {
         const bool real = tile < ntiles;
         const int t0 = kbeg + (real ? tile : 0) * KT;
         int nrows = kread - t0;
         nrows = real ? (nrows > KT ? KT : nrows) : 0;
         TileDma d;
         if constexpr (kPaged) {  // pool row of slot t0: its page's first row + the offset in the page
-            const int64_t row = ((int64_t)s_pages[(t0 >> pshift) - ppg0] << pshift) + (t0 & ((1 << pshift) - 1));
-            d.ra = buffer_rsrc(uniform_ptr(ckv_b + row * ldA), nrows * ldA);
-            d.rb = buffer_rsrc(uniform_ptr(kpe_b + row * ldB), nrows * ldB);
+            // page * (bytes of a page) + (row in the page) * (row bytes): a
+            // 32 x 32 -> 64-bit product and a 32-bit one (a page's bytes
+            // stay below 4 GiB), fewer scalar instructions per tile than a
+            // 64-bit row index times the stride
+            const uint32_t pg = (uint32_t)__builtin_amdgcn_readfirstlane(page);
+            const uint32_t in_pg = (uint32_t)(t0 & ((1 << pshift) - 1));
+            const uint64_t offA = (uint64_t)pg * pg_bytesA + in_pg * (uint32_t)ldA;
+            const uint64_t offB = (uint64_t)pg * pg_bytesB + in_pg * (uint32_t)ldB;
+            d.ra = buffer_rsrc(ckv_b + offA, nrows * ldA);
+            d.rb = buffer_rsrc(kpe_b + offB, nrows * ldB);
         } else {
             d.ra = buffer_rsrc(ckv_b + (int64_t)t0 * ldA, nrows * ldA);
             d.rb = buffer_rsrc(kpe_b + (int64_t)t0 * ldB, nrows * ldB);
@@ -1055,10 +1122,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     auto issue = [&](const TileDma& d, int i) {
         const bool ra = i < S::IA;
         const int jj = grp + S::NDW * (ra ? i : i - S::IA);
-        dma16(ra ? d.ra : d.rb, d.lds + (uint32_t)(((ra ? 0 : KT * S::CA) + jj * 64) * 16), voff[i]);
+        const uint32_t lds = d.lds + (uint32_t)(((ra ? 0 : KT * S::CA) + jj * 64) * 16);
+        if constexpr (kPairDma) {
+            if ((i & 1) == 0) dma16x2(ra ? d.ra : d.rb, lds, voff[i], voff[i + 1]);
+        } else {
+            dma16(ra ? d.ra : d.rb, lds, voff[i]);
+        }
     };
     auto issue_tile = [&](int tile) {
-        const TileDma d = tile_dma(tile);
+        const TileDma d = tile_dma(tile, page_direct(tile));
 #pragma unroll
         for (int i = 0; i < S::DPW; ++i) issue(d, i);
     };
@@ -1090,6 +1162,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             lsum[rb] = floatx16{};
         }
         mfma_settle();  // the zeroing writes above precede the first product
+        // paged: the first two page windows land with tile 0 (a second pass
+        // refills them: later windows took their slots)
+        pg_fill(0);
+        pg_fill(1);
+        pg_filled = 1;
         // (loading the first four tiles at once measured slower at the
         // K2-like head share: the burst delays tile 0)
         issue_tile(0);
@@ -1101,6 +1178,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         issue_tile(2);    // phase 1: scores of tile 1, softmax of tile 0
         wait_vmem_all();
         __syncthreads();  // tile 2 resident; probabilities of tile 0 published
+        // the descriptors of a tile are made once: a phase touches tile it+2,
+        // and the next phase loads it with the same descriptors
+        TileDma d_next = tile_dma(3, page_of(3));
+        int32_t pg_touch = page_of(4);  // (paged) page of the next touched tile
         for (int it = 2; it <= ntiles + 1; ++it) {
             // phase it: O^T (this wavefront's columns x 64 rows) += V^T . P^T
             // for tile it-2: key step outer, column tile inner, row group
@@ -1115,8 +1196,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             // the last-level cache) the touches are not issued at all.
             const int tv = it - 2;
             const char* slot = smem + (tv % NSTAGE) * S::STAGE_BYTES;
-            const TileDma d = tile_dma(it + 1);
-            const TileDma dt = tile_dma(it + 2);  // touched into L2 one phase before its load
+            if constexpr (kPaged) {
+                // keep the ring two windows ahead of the tile whose page this
+                // phase's end reads (it + 3): a window holds >= kPgWin
+                // tiles, so one fill per phase keeps up, and the slot it
+                // takes held a window no lookup needs any more.  Issued
+                // before the tile loads, it has landed by this phase's
+                // closing wait.
+                const int need = page_index(it + 3) / kPgWin + 2;
+                if (pg_filled < need && (pg_filled + 1) * kPgWin < npg) pg_fill(++pg_filled);
+            }
+            const TileDma d = d_next;
+            const TileDma dt = tile_dma(it + 2, pg_touch);  // touched into L2 one phase before its load
             const uint32_t touch_lds = lds_addr(s_touch);
             Frag pb[NGRP][S::NPS];
 #pragma unroll
@@ -1151,6 +1242,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
+            d_next = dt;
+            if constexpr (kPaged) pg_touch = page_of(it + 3);
             // tile it+1 landed (loads complete in issue order); this phase's
             // touches may stay in flight
             asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kTouch ? kTouches : 0) : "memory");
@@ -1352,12 +1445,14 @@ int check_desc(const ddt_attn_desc* d, const int32_t* prefix_len_host) {
     const int64_t es = ddt::elem_bytes(d->dtype);
     if ((d->ld_ql * es) % 16 || (d->ld_qp * es) % 16 || (d->ld_ckv * es) % 16 || (d->ld_kpe * es) % 16)
         return DDT_EINVAL;
+    if (d->ld_ckv * es > INT32_MAX || d->ld_kpe * es > INT32_MAX) return DDT_EINVAL;  // row strides in 32 bits
     if ((int64_t)d->H * d->N > (1 << 24)) return DDT_EINVAL;
     for (int b = 0; b < d->B; ++b)
         if (prefix_len_host[b] < 0 || (int64_t)prefix_len_host[b] + d->N > 0x7fffffff - 4096) return DDT_EINVAL;
     if (d->block_table != nullptr) {  // pages: a power of two of at least one key tile; every slot in the table
         const int ps = d->page_size;
         if (ps < KT || ps > (1 << 16) || (ps & (ps - 1)) != 0 || d->bt_ld < 1) return DDT_EINVAL;
+        if (d->ld_ckv * es * ps > UINT32_MAX || d->ld_kpe * es * ps > UINT32_MAX) return DDT_EINVAL;  // page < 4 GiB
         if (d->dtype != DDT_BF16) return DDT_EUNSUPPORTED;
         for (int b = 0; b < d->B; ++b)
             if (((int64_t)prefix_len_host[b] + d->N + ps - 1) / ps > d->bt_ld) return DDT_EINVAL;
@@ -1451,13 +1546,6 @@ int64_t plan_cost(const int64_t* T, int B, int row_tiles, int64_t chunk, int cus
     return finish + (split ? kMergeCost : 0) + part_cost;
 }
 
-// Longest split: a paged split lists at most kMaxSplitPages pages in LDS,
-// and a split of c keys touches at most floor((c-1)/page) + 2 pages.
-int64_t max_chunk(const ddt_attn_desc* d) {
-    if (d->block_table == nullptr) return INT64_MAX;
-    return (int64_t)(kMaxSplitPages - 1) * d->page_size / KT * KT;
-}
-
 // The key chunk with the lowest estimated finish time among chunks that cut
 // the longest request into 1 to 32 equal parts, that give the CUs 1 to 16
 // rounds of equal work (a spread of each), and the smallest chunk (ties go
@@ -1470,8 +1558,7 @@ int64_t choose_chunk(const ddt_attn_desc* d, const int32_t* P, int row_tiles, in
         tmax = T[b] > tmax ? T[b] : tmax;
         work += T[b] * row_tiles;
     }
-    int64_t top = (int64_t)ddt::round_up((size_t)tmax, KT);
-    if (top > max_chunk(d)) top = max_chunk(d);
+    const int64_t top = (int64_t)ddt::round_up((size_t)tmax, KT);
     int64_t best = top, best_cost = plan_cost(T, d->B, row_tiles, top, cus);
     int64_t tried[64];
     int nt = 0;
@@ -1502,7 +1589,7 @@ Plan make_plan(const ddt_attn_desc* d, const int32_t* P, VerifyParams* vp) {
     pl.row_tiles = (rows + ROWS_WG - 1) / ROWS_WG;
     const int cus = num_cus();
     if (d->kv_chunk > 0)
-        pl.chunk = (int)std::min<int64_t>((int64_t)ddt::round_up((size_t)d->kv_chunk, KT), max_chunk(d));
+        pl.chunk = (int)std::min<int64_t>((int64_t)ddt::round_up((size_t)d->kv_chunk, KT), int64_t(1) << 30);
     else
         pl.chunk = (int)choose_chunk(d, P, pl.row_tiles, cus);
     int64_t total = 0;

@@ -75,6 +75,8 @@ def test_host_side_validation(lib):
     assert lib.ddt_verify_workspace(ctypes.byref(bad), pl, ctypes.byref(n)) == -2   # not built
     bad = ddt.AttnDesc(1, 8, 64, 512, 64, ddt.DDT_BF16, 0.04, 0, 577, 576, 576, 576)
     assert lib.ddt_verify_workspace(ctypes.byref(bad), pl, ctypes.byref(n)) == -1   # stride alignment
+    bad = ddt.AttnDesc(1, 8, 64, 512, 64, ddt.DDT_BF16, 0.04, 0, 576, 576, 1 << 30, 576)
+    assert lib.ddt_verify_workspace(ctypes.byref(bad), pl, ctypes.byref(n)) == -1   # 2 GiB cache rows
     bad = ddt.AttnDesc(129, 8, 64, 512, 64, ddt.DDT_BF16, 0.04, 0, 576, 576, 576, 576)
     assert lib.ddt_verify_workspace(ctypes.byref(bad), pl, ctypes.byref(n)) == -1   # batch limit
     for scale in (0.0, -0.04, float("inf"), float("nan")):                         # scale must be > 0
@@ -163,6 +165,11 @@ def test_paged_desc_validation(lib):
     assert lib.ddt_verify_workspace(desc(16, 400), P, ctypes.byref(n)) == -1    # smaller than a key tile
     assert lib.ddt_verify_workspace(desc(1 << 17, 1), P, ctypes.byref(n)) == -1  # larger than 65536
     assert lib.ddt_verify_workspace(desc(0, 0, table=None), P, ctypes.byref(n)) == 0  # contiguous
+    big = ddt.AttnDesc(2, 8, 32, 512, 64, 1, 1 / 24, 0, 576, 576, 1 << 15, 576)  # 64 KiB rows
+    big.block_table, big.bt_ld, big.page_size = 1 << 20, 100, 1 << 16          # 4 GiB pages
+    assert lib.ddt_verify_workspace(ctypes.byref(big), P, ctypes.byref(n)) == -1
+    big.page_size, big.bt_ld = 1 << 15, 100                                     # 2 GiB pages
+    assert lib.ddt_verify_workspace(ctypes.byref(big), P, ctypes.byref(n)) == 0
     d = ddt.AttnDesc(2, 2, 8, 64, 16, 0, 0.1, 0, 80, 80, 80, 80)                 # fp32 (64, 16) instance
     d.block_table, d.bt_ld, d.page_size = 1 << 20, 100, 32
     assert lib.ddt_verify_workspace(ctypes.byref(d), P, ctypes.byref(n)) == -2  # paged: bf16 instance only

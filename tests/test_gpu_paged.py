@@ -51,31 +51,56 @@ def from_paged(phys, table, ps, w):
     (32, (100, 3000), 0, 32),
     (64, (100, 3000), 0, 32),
     (512, (100, 3000), 0, 32),
-    (32, (25000, 32000), 0, 32),      # splits capped at 767 pages: a plan of its own
-    (64, (100, 3000), 1 << 20, 32),   # an explicit chunk past the cap is capped
+    (32, (25000, 32000), 0, 32),      # splits of ~1000 pages: the page-window ring wraps many times
+    (64, (100, 3000), 1 << 20, 32),   # an explicit chunk of 2^20 keys: one split per request
     (64, (100, 1500), 256, 300),      # a large tree: splits end at each work item's last node
 ])
 def test_paged_attention_equals_contiguous(orc, ps, prefix_range, kv_chunk, N):
-    """Where the paged split fits the contiguous plan the two launches are
-    bit-identical; where the page cap shortens the splits, both still
-    match the oracle."""
+    """The paged launch has the contiguous launch's plan and arithmetic, so
+    the two are bit-identical, and both match the oracle."""
     w = synth.workload(3, B=2 if prefix_range[0] > 20000 or N > 128 else 4, N=N, prefix_range=prefix_range)
     rng = np.random.default_rng(ps)
     phys, table = to_paged(w, ps, rng)
     dw = DevWorkload(w)
     mask = ddt.build_mask(dw.parents)[0]
     out_c, lse_c = ddt.verify_attn(dw.q_lat(), dw.q_pe(), dw.ckv(), dw.kpe(), dw.kv_base, w.prefix_len, mask,
-                                   H=w.H, scale=w.scale, kv_chunk=kv_chunk if kv_chunk < (1 << 20) else 0)
+                                   H=w.H, scale=w.scale, kv_chunk=kv_chunk)
     pd, td = to_dev(phys), to_dev(table)
     dl = w.d_lat
     out_p, lse_p = ddt.verify_attn(dw.q_lat(), dw.q_pe(), pd[:, :dl], pd[:, dl:], None, w.prefix_len, mask,
                                    H=w.H, scale=w.scale, pages=(td, ps), kv_chunk=kv_chunk)
     torch.cuda.synchronize()
-    cap = 767 * ps
-    same_plan = kv_chunk < (1 << 20) and int(w.prefix_len.max()) + w.N <= cap
-    if same_plan:
-        assert torch.equal(out_c.view(torch.int16), out_p.view(torch.int16))
-        assert torch.equal(lse_c, lse_p)
+    assert torch.equal(out_c.view(torch.int16), out_p.view(torch.int16))
+    assert torch.equal(lse_c, lse_p)
+    ref_out, ref_lse = oracle_attn(orc, w)
+    check_attn(to_host(out_p), to_host(lse_p), ref_out, ref_lse, "bf16")
+
+
+@pytest.mark.parametrize("ps,kv_chunk", [(32, 0), (32, 1 << 20), (32, 4096), (64, 1 << 20)])
+def test_paged_attention_second_pass(orc, ps, kv_chunk):
+    """Scores far above the first tiles' late in each split force the second
+    pass after the page-window ring has moved on: the pass refills the
+    first windows, and the result is bit-identical to the contiguous launch
+    and matches the oracle."""
+    w = synth.workload(3, B=3, prefix_range=(6000, 9000))
+    rng = np.random.default_rng(1000 + ps)
+    for b in range(w.B):
+        P = int(w.prefix_len[b])
+        rows = w.kv_base[b] + rng.choice(np.arange(P - 1500, P), 3, replace=False)
+        big = synth.bf16_bits_to_f32(w.pool[rows]) * np.float32(1e4)
+        w.pool[rows] = synth.to_bf16_bits(big)
+    phys, table = to_paged(w, ps, rng)
+    dw = DevWorkload(w)
+    mask = ddt.build_mask(dw.parents)[0]
+    out_c, lse_c = ddt.verify_attn(dw.q_lat(), dw.q_pe(), dw.ckv(), dw.kpe(), dw.kv_base, w.prefix_len, mask,
+                                   H=w.H, scale=w.scale, kv_chunk=kv_chunk)
+    pd, td = to_dev(phys), to_dev(table)
+    dl = w.d_lat
+    out_p, lse_p = ddt.verify_attn(dw.q_lat(), dw.q_pe(), pd[:, :dl], pd[:, dl:], None, w.prefix_len, mask,
+                                   H=w.H, scale=w.scale, pages=(td, ps), kv_chunk=kv_chunk)
+    torch.cuda.synchronize()
+    assert torch.equal(out_c.view(torch.int16), out_p.view(torch.int16))
+    assert torch.equal(lse_c, lse_p)
     ref_out, ref_lse = oracle_attn(orc, w)
     check_attn(to_host(out_p), to_host(lse_p), ref_out, ref_lse, "bf16")
 
