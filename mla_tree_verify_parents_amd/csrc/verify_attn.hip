@@ -480,6 +480,7 @@ struct VerifyParams {
     int n_full_groups, n_units, unit_rows, units_per_group;
     int whole_blocks;  // blocks of the units dealt whole (a multiple of 8 units); the rest row by row
     int single_round;  // at most one workgroup per CU: XCD x takes a contiguous range of work items
+    int rt_desc;       // deal a split's row tiles last first (large trees: later rows see more keys)
     // target argmax riding along in the same launch (workgroups n_attn ..)
     int n_attn;                 // attention workgroups (the rest are argmax workgroups)
     int am_wgs, am_dtype, am_vec;
@@ -733,6 +734,7 @@ __host__ __device__ inline bool work_item(const VerifyParams& p, int blk, int& b
     const int grp = u / p.units_per_group, sg = u - grp * p.units_per_group;
     rt = sg * p.unit_rows + r_in;
     if (rt >= p.row_tiles) return false;
+    if (p.rt_desc) rt = p.row_tiles - 1 - rt;
     if (grp < p.n_full_groups) {
         int lo = 0, hi = p.B - 1;
         while (lo < hi) {
@@ -1643,6 +1645,11 @@ Plan make_plan(const ddt_attn_desc* d, const int32_t* P, VerifyParams* vp) {
         vp->n_units = (int)n_units;
         vp->whole_blocks = (int)whole;
         vp->single_round = pl.total_wg <= cus ? 1 : 0;
+        // trees past 128 nodes (prefill chunks, causal): a row tile's keys end
+        // at its last node, so later row tiles are longer work items; dealt
+        // longest first they pack the CUs tighter (a host simulation of the
+        // dispatch: 5 % shorter for an 8192-token prompt in 1024-token chunks)
+        vp->rt_desc = d->N > 128 ? 1 : 0;
         vp->unit_rows = unit_rows;
         vp->units_per_group = upg;
     }
