@@ -264,7 +264,8 @@ __device__ inline uint32_t lds_addr(const void* p) {
     return (uint32_t)reinterpret_cast<uintptr_t>((const lds_void*)p);
 }
 // LDS-DMA of 16 bytes per lane: lane l's chunk at byte voff of the buffer
-// goes to LDS address lds + 16 l.  Issued as inline asm, so the compiler
+// goes to LDS address lds + 16 l (lds: wave-uniform, read from the first
+// lane into M0).  Issued as inline asm, so the compiler
 // neither orders it against LDS reads of other addresses (its alias
 // analysis of LDS-DMA is conservative and would wait for every load) nor
 // counts it: the callers wait for it with explicit vmcnt waits before the
@@ -275,7 +276,7 @@ __device__ inline void dma16(u32x4 rsrc, uint32_t lds, uint32_t voff) {
         "s_nop 0\n\t"
         "buffer_load_dwordx4 %0, %1, 0 offen lds"
         :
-        : "v"(voff), "s"(rsrc), "s"(lds)
+        : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds))
         : "m0");
 }
 
@@ -288,7 +289,7 @@ __device__ inline void dma4(u32x4 rsrc, uint32_t lds, uint32_t voff) {
         "s_nop 0\n\t"
         "buffer_load_dword %0, %1, 0 offen lds"
         :
-        : "v"(voff), "s"(rsrc), "s"(lds)
+        : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds))
         : "m0");
 }
 
@@ -302,7 +303,7 @@ __device__ inline void dma16x2(u32x4 rsrc, uint32_t lds, uint32_t voff0, uint32_
         "buffer_load_dwordx4 %0, %2, 0 offen lds\n\t"
         "buffer_load_dwordx4 %1, %2, 0 offen offset:2048 lds"
         :
-        : "v"(voff0), "v"(voff1), "s"(rsrc), "s"(lds)
+        : "v"(voff0), "v"(voff1), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds))
         : "m0");
 }
 
