@@ -52,11 +52,14 @@ def test_verify_attn_device_lengths_clamped(orc):
     check_attn(to_host(out), to_host(lse), ref_out, ref_lse, "bf16")
 
 
-def test_paged_verify_attn_device_lengths(orc):
+@pytest.mark.parametrize("ps,extra,prefix_range,kv_chunk", [
+    (64, 1000, (200, 3000), 512),
+    (32, 3000, (4000, 9000), 1 << 20),   # one split of up to 375 pages: the page-window ring wraps
+])
+def test_paged_verify_attn_device_lengths(orc, ps, extra, prefix_range, kv_chunk):
     """Pages past each request's keys (inside its table row for the
     bounds) are NaN pages: none of them may be read."""
-    ps, extra = 64, 1000
-    w = synth.workload(3, B=3, N=32, prefix_range=(200, 3000))
+    w = synth.workload(3, B=3, N=32, prefix_range=prefix_range)
     rng = np.random.default_rng(5)
     T = w.prefix_len.astype(np.int64) + w.N
     bound = w.prefix_len.astype(np.int64) + extra
@@ -78,7 +81,7 @@ def test_paged_verify_attn_device_lengths(orc):
     pd, td = to_dev(phys), to_dev(table)
     dl = w.d_lat
     out, lse = ddt.verify_attn(dw.q_lat(), dw.q_pe(), pd[:, :dl], pd[:, dl:], None, bound, mask, H=w.H,
-                               scale=w.scale, pages=(td, ps), kv_chunk=512, prefix_len_dev=dw.prefix_dev)
+                               scale=w.scale, pages=(td, ps), kv_chunk=kv_chunk, prefix_len_dev=dw.prefix_dev)
     ref_out, ref_lse = oracle_attn(orc, w)
     check_attn(to_host(out), to_host(lse), ref_out, ref_lse, "bf16")
 
