@@ -161,6 +161,20 @@ typedef struct {
  * needed), and concurrent calls must not share one. */
 int ddt_verify_workspace(const ddt_attn_desc* d, const int32_t* prefix_len_host, size_t* bytes);
 
+/* Work plan of ddt_verify_attn for this shape and these host lengths, on
+ * the host (no device work): the split-KV decomposition of the attention
+ * below (request b's keys [0, P_b + N) cut into *chunk-key splits whose
+ * partial results the merge combines exactly).  *n_blocks: attention
+ * workgroups the launch starts; *chunk: keys per split; nsplit [B] (may be
+ * NULL): splits of each request; items [cap][3] int32 (may be NULL):
+ * workgroup k's (request, split, row tile of 64 query rows), or (-1, -1,
+ * -1) for a workgroup that only pads the deal to the XCDs.  Host arrays,
+ * caller-owned.  DDT_EINVAL when cap < *n_blocks (*n_blocks and *chunk are
+ * still set), or as ddt_verify_workspace.  For schedulers that size
+ * launches and for tests of the decomposition. */
+int ddt_verify_plan(const ddt_attn_desc* d, const int32_t* prefix_len_host, int* n_blocks, int* chunk,
+                    int32_t* nsplit, int32_t* items, int cap);
+
 /*
  * Tree-verify attention, absorbed MLA form.  For every (b, i, h):
  *   visible keys V = [0, P_b) u {P_b + j : mask bit j of row (b, i) set}

@@ -1854,6 +1854,37 @@ extern "C" int ddt_verify_workspace(const ddt_attn_desc* d, const int32_t* prefi
     return DDT_OK;
 }
 
+extern "C" int ddt_verify_plan(const ddt_attn_desc* d, const int32_t* prefix_len_host, int* n_blocks, int* chunk,
+                               int32_t* nsplit, int32_t* items, int cap) {
+    if (n_blocks == nullptr || chunk == nullptr) return DDT_EINVAL;
+    const int rc = check_desc(d, prefix_len_host);
+    if (rc != DDT_OK) return rc;
+    VerifyParams vp{};
+    const Plan pl = make_plan(d, prefix_len_host, &vp);
+    *n_blocks = pl.n_blocks;
+    *chunk = pl.chunk;
+    if (nsplit != nullptr)
+        for (int b = 0; b < d->B; ++b) nsplit[b] = vp.nsplit[b];
+    if (items == nullptr) return DDT_OK;
+    if (cap < pl.n_blocks) return DDT_EINVAL;
+    // the fields work_item reads besides the plan's (setup_attn sets them for a launch)
+    vp.B = d->B;
+    vp.H = d->H;
+    vp.N = d->N;
+    vp.rows = d->H * d->N;
+    vp.row_tiles = pl.row_tiles;
+    vp.chunk = pl.chunk;
+    vp.total_wg = pl.total_wg;
+    for (int blk = 0; blk < pl.n_blocks; ++blk) {
+        int b = -1, split = -1, rt = -1;
+        if (!work_item(vp, blk, b, split, rt)) b = split = rt = -1;
+        items[3 * blk] = b;
+        items[3 * blk + 1] = split;
+        items[3 * blk + 2] = rt;
+    }
+    return DDT_OK;
+}
+
 extern "C" int ddt_verify_attn(const ddt_attn_desc* d, const void* q_lat, const void* q_pe, const void* ckv,
                                const void* kpe, const int64_t* kv_base, const int32_t* prefix_len_host,
                                const uint64_t* mask, void* out, float* lse, void* workspace,
