@@ -66,7 +66,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true", help="skip the on-device MFMA / HBM peak probes")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the side measurements (paged, prefill, projections, HBM stages, config 2, loop)")
+                    help="skip the side measurements (paged, prefill, projections, HBM stages, configs 2 and 3, loop)")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache attention timing (configs 2 and 3)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget for the oracle timing")
@@ -201,6 +201,10 @@ def main():
         if args.config != 2:
             res["config2"] = guarded(lambda: measure_config(2, args, dev, headline=False))
             progress("config 2 timed")
+        if args.config != 3:
+            res["config3"] = guarded(lambda: measure_config(3, args, dev, headline=False))
+            progress("config 3 timed")
+        if args.config != 2:
             res["config5_loop"] = guarded(lambda: run_loop(args, dev, 3, 20, brief=True))
             progress("verify loop timed")
     add_peaks(res, args, dev)
@@ -341,6 +345,9 @@ def measure_config(cfg, args, dev, headline):
     ms_attn = float(np.median(attn_ms))
     del g_one, g_step, g_a1, g_attn
     progress(f"config {cfg} step and attention timed")
+    small = guarded(lambda: time_small_kernels(parents, draft, target if target is not None else tids, ckv, kpe,
+                                               kv_base, prefix0, new_prefix, mask, depth, terr, acc, path, tok,
+                                               stream))
 
     pairs = w.visible_pairs()
     flops = pairs * FLOP_PER_PAIR
@@ -381,6 +388,7 @@ def measure_config(cfg, args, dev, headline):
     }
     if spg > 1:
         res["step_timing"]["one_step_graphs_ms_per_step"] = spread(one_ms)
+    res["small_kernels"] = small
     if not headline:
         for k in ("metric", "n_gpus", "steps", "warmup", "higher_is_better", "scaling", "vs_baseline", "dtype",
                   "data", "unit"):
@@ -408,6 +416,42 @@ def measure_config(cfg, args, dev, headline):
     if not args.no_cpu_baseline:
         progress("oracle timing on the host")
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, flops)
+    return res
+
+
+def time_small_kernels(parents, draft, target, ckv, kpe, kv_base, prefix0, new_prefix, mask, depth, terr, acc, path,
+                       tok, stream):
+    """The latency-bound kernels of the step alone, at the configuration's
+    shape: µs per call (median of WINDOWS windows of >= WINDOW_MS of
+    back-to-back calls in graphs) of the ancestor-mask build, greedy
+    acceptance, and acceptance + compaction + length update in one launch
+    (the form the step uses), with the compaction's effective bandwidth:
+    bytes = 2 x (accepted path lengths, root included) x row bytes."""
+    import torch
+
+    from mla_tree_verify_parents_amd import ddt
+
+    def per_call_us(fn):
+        g1 = graph_of(fn, 1)
+        est = estimate_ms(g1.replay, 1, stream)
+        per = max(1, min(500, int(2.0 / max(est, 1e-4))))
+        g = graph_of(fn, per)
+        g.replay()
+        ms, units = time_windows(g.replay, per, est, stream)
+        del g1, g
+        return {"us": round(float(np.median(ms)) * 1e3, 3), "us_spread": spread([m * 1e3 for m in ms]),
+                "calls_per_window": units}
+
+    res = {"mask": per_call_us(lambda: ddt.build_mask(parents, mask, depth, terr)),
+           "greedy_accept": per_call_us(lambda: ddt.greedy_accept(target, draft, parents, acc, path, tok))}
+    res["accept_compact"] = per_call_us(lambda: ddt.accept_compact(target, draft, parents, ckv, kpe, kv_base,
+                                                                   prefix0, acc, path, tok,
+                                                                   new_prefix_len=new_prefix))
+    torch.cuda.synchronize()
+    moved = int(acc.sum().item()) + int(acc.numel())
+    row_bytes = (ckv.shape[1] + kpe.shape[1]) * ckv.element_size()
+    res["accept_compact"]["rows_moved"] = moved
+    res["accept_compact"]["GBps"] = round(2 * moved * row_bytes / (res["accept_compact"]["us"] * 1e-6) / 1e9, 2)
     return res
 
 
