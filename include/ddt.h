@@ -163,17 +163,19 @@ int ddt_verify_workspace(const ddt_attn_desc* d, const int32_t* prefix_len_host,
 
 /* Work plan of ddt_verify_attn for this shape and these host lengths, on
  * the host (no device work): the split-KV decomposition of the attention
- * below (request b's keys [0, P_b + N) cut into *chunk-key splits whose
- * partial results the merge combines exactly).  *n_blocks: attention
- * workgroups the launch starts; *chunk: keys per split; nsplit [B] (may be
- * NULL): splits of each request; items [cap][3] int32 (may be NULL):
- * workgroup k's (request, split, row tile of 64 query rows), or (-1, -1,
- * -1) for a workgroup that only pads the deal to the XCDs.  Host arrays,
- * caller-owned.  DDT_EINVAL when cap < *n_blocks (*n_blocks and *chunk are
- * still set), or as ddt_verify_workspace.  For schedulers that size
- * launches and for tests of the decomposition. */
+ * below.  Request b's keys [0, P_b + N) are cut into splits of *chunk keys
+ * whose partial results the merge combines exactly; a work item is one
+ * split of one request for one row tile of 64 query rows, one per
+ * attention workgroup.  *n_blocks: attention workgroups the launch starts
+ * (work items plus workgroups that only pad the deal to the XCDs);
+ * nsplit [B] (may be NULL): splits of each request; *n_items: work items;
+ * items [cap][6] int32 (may be NULL): per work item, in workgroup order,
+ * (workgroup, request, split, row tile, first key, end key).  Host arrays,
+ * caller-owned.  DDT_EINVAL when items is given and cap < *n_items (the
+ * counts are still set), or as ddt_verify_workspace.  For schedulers that
+ * size launches and for tests of the decomposition. */
 int ddt_verify_plan(const ddt_attn_desc* d, const int32_t* prefix_len_host, int* n_blocks, int* chunk,
-                    int32_t* nsplit, int32_t* items, int cap);
+                    int32_t* nsplit, int32_t* items, int cap, int* n_items);
 
 /*
  * Tree-verify attention, absorbed MLA form.  For every (b, i, h):

@@ -1855,8 +1855,8 @@ extern "C" int ddt_verify_workspace(const ddt_attn_desc* d, const int32_t* prefi
 }
 
 extern "C" int ddt_verify_plan(const ddt_attn_desc* d, const int32_t* prefix_len_host, int* n_blocks, int* chunk,
-                               int32_t* nsplit, int32_t* items, int cap) {
-    if (n_blocks == nullptr || chunk == nullptr) return DDT_EINVAL;
+                               int32_t* nsplit, int32_t* items, int cap, int* n_items) {
+    if (n_blocks == nullptr || chunk == nullptr || n_items == nullptr) return DDT_EINVAL;
     const int rc = check_desc(d, prefix_len_host);
     if (rc != DDT_OK) return rc;
     VerifyParams vp{};
@@ -1865,8 +1865,6 @@ extern "C" int ddt_verify_plan(const ddt_attn_desc* d, const int32_t* prefix_len
     *chunk = pl.chunk;
     if (nsplit != nullptr)
         for (int b = 0; b < d->B; ++b) nsplit[b] = vp.nsplit[b];
-    if (items == nullptr) return DDT_OK;
-    if (cap < pl.n_blocks) return DDT_EINVAL;
     // the fields work_item reads besides the plan's (setup_attn sets them for a launch)
     vp.B = d->B;
     vp.H = d->H;
@@ -1875,14 +1873,24 @@ extern "C" int ddt_verify_plan(const ddt_attn_desc* d, const int32_t* prefix_len
     vp.row_tiles = pl.row_tiles;
     vp.chunk = pl.chunk;
     vp.total_wg = pl.total_wg;
+    int n = 0;
     for (int blk = 0; blk < pl.n_blocks; ++blk) {
-        int b = -1, split = -1, rt = -1;
-        if (!work_item(vp, blk, b, split, rt)) b = split = rt = -1;
-        items[3 * blk] = b;
-        items[3 * blk + 1] = split;
-        items[3 * blk + 2] = rt;
+        int b, split, rt;
+        if (!work_item(vp, blk, b, split, rt)) continue;
+        if (items != nullptr && n < cap) {
+            const int64_t T = (int64_t)prefix_len_host[b] + d->N, k0 = (int64_t)split * pl.chunk;
+            int32_t* it = items + 6 * (int64_t)n;
+            it[0] = blk;
+            it[1] = b;
+            it[2] = split;
+            it[3] = rt;
+            it[4] = (int32_t)k0;
+            it[5] = (int32_t)(k0 + pl.chunk < T ? k0 + pl.chunk : T);
+        }
+        ++n;
     }
-    return DDT_OK;
+    *n_items = n;
+    return items != nullptr && cap < n ? DDT_EINVAL : DDT_OK;
 }
 
 extern "C" int ddt_verify_attn(const ddt_attn_desc* d, const void* q_lat, const void* q_pe, const void* ckv,

@@ -63,7 +63,8 @@ def lib():
         L.ddt_status_string.restype = ctypes.c_char_p
         L.ddt_build_mask.argtypes = [P, i32, i32, P, P, P, P]
         L.ddt_verify_workspace.argtypes = [ctypes.POINTER(AttnDesc), P, ctypes.POINTER(sz)]
-        L.ddt_verify_plan.argtypes = [ctypes.POINTER(AttnDesc), P, ctypes.POINTER(i32), ctypes.POINTER(i32), P, P, i32]
+        L.ddt_verify_plan.argtypes = [ctypes.POINTER(AttnDesc), P, ctypes.POINTER(i32), ctypes.POINTER(i32), P, P, i32,
+                                      ctypes.POINTER(i32)]
         L.ddt_verify_attn.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P, P, P, P, sz, P]
         L.ddt_verify_attn_noalloc.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P, P, P, P]
         L.ddt_verify_noalloc_scratch_bytes.argtypes = []
@@ -199,18 +200,19 @@ def verify_workspace_bytes(desc: AttnDesc, prefix_len_host) -> int:
 
 
 def verify_plan(desc: AttnDesc, prefix_len_host):
-    """ddt_verify_plan: (n_blocks, chunk, nsplit [B], items [n_blocks, 3]) of
+    """ddt_verify_plan: (n_blocks, chunk, nsplit [B], items [n_items, 6]) of
     the attention launch for this shape and these host lengths; an item is
-    (request, split, row tile), or (-1, -1, -1) for a padding workgroup."""
+    (workgroup, request, split, row tile, first key, end key)."""
     pl = np.ascontiguousarray(prefix_len_host, dtype=np.int32)
-    nb, ch = ctypes.c_int(0), ctypes.c_int(0)
+    nb, ch, ni = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
     nsplit = np.zeros(desc.B, np.int32)
     _check(lib().ddt_verify_plan(ctypes.byref(desc), pl.ctypes.data, ctypes.byref(nb), ctypes.byref(ch),
-                                 nsplit.ctypes.data, None, 0), "ddt_verify_plan")
-    items = np.zeros((max(nb.value, 1), 3), np.int32)
+                                 nsplit.ctypes.data, None, 0, ctypes.byref(ni)), "ddt_verify_plan")
+    items = np.zeros((max(ni.value, 1), 6), np.int32)
     _check(lib().ddt_verify_plan(ctypes.byref(desc), pl.ctypes.data, ctypes.byref(nb), ctypes.byref(ch),
-                                 nsplit.ctypes.data, items.ctypes.data, items.shape[0]), "ddt_verify_plan")
-    return nb.value, ch.value, nsplit, items[:nb.value]
+                                 nsplit.ctypes.data, items.ctypes.data, items.shape[0], ctypes.byref(ni)),
+           "ddt_verify_plan")
+    return nb.value, ch.value, nsplit, items[:ni.value]
 
 
 def _attn_args(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, H, scale, out, lse, workspace, kv_chunk,

@@ -34,19 +34,27 @@ def check_plan(B, H, N, P, kv_chunk=0):
     assert chunk > 0 and chunk % KT == 0
     if kv_chunk > 0:
         assert chunk == math.ceil(kv_chunk / KT) * KT
-    assert (nsplit == (T + chunk - 1) // chunk).all()
-    real = items[items[:, 0] >= 0]
-    pad = items[items[:, 0] < 0]
-    assert (pad == -1).all()
-    # every (request, split, row tile) exactly once: item k of the launch's
+    blk, b, s, r, k0, k1 = (items[:, i].astype(np.int64) for i in range(6))
+    assert ((blk >= 0) & (blk < nb)).all() and ((b >= 0) & (b < B)).all() and ((r >= 0) & (r < rt_n)).all()
+    assert ((s >= 0) & (s < nsplit[b])).all()
+    # every (request, split, row tile) exactly once: item k of the
     # (request, split, row tile) order is row tile r of split s of request b
     first = np.concatenate([[0], np.cumsum(nsplit.astype(np.int64) * rt_n)])
-    assert ((real[:, 0] < B) & (real[:, 1] >= 0) & (real[:, 1] < nsplit[np.clip(real[:, 0], 0, B - 1)])
-            & (real[:, 2] >= 0) & (real[:, 2] < rt_n)).all()
-    key = first[real[:, 0]] + real[:, 1].astype(np.int64) * rt_n + real[:, 2]
+    key = first[b] + s * rt_n + r
     assert len(key) == first[-1] and (np.sort(key) == np.arange(first[-1])).all()
+    # the splits of a request cut its keys [0, T_b) into consecutive,
+    # non-empty, tile-aligned ranges in split order
+    o = np.argsort(key)
+    kb, ke, bb, ss = k0[o], k1[o], b[o], s[o]
+    assert (kb % KT == 0).all() and (ke > kb).all()
+    assert (kb[ss == 0] == 0).all()
+    nxt = (bb[rt_n:] == bb[:-rt_n]) if len(kb) > rt_n else np.zeros(0, bool)
+    assert (kb[rt_n:][nxt] == ke[:-rt_n][nxt]).all()
+    last = ss == nsplit[bb] - 1
+    assert (ke[last] == T[bb[last]]).all()
+    assert len(blk) == len(np.unique(blk))                            # one work item per workgroup
+    assert (k0 == s * chunk).all() and (k1 == np.minimum((s + 1) * chunk, T[b])).all()
     n = len(key)
-    blk = np.nonzero(items[:, 0] >= 0)[0]
     xcd = blk % XCDS
     if n <= 256:
         # one round: XCD x runs a contiguous range of items in (request, split, row tile) order
@@ -59,9 +67,9 @@ def check_plan(B, H, N, P, kv_chunk=0):
         # a unit (up to 8 row tiles of one split) shares one XCD's L2; at most
         # the last n_units % 8 units are dealt row tile by row tile
         unit_rows = min(UNIT, rt_n)
-        r = real[:, 2].astype(np.int64)
         rr = r if N <= 128 else rt_n - 1 - r          # large trees: the split's row tiles go last first
-        unit = (first[real[:, 0]] // rt_n + real[:, 1]) * rt_n + rr // unit_rows
+        grp = first[b] // rt_n + s
+        unit = grp * rt_n + rr // unit_rows
         spread = {}
         for u, x in zip(unit.tolist(), xcd.tolist()):
             spread.setdefault(u, set()).add(x)
@@ -70,7 +78,6 @@ def check_plan(B, H, N, P, kv_chunk=0):
         # starts in an earlier round of the deal (longest work items first for
         # large trees, whose later rows see more keys)
         pos = blk // XCDS // unit_rows
-        grp = first[real[:, 0]] // rt_n + real[:, 1]
         o = np.lexsort((rr, grp))
         g, p = grp[o], pos[o]
         same = g[1:] == g[:-1]
@@ -121,7 +128,7 @@ def test_paged_plan_equals_contiguous():
         P = rng.integers(0, 100000, B).astype(np.int32)
         a = ddt.verify_plan(desc(B, 8, 64), P)
         b = ddt.verify_plan(desc(B, 8, 64, paged=64), P)
-        assert a[0] == b[0] and a[1] == b[1] and (a[2] == b[2]).all() and (a[3] == b[3]).all()
+        assert a[:2] == b[:2] and (a[2] == b[2]).all() and (a[3] == b[3]).all()
 
 
 def test_plan_validation():
