@@ -191,8 +191,19 @@ def attn_desc(q_lat, q_pe, ckv, kpe, *, B, H, N, scale, kv_chunk=0, pages=None, 
     return d
 
 
+def _host_lengths(prefix_len_host, B: int) -> np.ndarray:
+    """The [B] host committed lengths (or their bounds) as the library reads
+    them: int32, one per request (the library reads exactly B entries)."""
+    a = np.asarray(prefix_len_host)
+    if a.shape != (B,):
+        raise ValueError(f"prefix_len_host must have B = {B} entries, got shape {a.shape}")
+    if a.size and (a.min() < np.iinfo(np.int32).min or a.max() > np.iinfo(np.int32).max):
+        raise ValueError("prefix_len_host values must fit int32")
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
 def verify_workspace_bytes(desc: AttnDesc, prefix_len_host) -> int:
-    pl = np.ascontiguousarray(prefix_len_host, dtype=np.int32)
+    pl = _host_lengths(prefix_len_host, desc.B)
     n = ctypes.c_size_t(0)
     _check(lib().ddt_verify_workspace(ctypes.byref(desc), pl.ctypes.data, ctypes.byref(n)),
            "ddt_verify_workspace")
@@ -203,7 +214,7 @@ def verify_plan(desc: AttnDesc, prefix_len_host):
     """ddt_verify_plan: (n_blocks, chunk, nsplit [B], items [n_items, 6]) of
     the attention launch for this shape and these host lengths; an item is
     (workgroup, request, split, row tile, first key, end key)."""
-    pl = np.ascontiguousarray(prefix_len_host, dtype=np.int32)
+    pl = _host_lengths(prefix_len_host, desc.B)
     nb, ch, ni = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
     nsplit = np.zeros(desc.B, np.int32)
     _check(lib().ddt_verify_plan(ctypes.byref(desc), pl.ctypes.data, ctypes.byref(nb), ctypes.byref(ch),
@@ -229,9 +240,7 @@ def _attn_args(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, H, scale, 
     rows = B * N * H
     if q_lat.shape[0] != rows or q_pe.shape[0] != rows:
         raise ValueError("q rows must be B*N*H")
-    pl = np.ascontiguousarray(prefix_len_host, dtype=np.int32)
-    if pl.shape != (B,):
-        raise ValueError("prefix_len_host must have B entries")
+    pl = _host_lengths(prefix_len_host, B)
     desc = attn_desc(q_lat, q_pe, ckv, kpe, B=B, H=H, N=N, scale=scale, kv_chunk=kv_chunk, pages=pages,
                      prefix_len_dev=prefix_len_dev)
     if out is None:

@@ -133,6 +133,10 @@ def test_paged_plan_equals_contiguous():
 
 def test_plan_validation():
     P = np.array([100, 200], np.int32)
+    with pytest.raises(ValueError):
+        ddt.verify_plan(desc(2, 8, 64), np.array([100], np.int32))        # one length for two requests
+    with pytest.raises(ValueError):
+        ddt.verify_plan(desc(2, 8, 64), np.array([100, 1 << 33], np.int64))  # past int32
     with pytest.raises(ddt.DdtError):
         ddt.verify_plan(desc(2, 8, 2000), P)            # more nodes than the limit
     with pytest.raises(ddt.DdtError):
