@@ -6,7 +6,6 @@ from one array and written to another.  Between replays the program does
 its own eager work (the cache is restored, outputs are poisoned); each
 replay is compared with the eager step bit for bit (the kernels are
 deterministic)."""
-import numpy as np
 import pytest
 import torch
 

@@ -4,7 +4,6 @@ second with a smaller input, each bit-identical to ddt_verify_attn's
 output on the same inputs (same plan, same kernels; the split partials
 live in the library's scratch instead of a workspace) and within the
 oracle's bar; a call whose partials exceed the scratch is refused."""
-import numpy as np
 import pytest
 import torch
 
