@@ -348,38 +348,16 @@ template <>
 __device__ inline void store4<float>(float* dst, const float* v) {
     *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
 }
-// The same with a non-temporal hint: split partials are streamed to memory
-// for the merge launch rather than kept in this XCD's L2 (measured 1.1 us
-// off the attention launch at the K2-like head share).
-template <typename T>
-__device__ inline void store4_nt(T* dst, const float* v);
-template <>
-__device__ inline void store4_nt<uint16_t>(uint16_t* dst, const float* v) {
-    typedef uint32_t U2 __attribute__((ext_vector_type(2)));
-    U2 w;
-    w.x = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
-    w.y = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
-    __builtin_nontemporal_store(w, reinterpret_cast<U2*>(dst));
-}
-template <>
-__device__ inline void store4_nt<float>(float* dst, const float* v) {
+// Four fp32 values with a non-temporal hint: split partials are streamed to
+// memory for the merge launch rather than kept in this XCD's L2 (measured
+// 1.1 us off the attention launch at the K2-like head share).
+__device__ inline void store4_nt_f32(float* dst, const float* v) {
     typedef float F4 __attribute__((ext_vector_type(4)));
     const F4 w = {v[0], v[1], v[2], v[3]};
     __builtin_nontemporal_store(w, reinterpret_cast<F4*>(dst));
 }
-// four consecutive elements widened to fp32
-template <typename T>
-__device__ inline float4 load4(const T* src);
-template <>
-__device__ inline float4 load4<uint16_t>(const uint16_t* src) {
-    const uint2 w = *reinterpret_cast<const uint2*>(src);
-    return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), __uint_as_float(w.y << 16),
-                       __uint_as_float(w.y & 0xffff0000u));
-}
-template <>
-__device__ inline float4 load4<float>(const float* src) {
-    return *reinterpret_cast<const float4*>(src);
-}
+// four consecutive fp32 values
+__device__ inline float4 load4_f32(const float* src) { return *reinterpret_cast<const float4*>(src); }
 
 // Wait until this wavefront's vector-memory loads (the LDS-DMA of later
 // tiles, issued as inline asm the compiler does not count) have landed.
@@ -813,7 +791,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
     const int wrow0 = rt * ROWS_WG + grp * 32;
     const bool active = wrow0 < p.rows;            // the row group has real rows
-    const bool row_ok = wrow0 + l32 < p.rows;
     const int row = min(wrow0 + l32, p.rows - 1);  // padded rows recompute the last row, never stored
     const int64_t qrow = (int64_t)b * p.rows + row;
     // probabilities of tile j for row group grp: pbuf0 + (j & 1) * NGRP * PBUF
@@ -1306,7 +1283,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                     float v[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) v[e] = o[rb][c][v4 * 4 + e];
-                    store4_nt<float>(ws + ((c * 4 + v4) * 64 + lane) * 4, v);
+                    store4_nt_f32(ws + ((c * 4 + v4) * 64 + lane) * 4, v);
                 }
             }
         }
@@ -1371,7 +1348,7 @@ __global__ __launch_bounds__(256) void verify_combine(const VerifyParams p) {
                 if (s0 + k < ns) {  // uniform: no load for the padding
                     const int slot = slot_of(s0 + k);
                     ml[k] = p.ws_ml[(size_t)slot * ROWS_WG + prow];
-                    v[k] = load4<float>(static_cast<const float*>(p.ws_o) + ((size_t)slot * NW + wave) * (NCTW * 4 * 64 * 4) +
+                    v[k] = load4_f32(static_cast<const float*>(p.ws_o) + ((size_t)slot * NW + wave) * (NCTW * 4 * 64 * 4) +
                                     ((c * 4 + grp) * 64 + lane) * 4);
                 }
             }
