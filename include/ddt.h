@@ -369,6 +369,21 @@ int ddt_accept_compact(const int32_t* target_ids, const int32_t* draft_ids, cons
                        const int32_t* prefix_len, int32_t* new_prefix_len, int32_t* src_slot, hipStream_t stream);
 
 /*
+ * ddt_accept_compact on a paged cache, as ddt_compact_kv_paged addresses it
+ * (slot t of request b at pool row block_table[b*bt_ld + t/page_size] *
+ * page_size + t%page_size; page_size a power of two in [1, 65536], bt_ld >=
+ * 1).  A request whose slots P .. P+path[k] run past its table row gets its
+ * acceptance outputs and new_prefix_len = prefix_len, with no rows moved;
+ * the page numbers must name pages inside the pool (not checked).
+ * Otherwise as ddt_accept_compact.
+ */
+int ddt_accept_compact_paged(const int32_t* target_ids, const int32_t* draft_ids, const int32_t* parents, int B,
+                             int N, int32_t* accept_len, int32_t* path, int32_t* tokens, void* ckv, int64_t ld_ckv,
+                             void* kpe, int64_t ld_kpe, int dtype, int d_lat, int d_rope, const int32_t* block_table,
+                             int64_t bt_ld, int page_size, const int32_t* prefix_len, int32_t* new_prefix_len,
+                             int32_t* src_slot, hipStream_t stream);
+
+/*
  * One verify step after the mask: tree-verify attention, target argmax,
  * greedy acceptance and KV compaction with the length update, in two
  * launches.  [Ambition], sections "The Thinking Process", "The Decision

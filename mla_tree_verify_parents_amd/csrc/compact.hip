@@ -107,16 +107,14 @@ extern "C" int ddt_compact_kv_paged(void* ckv, int64_t ld_ckv, void* kpe, int64_
                           path, accept_len, B, N, src_slot, stream);
 }
 
-extern "C" int ddt_accept_compact(const int32_t* target_ids, const int32_t* draft_ids, const int32_t* parents,
-                                  int B, int N, int32_t* accept_len, int32_t* path, int32_t* tokens, void* ckv,
-                                  int64_t ld_ckv, void* kpe, int64_t ld_kpe, int dtype, int d_lat, int d_rope,
-                                  const int64_t* kv_base, const int32_t* prefix_len, int32_t* new_prefix_len,
-                                  int32_t* src_slot, hipStream_t stream) {
-    if (B < 0 || N < 1 || N > DDT_MAX_NODES || d_lat < 1 || d_rope < 0) return DDT_EINVAL;
-    if (dtype != DDT_F32 && dtype != DDT_BF16) return DDT_EUNSUPPORTED;
-    if (B == 0) return DDT_OK;
+// The launch of ddt_accept_compact and ddt_accept_compact_paged after their
+// own argument checks (slots mapped by `map`).
+int launch_accept_compact(const int32_t* target_ids, const int32_t* draft_ids, const int32_t* parents, int B, int N,
+                          int32_t* accept_len, int32_t* path, int32_t* tokens, void* ckv, int64_t ld_ckv, void* kpe,
+                          int64_t ld_kpe, int dtype, int d_lat, int d_rope, const ddt::SlotMap& map,
+                          const int32_t* prefix_len, int32_t* new_prefix_len, int32_t* src_slot, hipStream_t stream) {
     if (!target_ids || !draft_ids || !parents || !accept_len || !path || !tokens) return DDT_EINVAL;
-    if (!ckv || !kv_base || !prefix_len || !new_prefix_len) return DDT_EINVAL;
+    if (!ckv || !prefix_len || !new_prefix_len) return DDT_EINVAL;
     if (d_rope > 0 && !kpe) return DDT_EINVAL;
     if (d_rope == 0) kpe = ckv;
     ddt::CompactLayout lay;
@@ -124,7 +122,7 @@ extern "C" int ddt_accept_compact(const int32_t* target_ids, const int32_t* draf
     if (rc != DDT_OK) return rc;
     ddt::AcceptCompactArgs a{target_ids, draft_ids, parents, N, accept_len, path, tokens, (char*)ckv, (char*)kpe,
                              lay.lc, lay.lk, lay.ckv_units, lay.kpe_units, lay.rows_per_block,
-                             ddt::SlotMap{kv_base, nullptr, 0, 0}, prefix_len, new_prefix_len, src_slot};
+                             map, prefix_len, new_prefix_len, src_slot};
     if (lay.vec16)
         hipLaunchKernelGGL(accept_compact_kernel<uint4>, dim3(B), dim3(ddt::kCompactThreads), lay.stage_bytes,
                            stream, a);
@@ -133,4 +131,35 @@ extern "C" int ddt_accept_compact(const int32_t* target_ids, const int32_t* draf
                            stream, a);
     DDT_CHECK_LAUNCH();
     return DDT_OK;
+}
+
+extern "C" int ddt_accept_compact(const int32_t* target_ids, const int32_t* draft_ids, const int32_t* parents,
+                                  int B, int N, int32_t* accept_len, int32_t* path, int32_t* tokens, void* ckv,
+                                  int64_t ld_ckv, void* kpe, int64_t ld_kpe, int dtype, int d_lat, int d_rope,
+                                  const int64_t* kv_base, const int32_t* prefix_len, int32_t* new_prefix_len,
+                                  int32_t* src_slot, hipStream_t stream) {
+    if (B < 0 || N < 1 || N > DDT_MAX_NODES || d_lat < 1 || d_rope < 0) return DDT_EINVAL;
+    if (dtype != DDT_F32 && dtype != DDT_BF16) return DDT_EUNSUPPORTED;
+    if (B == 0) return DDT_OK;
+    if (!kv_base) return DDT_EINVAL;
+    return launch_accept_compact(target_ids, draft_ids, parents, B, N, accept_len, path, tokens, ckv, ld_ckv, kpe,
+                                 ld_kpe, dtype, d_lat, d_rope, ddt::SlotMap{kv_base, nullptr, 0, 0}, prefix_len,
+                                 new_prefix_len, src_slot, stream);
+}
+
+extern "C" int ddt_accept_compact_paged(const int32_t* target_ids, const int32_t* draft_ids, const int32_t* parents,
+                                        int B, int N, int32_t* accept_len, int32_t* path, int32_t* tokens, void* ckv,
+                                        int64_t ld_ckv, void* kpe, int64_t ld_kpe, int dtype, int d_lat, int d_rope,
+                                        const int32_t* block_table, int64_t bt_ld, int page_size,
+                                        const int32_t* prefix_len, int32_t* new_prefix_len, int32_t* src_slot,
+                                        hipStream_t stream) {
+    if (B < 0 || N < 1 || N > DDT_MAX_NODES || d_lat < 1 || d_rope < 0) return DDT_EINVAL;
+    if (dtype != DDT_F32 && dtype != DDT_BF16) return DDT_EUNSUPPORTED;
+    if (page_size < 1 || page_size > (1 << 16) || (page_size & (page_size - 1)) != 0 || bt_ld < 1) return DDT_EINVAL;
+    if (B == 0) return DDT_OK;
+    if (!block_table) return DDT_EINVAL;
+    return launch_accept_compact(target_ids, draft_ids, parents, B, N, accept_len, path, tokens, ckv, ld_ckv, kpe,
+                                 ld_kpe, dtype, d_lat, d_rope,
+                                 ddt::SlotMap{nullptr, block_table, bt_ld, __builtin_ctz((unsigned)page_size)},
+                                 prefix_len, new_prefix_len, src_slot, stream);
 }

@@ -75,6 +75,8 @@ def lib():
         L.ddt_compact_kv.argtypes = [P, i64, P, i64, i32, i32, i32, P, P, P, P, i32, i32, P, P]
         L.ddt_compact_kv_paged.argtypes = [P, i64, P, i64, i32, i32, i32, P, i64, i32, P, P, P, i32, i32, P, P]
         L.ddt_accept_compact.argtypes = [P, P, P, i32, i32, P, P, P, P, i64, P, i64, i32, i32, i32, P, P, P, P, P]
+        L.ddt_accept_compact_paged.argtypes = [P, P, P, i32, i32, P, P, P, P, i64, P, i64, i32, i32, i32, P, i64, i32,
+                                               P, P, P, P]
         L.ddt_verify_attn_argmax.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P, P, P, P, sz,
                                              ctypes.POINTER(ArgmaxTask), P]
         L.ddt_verify_step.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P, P, P, P, sz,
@@ -90,7 +92,7 @@ def lib():
         for f in ("ddt_version", "ddt_build_mask", "ddt_verify_workspace", "ddt_verify_plan", "ddt_verify_attn",
                   "ddt_verify_attn_noalloc",
                   "ddt_argmax_workspace", "ddt_argmax", "ddt_greedy_accept", "ddt_compact_kv", "ddt_compact_kv_paged",
-                  "ddt_accept_compact", "ddt_verify_attn_argmax", "ddt_verify_step",
+                  "ddt_accept_compact", "ddt_accept_compact_paged", "ddt_verify_attn_argmax", "ddt_verify_step",
                   "ddt_draft_topk_workspace", "ddt_draft_topk", "ddt_best_first_tree",
                   "ddt_proj_pack_weight", "ddt_head_proj",
                   "ddt_probe_mfma_bf16", "ddt_probe_read", "ddt_probe_copy"):
@@ -447,15 +449,18 @@ def compact_kv(ckv, kpe, kv_base, prefix_len, path, accept_len, src_slot=None, p
 
 
 def accept_compact(target_ids, draft_ids, parents, ckv, kpe, kv_base, prefix_len, accept_len=None, path=None,
-                   tokens=None, src_slot=None, new_prefix_len=None, stream=None):
+                   tokens=None, src_slot=None, new_prefix_len=None, pages=None, stream=None):
     """greedy_accept + compact_kv in one launch -> (accept_len, path, tokens).
 
-    The advanced lengths go to new_prefix_len (default: prefix_len, in place)."""
+    The advanced lengths go to new_prefix_len (default: prefix_len, in place).
+    pages: None (contiguous from kv_base) or (block_table [B, bt_ld] int32,
+    page_size); kv_base is then unused (may be None)."""
     for t, n in ((target_ids, "target_ids"), (draft_ids, "draft_ids"), (parents, "parents")):
         _contig(t, torch.int32, n)
     _dev(ckv, None, "ckv")
     _dev(kpe, ckv.dtype, "kpe")
-    _contig(kv_base, torch.int64, "kv_base")
+    if pages is None:
+        _contig(kv_base, torch.int64, "kv_base")
     _contig(prefix_len, torch.int32, "prefix_len")
     if new_prefix_len is None:
         new_prefix_len = prefix_len
@@ -463,6 +468,18 @@ def accept_compact(target_ids, draft_ids, parents, ckv, kpe, kv_base, prefix_len
     B, N = parents.shape
     accept_len, path, tokens = _accept_outputs(parents, accept_len, path, tokens)
     _src_slot(src_slot, B, N)
+    if pages is not None:
+        table, page_size = pages
+        _contig(table, torch.int32, "block_table")
+        if table.dim() != 2 or table.shape[0] != B:
+            raise ValueError("block_table must be [B, bt_ld]")
+        _check(lib().ddt_accept_compact_paged(_p(target_ids), _p(draft_ids), _p(parents), B, N, _p(accept_len),
+                                              _p(path), _p(tokens), _p(ckv), _rows(ckv, "ckv"), _p(kpe),
+                                              _rows(kpe, "kpe"), _dtype_code(ckv), ckv.shape[1], kpe.shape[1],
+                                              _p(table), table.shape[1], int(page_size), _p(prefix_len),
+                                              _p(new_prefix_len), _p(src_slot), _stream(stream)),
+               "ddt_accept_compact_paged")
+        return accept_len, path, tokens
     _check(lib().ddt_accept_compact(_p(target_ids), _p(draft_ids), _p(parents), B, N, _p(accept_len), _p(path),
                                     _p(tokens), _p(ckv), _rows(ckv, "ckv"), _p(kpe), _rows(kpe, "kpe"),
                                     _dtype_code(ckv), ckv.shape[1], kpe.shape[1], _p(kv_base), _p(prefix_len),

@@ -184,6 +184,14 @@ def test_compact_paged_validation(lib):
     assert lib.ddt_compact_kv_paged(*args(64, 0)) == -1           # bt_ld < 1
     assert lib.ddt_compact_kv_paged(*args(64, 10, table=null)) == -1
     assert lib.ddt_compact_kv_paged(*args(64, 10, B=0)) == 0       # nothing to do
+    # acceptance + compaction on a paged cache: the same table checks
+    acp = lambda ps, bt_ld, B=1, table=f, N=8: (f, f, f, B, N, f, f, f, f, 576, f, 576, 1, 512, 64, table, bt_ld, ps,
+                                                 f, f, null, null)
+    assert lib.ddt_accept_compact_paged(*acp(48, 10)) == -1
+    assert lib.ddt_accept_compact_paged(*acp(64, 0)) == -1
+    assert lib.ddt_accept_compact_paged(*acp(64, 10, table=null)) == -1
+    assert lib.ddt_accept_compact_paged(*acp(64, 10, N=0)) == -1
+    assert lib.ddt_accept_compact_paged(*acp(64, 10, B=0)) == 0
 
 
 def test_proj_validation(lib):

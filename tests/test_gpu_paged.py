@@ -325,3 +325,76 @@ def test_paged_verify_step_unmappable_length(orc):
     assert (from_paged(got_phys, table, ps, w).view(np.uint8) == opool.view(np.uint8)).all()
     sp = slice(spare * ps, (spare + 1) * ps)
     assert (got_phys[sp].view(np.uint8) == phys[sp].view(np.uint8)).all()
+
+
+@pytest.mark.parametrize("ps,cfg", [(1, 3), (32, 1), (128, 3)])
+def test_paged_accept_compact(orc, ps, cfg):
+    """Acceptance and compaction in one launch through a block table
+    (ddt_accept_compact_paged): acceptance outputs, advanced lengths and
+    source slots bit-exact against the oracle's acceptance and compaction of
+    the logical cache, the compacted rows bit for bit, rows no table entry
+    names untouched, and the committed lengths left as they were."""
+    w = synth.workload(3, B=6, prefix_range=(0, 900)) if cfg == 3 else synth.workload(1, B=6, N=8, prefix=45)
+    rng = np.random.default_rng(31 + ps)
+    B, N, dl = w.B, w.N, w.d_lat
+    w.draft_ids = w.draft_ids % 50
+    t = synth.planted_targets(rng, w.parents, w.draft_ids, 50, 0.85)
+    oa, op, ot = orc.greedy_accept(t, w.draft_ids, w.parents)
+    phys, table = to_paged(w, ps, rng)
+    opool = w.pool.copy()
+    opl, osrc = orc.compact_kv(opool[:, :dl], opool[:, dl:], w.kv_base, w.prefix_len, op, oa)
+
+    pd, td = to_dev(phys), to_dev(table)
+    dpl = to_dev(w.prefix_len)
+    npl = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    src = torch.empty((B, N), dtype=torch.int32, device="cuda")
+    acc, path, tok = ddt.accept_compact(to_dev(t), to_dev(w.draft_ids), to_dev(w.parents), pd[:, :dl], pd[:, dl:],
+                                        None, dpl, src_slot=src, new_prefix_len=npl, pages=(td, ps))
+    torch.cuda.synchronize()
+    assert (to_host(acc) == oa).all() and (to_host(path) == op).all() and (to_host(tok) == ot).all()
+    assert (to_host(npl) == opl).all() and (to_host(src) == osrc).all()
+    assert (to_host(dpl) == w.prefix_len).all()
+    got_phys = np.ascontiguousarray(to_host(pd))
+    assert (from_paged(got_phys, table, ps, w).view(np.uint8) == opool.view(np.uint8)).all()
+    named = np.zeros(got_phys.shape[0], bool)
+    for b in range(B):
+        tt = np.arange(int(w.prefix_len[b]) + N)
+        named[table[b, tt // ps].astype(np.int64) * ps + tt % ps] = True
+    assert (got_phys[~named].view(np.uint8) == phys[~named].view(np.uint8)).all()
+
+
+def test_paged_accept_compact_unmappable_left_untouched(orc):
+    """ddt_accept_compact_paged with committed lengths whose accepted slots
+    run past the request's table row: those requests still get their
+    acceptance outputs, with new length = old length, src_slot -1 and no
+    row written; the others are compacted as the oracle does."""
+    w = synth.workload(3, B=3, N=8, prefix_range=(40, 90))
+    ps, B, N, dl = 32, 3, 8, 512
+    rng = np.random.default_rng(13)
+    w.draft_ids = w.draft_ids % 20
+    t = synth.planted_targets(rng, w.parents, w.draft_ids, 20, 0.9)
+    oa, op, ot = orc.greedy_accept(t, w.draft_ids, w.parents)
+    phys, table = to_paged(w, ps, rng, spare=2)
+    spare = _spare_page(table, w, ps, phys.shape[0] // ps)
+    L = table.shape[1]
+    P_dev = w.prefix_len.copy()
+    P_dev[1] = L * ps - 1                               # the path's slots run past row 1 (unless only the root)
+    P_dev[2] = L * ps + 5                               # past the table itself
+    mappable = [0] + [b for b in (1, 2) if int(P_dev[b]) + int(op[b, oa[b]]) < L * ps]
+    opool = w.pool.copy()
+    opl, osrc = _oracle_compact_some(orc, opool, dl, w.kv_base, w.prefix_len, op, oa, [0])
+    opl[1:], osrc[1:] = P_dev[1:], -1
+    pd = to_dev(phys)
+    _, td = _padded_table(table, 2, spare)
+    npl = torch.empty((B,), dtype=torch.int32, device="cuda")
+    src = torch.empty((B, N), dtype=torch.int32, device="cuda")
+    acc, path, tok = ddt.accept_compact(to_dev(t), to_dev(w.draft_ids), to_dev(w.parents), pd[:, :dl], pd[:, dl:],
+                                        None, to_dev(P_dev), src_slot=src, new_prefix_len=npl, pages=(td, ps))
+    torch.cuda.synchronize()
+    assert mappable == [0], mappable                   # the case exercises two unmappable requests
+    assert (to_host(acc) == oa).all() and (to_host(path) == op).all() and (to_host(tok) == ot).all()
+    assert (to_host(npl) == opl).all() and (to_host(src) == osrc).all()
+    got_phys = np.ascontiguousarray(to_host(pd))
+    assert (from_paged(got_phys, table, ps, w).view(np.uint8) == opool.view(np.uint8)).all()
+    sp = slice(spare * ps, (spare + 1) * ps)
+    assert (got_phys[sp].view(np.uint8) == phys[sp].view(np.uint8)).all()
