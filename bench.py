@@ -597,6 +597,31 @@ def run_loop(args, dev, W, K, brief=False):
     attn_ms, attn_units = time_windows(gn.replay, per, est, stream)
     ms_attn = float(np.median(attn_ms))
     del g1, gn
+    # the whole verify step on the same inputs, back to back: the loop's own
+    # iterations leave the GPU idle while the host draws the next inputs, and
+    # the clock is lower after such gaps, so this is the step at a steady clock
+    # (committed lengths read from a copy, advanced lengths to another: every
+    # replay is the same step)
+    p_before = torch.from_numpy(inp.prefix_len.astype(np.int32)).to(dev)
+    p_after = torch.empty_like(p_before)
+
+    def step():
+        ddt.verify_step(inp.q[:, :dl], inp.q[:, dl:], loop.ckv(), loop.kpe(),
+                        None if loop.page_size else loop.kv_base, inp.prefix_len, mask if loop.N > 128 else None,
+                        inp.logits, inp.draft_dev, inp.parents_dev, p_before, H=loop.H, scale=loop.scale,
+                        new_prefix_len=p_after, out=loop.out, lse=loop.lse, workspace=ws, idx=loop.idx,
+                        argmax_workspace=loop.am_ws, accept_len=loop.acc, path=loop.path, tokens=loop.tok,
+                        pages=loop.pages())
+
+    step()
+    torch.cuda.synchronize()
+    g1 = graph_of(step, 1)
+    est = estimate_ms(g1.replay, 1, stream)
+    per = max(1, min(100, int(WINDOW_MS / max(est, 1e-4))))
+    gn = graph_of(step, per)
+    gn.replay()
+    step_ms, step_units = time_windows(gn.replay, per, est, stream)
+    del g1, gn
     last_flops = inp.visible_pairs(loop.H) * FLOP_PER_PAIR
     achieved = last_flops / (ms_attn * 1e-3) / 1e12
     last_keys = int(inp.prefix_len.sum()) + loop.B * loop.N
@@ -638,6 +663,11 @@ def run_loop(args, dev, W, K, brief=False):
         "stage_ms_per_iteration": {"draft_topk_and_trees": round(draft_ms / K, 5),
                                    "verify_step": round(verify_ms / K, 5),
                                    "note": "device time; ms_per_step is their sum"},
+        "verify_step_steady": {"ms": round(float(np.median(step_ms)), 5), "ms_spread": spread(step_ms),
+                               "steps_per_window": step_units,
+                               "note": "ddt_verify_step on the last iteration's inputs, back-to-back graph "
+                                       "replays (median of 5 windows of >= 50 ms): the step at a steady clock, "
+                                       "without the idle gaps the loop's host-side input drawing leaves"},
         "host_ms_per_iteration": {"inputs_and_trees": round(host_s * 1e3 / K, 3),
                                   "plan_and_enqueue": round(plan_s * 1e3 / K, 3),
                                   "note": "host wall time: drawing the inputs and running the draft stage (with "

@@ -3,7 +3,11 @@
 This module only draws inputs: random latents and queries, draft trees and
 target tokens.  It holds none of the arithmetic of the verify step (no mask,
 attention, argmax, acceptance or compaction) and is the only code that both
-the HIP path's tests and the oracle consume.
+the HIP path's tests and the oracle consume.  One step before the verify
+path does live here: `best_first_tree` grows the input trees of the
+best-first configurations.  It is input generation only; the device builder
+(ddt_best_first_tree) is checked against the oracle's own builder, never
+against this one.
 
 Shapes follow the Kimi-K2 style MLA attention the pages target: a latent
 cache row is c_kv (kv_lora_rank wide) followed by the decoupled rope key
