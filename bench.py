@@ -22,8 +22,9 @@ the attention launch against the bf16 MFMA peak; `hbm_stages` the HBM scans
 of the end-to-end step (argmax over 2048 x 163840 fp32 target logits, draft
 top-8 over 256 x 163840) against 8 TB/s; `cpu_baseline` times the fp64
 oracle on the host for a sample of the same workload.  The default run
-also reports the K2-like head share's step and a short verify loop as
-extra keys (`config2`, `config5_loop`).
+also reports the K2-like head share's step, the batched ragged step and a
+short verify loop (with its last step replayed at a steady clock) as extra
+keys (`config2`, `config3`, `config5_loop`).
 
 `--traffic-probe` runs a few attention launches of the workload and one
 device-to-device copy of known size, and exits: it is the program that the
@@ -174,7 +175,7 @@ def estimate_ms(replay, units, stream, reps=3):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build's verify path runs on a single GPU and has no "
+        print(f"bench.py measures one GPU only: the verify path here runs on a single GPU and has no "
               f"multi-GPU part (got --gpus {args.gpus})", file=sys.stderr)
         sys.exit(2)
     import torch
