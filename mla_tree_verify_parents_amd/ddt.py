@@ -130,6 +130,13 @@ def _contig(t, dtype, name):
     return t
 
 
+def _holds(t, n, name):
+    """A contiguous tensor the library reads or writes n consecutive elements of."""
+    if t.numel() < n:
+        raise ValueError(f"{name} must hold at least {n} elements, got {t.numel()}")
+    return t
+
+
 def _src_slot(src_slot, B, N):
     """The optional [B, N] int32 src_slot output: the library writes B*N entries."""
     if src_slot is not None:
@@ -157,6 +164,8 @@ def _dtype_code(t):
 def build_mask(parents, mask=None, depth=None, tree_err=None, stream=None):
     """parents [B, N] int32 -> (mask [B, N, W] int64 bit words, depth [B, N], tree_err [B])."""
     _contig(parents, torch.int32, "parents")
+    if parents.dim() != 2:
+        raise ValueError("parents must be [B, N]")
     B, N = parents.shape
     W = (N + 63) // 64
     dev = parents.device
@@ -166,6 +175,9 @@ def build_mask(parents, mask=None, depth=None, tree_err=None, stream=None):
         depth = torch.empty((B, N), dtype=torch.int32, device=dev)
     if tree_err is None:
         tree_err = torch.empty((B,), dtype=torch.int32, device=dev)
+    _holds(_contig(mask, torch.int64, "mask"), B * N * W, "mask")
+    _holds(_contig(depth, torch.int32, "depth"), B * N, "depth")
+    _holds(_contig(tree_err, torch.int32, "tree_err"), B, "tree_err")
     _check(lib().ddt_build_mask(_p(parents), B, N, _p(mask), _p(depth), _p(tree_err), _stream(stream)),
            "ddt_build_mask")
     return mask, depth, tree_err
@@ -238,7 +250,11 @@ def _attn_args(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, H, scale, 
         B, N = BN
     else:
         _contig(mask, torch.int64, "mask")
+        if mask.dim() != 3 or mask.shape[2] != (mask.shape[1] + 63) // 64:
+            raise ValueError("mask must be [B, N, ceil(N/64)] (from build_mask)")
         B, N = mask.shape[0], mask.shape[1]
+    if kv_base is not None:
+        _holds(kv_base, B, "kv_base")
     rows = B * N * H
     if q_lat.shape[0] != rows or q_pe.shape[0] != rows:
         raise ValueError("q rows must be B*N*H")
@@ -249,8 +265,8 @@ def _attn_args(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, H, scale, 
         out = torch.empty((rows, q_lat.shape[1]), dtype=q_lat.dtype, device=q_lat.device)
     if lse is None:
         lse = torch.empty((rows,), dtype=torch.float32, device=q_lat.device)
-    _contig(out, q_lat.dtype, "out")
-    _contig(lse, torch.float32, "lse")
+    _holds(_contig(out, q_lat.dtype, "out"), rows * q_lat.shape[1], "out")
+    _holds(_contig(lse, torch.float32, "lse"), rows, "lse")
     if workspace is None and alloc_workspace:  # (a caller's workspace is checked by the library)
         need = verify_workspace_bytes(desc, pl)
         if need > 0:
@@ -302,7 +318,7 @@ def _argmax_task(logits, idx, argmax_workspace):
     rows, V = logits.shape
     if idx is None:
         idx = torch.empty((rows,), dtype=torch.int32, device=logits.device)
-    _contig(idx, torch.int32, "idx")
+    _holds(_contig(idx, torch.int32, "idx"), rows, "idx")
     need = argmax_workspace_bytes(rows, V)
     if argmax_workspace is None and need > 0:
         argmax_workspace = torch.zeros((need,), dtype=torch.uint8, device=logits.device)  # zero before first use
@@ -335,7 +351,24 @@ def _accept_outputs(parents, accept_len, path, tokens):
         tokens = torch.empty((B, N), dtype=torch.int32, device=dev)
     for t, n in ((accept_len, "accept_len"), (path, "path"), (tokens, "tokens")):
         _contig(t, torch.int32, n)
+    _holds(accept_len, B, "accept_len")
+    for t, n in ((path, "path"), (tokens, "tokens")):
+        if tuple(t.shape) != (B, N):
+            raise ValueError(f"{n} must be [B, N] = [{B}, {N}], got {tuple(t.shape)}")
     return accept_len, path, tokens
+
+
+def _tree_inputs(parents, named):
+    """parents [B, N] int32 and per-node int32 inputs of B*N entries each."""
+    _contig(parents, torch.int32, "parents")
+    if parents.dim() != 2:
+        raise ValueError("parents must be [B, N]")
+    B, N = parents.shape
+    for t, n in named:
+        _contig(t, torch.int32, n)
+        if t.numel() != B * N:
+            raise ValueError(f"{n} must hold B*N = {B * N} entries (one per tree node), got {t.numel()}")
+    return B, N
 
 
 def verify_step(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, logits, draft_ids, parents, prefix_len, *,
@@ -363,9 +396,10 @@ def verify_step(q_lat, q_pe, ckv, kpe, kv_base, prefix_len_host, mask, logits, d
         _contig(t, torch.int32, n)
     if tuple(parents.shape) != (desc.B, desc.N) or tuple(draft_ids.shape) != (desc.B, desc.N):
         raise ValueError("draft_ids and parents must be [B, N]")
+    _holds(prefix_len, desc.B, "prefix_len")
     if new_prefix_len is None:
         new_prefix_len = prefix_len
-    _contig(new_prefix_len, torch.int32, "new_prefix_len")
+    _holds(_contig(new_prefix_len, torch.int32, "new_prefix_len"), desc.B, "new_prefix_len")
     accept_len, path, tokens = _accept_outputs(parents, accept_len, path, tokens)
     _src_slot(src_slot, desc.B, desc.N)
     acc = AcceptTask(_p(draft_ids), _p(parents), _p(accept_len), _p(path), _p(tokens), _p(prefix_len),
@@ -393,7 +427,7 @@ def argmax(logits, idx=None, workspace=None, stream=None):
     rows, V = logits.shape
     if idx is None:
         idx = torch.empty((rows,), dtype=torch.int32, device=logits.device)
-    _contig(idx, torch.int32, "idx")
+    _holds(_contig(idx, torch.int32, "idx"), rows, "idx")
     need = argmax_workspace_bytes(rows, V)
     if workspace is None and need > 0:
         workspace = torch.zeros((need,), dtype=torch.uint8, device=logits.device)  # zero before first use
@@ -405,16 +439,8 @@ def argmax(logits, idx=None, workspace=None, stream=None):
 
 def greedy_accept(target_ids, draft_ids, parents, accept_len=None, path=None, tokens=None, stream=None):
     """-> (accept_len [B], path [B, N], tokens [B, N]) int32 device tensors."""
-    for t, n in ((target_ids, "target_ids"), (draft_ids, "draft_ids"), (parents, "parents")):
-        _contig(t, torch.int32, n)
-    B, N = parents.shape
-    dev = parents.device
-    if accept_len is None:
-        accept_len = torch.empty((B,), dtype=torch.int32, device=dev)
-    if path is None:
-        path = torch.empty((B, N), dtype=torch.int32, device=dev)
-    if tokens is None:
-        tokens = torch.empty((B, N), dtype=torch.int32, device=dev)
+    B, N = _tree_inputs(parents, ((target_ids, "target_ids"), (draft_ids, "draft_ids")))
+    accept_len, path, tokens = _accept_outputs(parents, accept_len, path, tokens)
     _check(lib().ddt_greedy_accept(_p(target_ids), _p(draft_ids), _p(parents), B, N, _p(accept_len), _p(path),
                                    _p(tokens), _stream(stream)), "ddt_greedy_accept")
     return accept_len, path, tokens
@@ -426,10 +452,12 @@ def compact_kv(ckv, kpe, kv_base, prefix_len, path, accept_len, src_slot=None, p
     is then unused (may be None)."""
     _dev(ckv, None, "ckv")
     _dev(kpe, ckv.dtype, "kpe")
-    _contig(prefix_len, torch.int32, "prefix_len")
     _contig(path, torch.int32, "path")
-    _contig(accept_len, torch.int32, "accept_len")
+    if path.dim() != 2:
+        raise ValueError("path must be [B, N]")
     B, N = path.shape
+    _holds(_contig(prefix_len, torch.int32, "prefix_len"), B, "prefix_len")
+    _holds(_contig(accept_len, torch.int32, "accept_len"), B, "accept_len")
     _src_slot(src_slot, B, N)
     if pages is not None:
         table, page_size = pages
@@ -441,7 +469,7 @@ def compact_kv(ckv, kpe, kv_base, prefix_len, path, accept_len, src_slot=None, p
                                           _p(prefix_len), _p(path), _p(accept_len), B, N, _p(src_slot),
                                           _stream(stream)), "ddt_compact_kv_paged")
         return prefix_len, src_slot
-    _contig(kv_base, torch.int64, "kv_base")
+    _holds(_contig(kv_base, torch.int64, "kv_base"), B, "kv_base")
     _check(lib().ddt_compact_kv(_p(ckv), _rows(ckv, "ckv"), _p(kpe), _rows(kpe, "kpe"), _dtype_code(ckv),
                                 ckv.shape[1], kpe.shape[1], _p(kv_base), _p(prefix_len), _p(path),
                                 _p(accept_len), B, N, _p(src_slot), _stream(stream)), "ddt_compact_kv")
@@ -455,17 +483,15 @@ def accept_compact(target_ids, draft_ids, parents, ckv, kpe, kv_base, prefix_len
     The advanced lengths go to new_prefix_len (default: prefix_len, in place).
     pages: None (contiguous from kv_base) or (block_table [B, bt_ld] int32,
     page_size); kv_base is then unused (may be None)."""
-    for t, n in ((target_ids, "target_ids"), (draft_ids, "draft_ids"), (parents, "parents")):
-        _contig(t, torch.int32, n)
+    B, N = _tree_inputs(parents, ((target_ids, "target_ids"), (draft_ids, "draft_ids")))
     _dev(ckv, None, "ckv")
     _dev(kpe, ckv.dtype, "kpe")
     if pages is None:
-        _contig(kv_base, torch.int64, "kv_base")
-    _contig(prefix_len, torch.int32, "prefix_len")
+        _holds(_contig(kv_base, torch.int64, "kv_base"), B, "kv_base")
+    _holds(_contig(prefix_len, torch.int32, "prefix_len"), B, "prefix_len")
     if new_prefix_len is None:
         new_prefix_len = prefix_len
-    _contig(new_prefix_len, torch.int32, "new_prefix_len")
-    B, N = parents.shape
+    _holds(_contig(new_prefix_len, torch.int32, "new_prefix_len"), B, "new_prefix_len")
     accept_len, path, tokens = _accept_outputs(parents, accept_len, path, tokens)
     _src_slot(src_slot, B, N)
     if pages is not None:
@@ -503,8 +529,8 @@ def draft_topk(logits, K, ids=None, logp=None, workspace=None, stream=None):
         ids = torch.empty((rows, K), dtype=torch.int32, device=dev)
     if logp is None:
         logp = torch.empty((rows, K), dtype=torch.float32, device=dev)
-    _contig(ids, torch.int32, "ids")
-    _contig(logp, torch.float32, "logp")
+    _holds(_contig(ids, torch.int32, "ids"), rows * K, "ids")
+    _holds(_contig(logp, torch.float32, "logp"), rows * K, "logp")
     if workspace is None:
         workspace = torch.empty((max(16, draft_topk_workspace_bytes(rows, V, K)),), dtype=torch.uint8, device=dev)
     ws_n = workspace.numel() * workspace.element_size()
@@ -527,7 +553,7 @@ def best_first_tree(ids, logp, root_tokens, budget, parents=None, tokens=None, d
     for t, n in ((parents, "parents"), (tokens, "tokens"), (depth, "depth")):
         if t is None:
             t = torch.empty((B, budget + 1), dtype=torch.int32, device=dev)
-        _contig(t, torch.int32, n)
+        _holds(_contig(t, torch.int32, n), B * (budget + 1), n)
         outs.append(t)
     _check(lib().ddt_best_first_tree(_p(ids), _p(logp), B, D, K, budget, _p(root_tokens), _p(outs[0]), _p(outs[1]),
                                      _p(outs[2]), _stream(stream)), "ddt_best_first_tree")
