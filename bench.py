@@ -385,7 +385,8 @@ def measure_config(cfg, args, dev, headline):
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": recorded_traffic(cfg),
                      "algorithmic_flop_per_launch": flops, "algorithmic_bytes": attn_bytes,
-                     "achieved_GBps": round(attn_bytes / (ms_attn * 1e-3) / 1e9, 1)},
+                     "achieved_GBps": round(attn_bytes / (ms_attn * 1e-3) / 1e9, 1),
+                     "achieved_hbm_frac": round(attn_bytes / (ms_attn * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
     }
     if spg > 1:
         res["step_timing"]["one_step_graphs_ms_per_step"] = spread(one_ms)
@@ -659,7 +660,8 @@ def run_loop(args, dev, W, K, brief=False):
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": recorded_traffic(5),
                      "algorithmic_flop_per_launch": last_flops, "algorithmic_bytes": attn_bytes,
-                     "achieved_GBps": round(attn_bytes / (ms_attn * 1e-3) / 1e9, 1)},
+                     "achieved_GBps": round(attn_bytes / (ms_attn * 1e-3) / 1e9, 1),
+                     "achieved_hbm_frac": round(attn_bytes / (ms_attn * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
         "draft_step": draft,
         "stage_ms_per_iteration": {"draft_topk_and_trees": round(draft_ms / K, 5),
                                    "verify_step": round(verify_ms / K, 5),
