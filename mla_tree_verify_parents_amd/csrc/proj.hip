@@ -98,21 +98,46 @@ __global__ __launch_bounds__(kThreads) void proj_kernel(const uint16_t* __restri
     const int t0 = tt * kRows;
 
     // the B fragments of the first KP k-steps load before the input tile, so
-    // their (L2) latency overlaps the tile's
+    // their (L2) latency overlaps the tile's.  The deepest reduction (K =
+    // 512: 64 KB of input per workgroup, two workgroups per CU) prefetches
+    // every fragment and puts all of a thread's tile loads in flight before
+    // its first LDS write: measured 13.3 -> 11.6 us at 512 tokens x 64 heads
+    // and 7.3 -> 6.3 us at 2048 x 8.  At K = 128 the same took more
+    // registers and fewer workgroups per CU, 3 % slower, so the shallower
+    // reductions keep eight fragments ahead and a load-store loop.
+    constexpr bool kBurst = K >= 512;
     const int nb = cb * (kCols / 32) + wave;  // this wavefront's 32-column tile
     const bool has_cols = nb * 32 < n_out;
     const bf16x8* wf = wp + ((int64_t)(h * (n_out / 32) + (has_cols ? nb : 0)) * KS) * 64 + lane;
-    constexpr int KP = KS < 8 ? KS : 8;
+    constexpr int KP = kBurst ? KS : (KS < 8 ? KS : 8);
     bf16x8 bpre[KP];
 #pragma unroll
     for (int ks = 0; ks < KP; ++ks) bpre[ks] = wf[ks * 64];
     // input tile: rows t0..t0+63 of head h, zero past M
-    for (int c = tid; c < kRows * XCH; c += kThreads) {
-        const int row = c / XCH, ch = c % XCH;
-        const int t = t0 + row;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (t < M) v = *reinterpret_cast<const u32x4*>(x + ((int64_t)t * H + h) * ld_x + ch * 8);
-        *reinterpret_cast<u32x4*>(smem + row * XROW + ch * 16) = v;
+    if constexpr (kBurst) {
+        constexpr int XU = kRows * XCH / kThreads;  // 16-byte chunks per thread
+        static_assert((kRows * XCH) % kThreads == 0, "whole chunks per thread");
+        u32x4 xv[XU];
+#pragma unroll
+        for (int u = 0; u < XU; ++u) {
+            const int c = tid + u * kThreads, row = c / XCH, ch = c % XCH;
+            const int t = t0 + row;
+            xv[u] = u32x4{0u, 0u, 0u, 0u};
+            if (t < M) xv[u] = *reinterpret_cast<const u32x4*>(x + ((int64_t)t * H + h) * ld_x + ch * 8);
+        }
+#pragma unroll
+        for (int u = 0; u < XU; ++u) {
+            const int c = tid + u * kThreads, row = c / XCH, ch = c % XCH;
+            *reinterpret_cast<u32x4*>(smem + row * XROW + ch * 16) = xv[u];
+        }
+    } else {
+        for (int c = tid; c < kRows * XCH; c += kThreads) {
+            const int row = c / XCH, ch = c % XCH;
+            const int t = t0 + row;
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (t < M) v = *reinterpret_cast<const u32x4*>(x + ((int64_t)t * H + h) * ld_x + ch * 8);
+            *reinterpret_cast<u32x4*>(smem + row * XROW + ch * 16) = v;
+        }
     }
     __syncthreads();
 
