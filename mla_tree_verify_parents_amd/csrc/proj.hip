@@ -104,7 +104,9 @@ __global__ __launch_bounds__(kThreads) void proj_kernel(const uint16_t* __restri
     // its first LDS write: measured 13.3 -> 11.6 us at 512 tokens x 64 heads
     // and 7.3 -> 6.3 us at 2048 x 8.  At K = 128 the same took more
     // registers and fewer workgroups per CU, 3 % slower, so the shallower
-    // reductions keep eight fragments ahead and a load-store loop.
+    // reductions keep eight fragments ahead and put a thread's tile loads
+    // in flight two at a time (12.6 -> 11.4 us at K = 128 against one at a
+    // time, with no more registers).
     constexpr bool kBurst = K >= 512;
     const int nb = cb * (kCols / 32) + wave;  // this wavefront's 32-column tile
     const bool has_cols = nb * 32 < n_out;
@@ -131,12 +133,23 @@ __global__ __launch_bounds__(kThreads) void proj_kernel(const uint16_t* __restri
             *reinterpret_cast<u32x4*>(smem + row * XROW + ch * 16) = xv[u];
         }
     } else {
-        for (int c = tid; c < kRows * XCH; c += kThreads) {
-            const int row = c / XCH, ch = c % XCH;
-            const int t = t0 + row;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (t < M) v = *reinterpret_cast<const u32x4*>(x + ((int64_t)t * H + h) * ld_x + ch * 8);
-            *reinterpret_cast<u32x4*>(smem + row * XROW + ch * 16) = v;
+        constexpr int XU = kRows * XCH / kThreads;
+        constexpr int XB = XU >= 2 ? 2 : 1;  // loads in flight per batch
+#pragma unroll
+        for (int u0 = 0; u0 < XU; u0 += XB) {
+            u32x4 xv[XB];
+#pragma unroll
+            for (int u = 0; u < XB; ++u) {
+                const int c = tid + (u0 + u) * kThreads, row = c / XCH, ch = c % XCH;
+                const int t = t0 + row;
+                xv[u] = u32x4{0u, 0u, 0u, 0u};
+                if (t < M) xv[u] = *reinterpret_cast<const u32x4*>(x + ((int64_t)t * H + h) * ld_x + ch * 8);
+            }
+#pragma unroll
+            for (int u = 0; u < XB; ++u) {
+                const int c = tid + (u0 + u) * kThreads, row = c / XCH, ch = c % XCH;
+                *reinterpret_cast<u32x4*>(smem + row * XROW + ch * 16) = xv[u];
+            }
         }
     }
     __syncthreads();
