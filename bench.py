@@ -839,7 +839,8 @@ def time_projections(tokens, H, dev, reps=200, d_nope=128, d_lat=512, d_rope=64,
     """The per-head projections around the attention (ddt_head_proj) at
     `tokens` tree nodes x H heads: q_nope @ w_kc[h] -> the first d_lat
     columns of the q_lat|q_pe rows, and out_lat @ w_vc[h] -> o.  Each is
-    timed as `reps` back-to-back launches in one graph.  Algorithmic bytes
+    a graph of `reps` back-to-back launches, timed in 5 windows of >= 50 ms
+    of replays (the median reported).  Algorithmic bytes
     per launch: every input and output row once plus the weights once; at
     about 100 flop/B they are HBM-bound, reported against 8 TB/s (and
     their flops against the bf16 MFMA peak)."""
@@ -870,16 +871,14 @@ def time_projections(tokens, H, dev, reps=200, d_nope=128, d_lat=512, d_rope=64,
                 f()
         graph.replay()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        graph.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / reps
+        est = estimate_ms(graph.replay, reps, stream)
+        win, units = time_windows(graph.replay, reps, est, stream)
+        ms = float(np.median(win))
         nbytes = rows * (K + n) * 2 + H * K * n * 2
         flop = 2 * rows * K * n
         gbps = nbytes / (ms * 1e-3) / 1e9
-        res[name] = {"K": K, "n_out": n, "us": round(ms * 1e3, 3), "GBps": round(gbps, 1),
+        res[name] = {"K": K, "n_out": n, "us": round(ms * 1e3, 3), "us_spread": spread([x * 1e3 for x in win]),
+                     "launches_per_window": units, "GBps": round(gbps, 1),
                      "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
                      "TFLOPs": round(flop / (ms * 1e-3) / 1e12, 2), "bytes": nbytes}
     return res
