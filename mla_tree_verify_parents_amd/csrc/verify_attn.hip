@@ -42,8 +42,10 @@
 //  * Optional co-tasks: target-argmax workgroups on the CUs the attention
 //    leaves idle (verify_split), and acceptance + compaction workgroups
 //    beside the merge (verify_combine).
-//  * Paged caches: a paged work item lists its split's page numbers in LDS
-//    and looks up one pool row per tile (a tile never crosses a page).
+//  * Paged caches: a split's page numbers stream through a small ring of
+//    LDS windows (filled by LDS-DMA two windows ahead of the tiles), and
+//    each tile takes its pool rows from one page (a tile never crosses a
+//    page).
 #include <math.h>
 
 #include <algorithm>
