@@ -151,6 +151,53 @@ def test_paged_verify_step(orc, ps, with_mask):
     print(f"paged ps={ps}: accepted {oa.tolist()}")
 
 
+@pytest.mark.parametrize("ps,extra", [(32, 200), (64, 1000)])
+def test_paged_verify_step_device_lengths(orc, ps, extra):
+    """The fused step on a paged cache with the committed lengths read on
+    the device: the host passes bounds `extra` keys above them, the table
+    rows run that far with NaN pages past each request's keys, and the
+    results (attention, acceptance, compaction through the table, lengths)
+    equal the oracle's on the actual lengths."""
+    w = synth.workload(3, B=4, prefix_range=(0, 2500))
+    rng = np.random.default_rng(300 + ps)
+    V = 2000
+    w.draft_ids = w.draft_ids % V
+    t = synth.planted_targets(rng, w.parents, w.draft_ids, V, 0.8)
+    x = synth.target_logits(rng, t.reshape(-1), V)
+    phys, table = to_paged(w, ps, rng)
+    B, N, dl = w.B, w.N, w.d_lat
+    npg = (w.prefix_len.astype(np.int64) + N + ps - 1) // ps
+    named = set()
+    for b in range(B):
+        named |= set(table[b, : npg[b]].tolist())
+    free = np.array(sorted(set(range(phys.shape[0] // ps)) - named), np.int32)  # NaN pages no request owns
+    assert len(free) > 0
+    bound = w.prefix_len.astype(np.int64) + extra
+    cols = int(((bound + N + ps - 1) // ps).max())
+    wide = np.empty((B, cols), np.int32)
+    for b in range(B):
+        wide[b, : npg[b]] = table[b, : npg[b]]
+        wide[b, npg[b]:] = free[np.arange(cols - npg[b]) % len(free)]
+    ref_out, ref_lse = oracle_attn(orc, w)
+    t_ref = orc.argmax(x).reshape(B, N)
+    oa, op, ot = orc.greedy_accept(t_ref, w.draft_ids, w.parents)
+    opool = w.pool.copy()
+    opl, _ = orc.compact_kv(opool[:, :dl], opool[:, dl:], w.kv_base, w.prefix_len, op, oa)
+    pd, td = to_dev(phys), to_dev(wide)
+    prefix = to_dev(w.prefix_len)
+    q = to_dev(w.q)
+    out, lse, idx, acc, path, tok, npl = ddt.verify_step(
+        q[:, :dl], q[:, dl:], pd[:, :dl], pd[:, dl:], None, bound, None, to_dev(x), to_dev(w.draft_ids),
+        to_dev(w.parents), prefix, H=w.H, scale=w.scale, pages=(td, ps), device_lengths=True, kv_chunk=256)
+    torch.cuda.synchronize()
+    assert (to_host(idx).reshape(B, N) == t_ref).all()
+    check_attn(to_host(out), to_host(lse), ref_out, ref_lse, "bf16")
+    assert (to_host(acc) == oa).all() and (to_host(path) == op).all() and (to_host(tok) == ot).all()
+    assert (to_host(prefix) == opl).all()
+    got = from_paged(np.ascontiguousarray(to_host(pd)), wide, ps, w)
+    assert (got.view(np.uint8) == opool.view(np.uint8)).all()
+
+
 @pytest.mark.parametrize("ps,cfg", [(1, 3), (32, 1), (256, 3)])
 def test_paged_compact_kv(orc, ps, cfg):
     """Standalone compaction through a block table (ddt_compact_kv_paged):
