@@ -33,6 +33,19 @@ def test_verify_attn_device_lengths(orc, extra, kv_chunk):
     check_attn(to_host(out), to_host(lse), ref_out, ref_lse, "bf16", f"extra {extra}")
 
 
+def test_verify_attn_device_lengths_fp32(orc):
+    """The fp32 instance (MFMA 32x32x2 f32, the tiny configuration's
+    shapes) reads device lengths the same way."""
+    w = synth.workload(1, B=3, prefix_range=(10, 300), extra_rows=500)
+    dw = DevWorkload(w)
+    mask = ddt.build_mask(dw.parents)[0]
+    bound = w.prefix_len.astype(np.int64) + 400
+    out, lse = ddt.verify_attn(dw.q_lat(), dw.q_pe(), dw.ckv(), dw.kpe(), dw.kv_base, bound, mask, H=w.H,
+                               scale=w.scale, kv_chunk=64, prefix_len_dev=dw.prefix_dev)
+    ref_out, ref_lse = oracle_attn(orc, w)
+    check_attn(to_host(out), to_host(lse), ref_out, ref_lse, "f32")
+
+
 def test_verify_attn_device_lengths_clamped(orc):
     """A device length above its bound is taken as the bound; a negative
     one as 0 (the request then sees its N tree keys only)."""
